@@ -1,0 +1,127 @@
+"""Test helpers: build the same seeded layer for the oracle and for the GPU path.
+
+Only the seeded generator (``moe_inputs``) is shared; the oracle receives its
+own quantization of 2-bit experts (``oracle.q2_quantize``), the GPU path gets
+the library packer's bytes.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import moe_inputs as mi
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def sig(a):
+    return 1.0 / (1.0 + math.exp(-a))
+
+
+def silu(a):
+    return a * sig(a)
+
+
+def eval_closed_form(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"sig": sig, "silu": silu, "exp": math.exp,
+                                                   "log": math.log}))
+
+
+def load_hand_fixture(name="hand_layer_f32.json"):
+    """Dense fp32 arrays of the hand fixture plus its expected closed forms."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    H, E, I, Is = g["H"], g["E"], g["I"], g["Is"]
+    x = np.zeros((1, H), np.float32)
+    for h, v in g["x"]:
+        x[0, h] = v
+    rw = np.zeros((E, H), np.float32)
+    for e, h, v in g["router_w"]:
+        rw[e, h] = v
+    gv = np.zeros((H,), np.float32)
+    for h, v in g["gate_vec"]:
+        gv[h] = v
+    eg = np.zeros((E, I, H), np.float32)
+    eu = np.zeros((E, I, H), np.float32)
+    ed = np.zeros((E, H, I), np.float32)
+    for e, i, h, v in g["exp_gate"]:
+        eg[e, i, h] = v
+    for e, i, h, v in g["exp_up"]:
+        eu[e, i, h] = v
+    for e, j, i, v in g["exp_down"]:
+        ed[e, j, i] = v
+    sg = np.zeros((Is, H), np.float32)
+    su = np.zeros((Is, H), np.float32)
+    sd = np.zeros((H, Is), np.float32)
+    for i, h, v in g["sh_gate"]:
+        sg[i, h] = v
+    for i, h, v in g["sh_up"]:
+        su[i, h] = v
+    for j, i, v in g["sh_down"]:
+        sd[j, i] = v
+    exp = g["expected"]
+    y = np.zeros((H,), np.float64)
+    for j, expr in exp["y_nonzero"].items():
+        y[int(j)] = eval_closed_form(expr)
+    expected = dict(ids=np.array(exp["ids"], np.int32),
+                    wts=np.array([eval_closed_form(s) for s in exp["wts"]]),
+                    gate=eval_closed_form(exp["gate"]), y=y)
+    arrays = dict(H=H, E=E, K=g["K"], I=I, Is=Is, x=x, router_w=rw, gate_vec=gv, router_bias=None,
+                  exp_gate=eg, exp_up=eu, exp_down=ed, sh_gate=sg, sh_up=su, sh_down=sd)
+    return arrays, expected
+
+
+def oracle_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_t="f32", renormalize=1):
+    """Oracle layer from dense arrays (f32 values or bf16 bits; experts may be
+    a list of ``oracle.Q2``)."""
+    import oracle
+    E = a["E"]
+    return oracle.Layer(H=a["H"], E=E, K=a["K"], I=a["I"], Is=a["Is"], router_t=router_t,
+                        expert_t=expert_t, shared_t=shared_t, router_w=a["router_w"],
+                        gate_vec=a["gate_vec"], router_bias=a.get("router_bias"),
+                        exp_gate=[a["exp_gate"][e] for e in range(E)],
+                        exp_up=[a["exp_up"][e] for e in range(E)],
+                        exp_down=[a["exp_down"][e] for e in range(E)],
+                        sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"],
+                        renormalize=renormalize)
+
+
+def oracle_layer_from_config(cfg: mi.LayerConfig, dense=None, experts=None, stacks=None):
+    """Oracle layer for a seeded workload.
+
+    ``experts``: restrict routed experts to this set (others absent; the oracle
+    fails loudly if it selects one). 2-bit experts are quantized here with the
+    oracle's own quantizer from the generator's fp32 source.
+    """
+    import oracle
+    dense = dense if dense is not None else mi.dense_weights(cfg)
+    todo = range(cfg.E) if experts is None else sorted(set(int(e) for e in experts))
+    G = [None] * cfg.E
+    U = [None] * cfg.E
+    D = [None] * cfg.E
+    if cfg.expert_t == "q2":
+        for e in todo:
+            G[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_GATE))
+            U[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_UP))
+            D[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_DOWN))
+    else:
+        if stacks is None:
+            stacks = mi.expert_stacks(cfg, experts)
+        g, u, d = stacks
+        for e in todo:
+            G[e], U[e], D[e] = g[e], u[e], d[e]
+    return oracle.Layer(H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t,
+                        expert_t=cfg.expert_t, shared_t=cfg.shared_t, router_w=dense["router_w"],
+                        gate_vec=dense["gate_vec"], router_bias=dense["router_bias"],
+                        exp_gate=G, exp_up=U, exp_down=D, sh_gate=dense["sh_gate"],
+                        sh_up=dense["sh_up"], sh_down=dense["sh_down"])
+
+
+def tolerance_ok(got, ref, atol=1e-4, rtol=2e-3):
+    """Elementwise |got - ref| <= atol + rtol*|ref| (the stated output bound)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(got - ref) <= atol + rtol * np.abs(ref)
