@@ -1,0 +1,249 @@
+"""Python binding of libmoe.so, the gfx950 sparse MoE layer library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch provides device memory and streams; tensors are passed to
+the C ABI as raw pointers. There is no fallback: if the built library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EALIGN, MOE_EHIP, MOE_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
+MOE_F32, MOE_BF16, MOE_Q2B32 = 0, 1, 2
+WTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "q2": MOE_Q2B32}
+
+EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_forward",
+           "moe_sort_workspace_bytes", "moe_sort_by_expert", "moe_q2_packed_bytes", "moe_q2_pack",
+           "moe_q2_unpack")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [
+        ("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("inter", C.c_int32),
+        ("shared_inter", C.c_int32), ("renormalize", C.c_int32), ("router_t", C.c_int32),
+        ("expert_t", C.c_int32), ("shared_t", C.c_int32), ("reserved", C.c_int32),
+        ("router_w", C.c_void_p), ("router_bias", C.c_void_p), ("shared_gate_w", C.c_void_p),
+        ("exp_gate", C.c_void_p), ("exp_up", C.c_void_p), ("exp_down", C.c_void_p),
+        ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (built in-tree by ``sparse_moe_decode_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_moe_decode_amd.build`")
+            L = C.CDLL(LIB_PATH)
+            vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+            L.moe_abi_version.restype = C.c_uint32
+            L.moe_strerror.argtypes = [C.c_int]
+            L.moe_strerror.restype = C.c_char_p
+            L.moe_workspace_bytes.argtypes = [C.POINTER(LayerDesc), i32]
+            L.moe_workspace_bytes.restype = sz
+            L.moe_route.argtypes = [C.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp]
+            L.moe_route.restype = C.c_int
+            L.moe_forward.argtypes = [C.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_forward.restype = C.c_int
+            L.moe_sort_workspace_bytes.argtypes = [i32, i32, i32]
+            L.moe_sort_workspace_bytes.restype = sz
+            L.moe_sort_by_expert.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+            L.moe_sort_by_expert.restype = C.c_int
+            L.moe_q2_packed_bytes.argtypes = [i64, i64]
+            L.moe_q2_packed_bytes.restype = sz
+            L.moe_q2_pack.argtypes = [vp, i64, i64, vp, sz]
+            L.moe_q2_pack.restype = C.c_int
+            L.moe_q2_unpack.argtypes = [vp, i64, i64, vp, vp]
+            L.moe_q2_unpack.restype = C.c_int
+            _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MOE_OK:
+        raise MoEError(rc, where)
+
+
+def abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+# ------------------------------------------------------------ packer (host)
+
+def q2_packed_bytes(rows: int, cols: int) -> int:
+    return int(lib().moe_q2_packed_bytes(rows, cols))
+
+
+def q2_pack(w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Pack an fp32 [rows][cols] matrix (host) into the 2-bit block format."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    n = q2_packed_bytes(rows, cols)
+    if n == 0:
+        raise MoEError(MOE_EINVAL, "moe_q2_pack")
+    if out is None:
+        out = np.empty(n, np.uint8)
+    assert out.flags.c_contiguous and out.nbytes >= n
+    _check(lib().moe_q2_pack(w.ctypes.data, rows, cols, out.ctypes.data, out.nbytes), "moe_q2_pack")
+    return out
+
+
+# --------------------------------------------------------------- device calls
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def workspace_bytes(desc: LayerDesc, T: int) -> int:
+    return int(lib().moe_workspace_bytes(C.byref(desc), T))
+
+
+def route(desc: LayerDesc, x, ids, wts, gate, ws, stream=None) -> None:
+    T = x.shape[0]
+    _check(lib().moe_route(C.byref(desc), _ptr(x), T, _ptr(ids), _ptr(wts), _ptr(gate), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+
+
+def forward(desc: LayerDesc, x, y, ws, ids_in=None, wts_in=None, gate_in=None, ids_out=None, wts_out=None,
+            gate_out=None, stream=None) -> None:
+    T = x.shape[0]
+    _check(lib().moe_forward(C.byref(desc), _ptr(x), T, _ptr(y), _ptr(ids_in), _ptr(wts_in), _ptr(gate_in),
+                             _ptr(ids_out), _ptr(wts_out), _ptr(gate_out), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def sort_workspace_bytes(T: int, K: int, E: int) -> int:
+    return int(lib().moe_sort_workspace_bytes(T, K, E))
+
+
+def sort_by_expert(ids, E: int, counts, offsets, perm, ws, stream=None) -> None:
+    T, K = ids.shape
+    _check(lib().moe_sort_by_expert(_ptr(ids), T, K, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "moe_sort_by_expert")
+
+
+def q2_unpack(packed, rows: int, cols: int, dst, stream=None) -> None:
+    _check(lib().moe_q2_unpack(_ptr(packed), rows, cols, _ptr(dst), _stream(stream)), "moe_q2_unpack")
+
+
+# ------------------------------------------------------------- layer holder
+
+class Layer:
+    """Device-resident weights of one layer and its descriptor.
+
+    Built from host arrays (fp32 values, bf16 bit patterns as uint16, or fp32
+    sources of 2-bit experts which are packed here by the library packer).
+    """
+
+    def __init__(self, *, H, E, K, I, Is, router_t, expert_t, shared_t, router_w, gate_vec, router_bias,
+                 sh_gate, sh_up, sh_down, exp_gate=None, exp_up=None, exp_down=None, expert_source=None,
+                 renormalize=1, device="cuda"):
+        import torch
+        self.H, self.E, self.K, self.I, self.Is = H, E, K, I, Is
+        self.router_t, self.expert_t, self.shared_t = router_t, expert_t, shared_t
+        self.device = device
+
+        def up(a, fmt=None):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            if fmt == "bf16" or a.dtype == np.uint16:
+                t = torch.from_numpy(a.view(np.int16)).to(device)
+            else:
+                t = torch.from_numpy(a).to(device)
+            return t
+
+        self.router_w = up(router_w, router_t)
+        self.gate_vec = up(gate_vec, router_t)
+        self.router_bias = up(None if router_bias is None else np.asarray(router_bias, np.float32))
+        self.sh_gate, self.sh_up, self.sh_down = up(sh_gate), up(sh_up), up(sh_down)
+        if expert_t == "q2":
+            # expert_source(e, mat) -> fp32 [rows][cols]; mat 0 gate, 1 up, 2 down
+            self.exp_gate = self._pack_stack(expert_source, 0, I, H)
+            self.exp_up = self._pack_stack(expert_source, 1, I, H)
+            self.exp_down = self._pack_stack(expert_source, 2, H, I)
+        else:
+            self.exp_gate, self.exp_up, self.exp_down = up(exp_gate), up(exp_up), up(exp_down)
+        self.desc = LayerDesc(H, E, K, I, Is, renormalize, WTYPE[router_t], WTYPE[expert_t], WTYPE[shared_t], 0,
+                              _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.gate_vec),
+                              _ptr(self.exp_gate), _ptr(self.exp_up), _ptr(self.exp_down),
+                              _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down))
+
+    def _pack_stack(self, source, mat, rows, cols):
+        import torch
+        from concurrent.futures import ThreadPoolExecutor
+        n = q2_packed_bytes(rows, cols)
+        host = np.empty((self.E, n), np.uint8)
+
+        def one(e):
+            q2_pack(source(e, mat), out=host[e])
+
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(one, range(self.E)))
+        return torch.from_numpy(host).to(self.device)
+
+    def workspace(self, T: int):
+        import torch
+        n = workspace_bytes(self.desc, T)
+        if n == 0:
+            raise MoEError(MOE_EINVAL, "moe_workspace_bytes")
+        return torch.zeros((n + 15) // 16 * 16, dtype=torch.uint8, device=self.device)
+
+    def forward(self, x, y=None, ws=None, routing=None, want_routing=False, stream=None):
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float32, device=self.device)
+        if ws is None:
+            ws = self.workspace(T)
+        ids = wts = gate = None
+        if want_routing:
+            ids = torch.empty((T, self.K), dtype=torch.int32, device=self.device)
+            wts = torch.empty((T, self.K), dtype=torch.float32, device=self.device)
+            gate = torch.empty((T,), dtype=torch.float32, device=self.device)
+        if routing is not None:
+            forward(self.desc, x, y, ws, ids_in=routing[0], wts_in=routing[1], gate_in=routing[2], stream=stream)
+        else:
+            forward(self.desc, x, y, ws, ids_out=ids, wts_out=wts, gate_out=gate, stream=stream)
+        return (y, ids, wts, gate) if want_routing else y
+
+    def route(self, x, ws=None, stream=None):
+        import torch
+        T = x.shape[0]
+        ids = torch.empty((T, self.K), dtype=torch.int32, device=self.device)
+        wts = torch.empty((T, self.K), dtype=torch.float32, device=self.device)
+        gate = torch.empty((T,), dtype=torch.float32, device=self.device)
+        if ws is None:
+            ws = self.workspace(T)
+        route(self.desc, x, ids, wts, gate, ws, stream=stream)
+        return ids, wts, gate

@@ -1,0 +1,236 @@
+// C ABI of the MoE layer library: host-side argument validation, workspace
+// sizing and path dispatch. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "device_common.cuh"
+#include "internal.h"
+#include "moe.h"
+
+namespace {
+
+enum Path { kDecode = 0, kFewRow = 1, kPrefill = 2 };
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_desc(const moe_layer_desc *d)
+{
+    if (!d)
+        return MOE_EINVAL;
+    if (d->reserved != 0)
+        return MOE_EINVAL;
+    if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->inter <= 0 || d->shared_inter <= 0)
+        return MOE_EINVAL;
+    if (d->hidden % 32 || d->inter % 32 || d->shared_inter % 32)
+        return MOE_EINVAL;
+    if (d->top_k > d->n_experts || d->top_k > moe::kMaxK)
+        return MOE_EINVAL;
+    if (d->renormalize != 0 && d->renormalize != 1)
+        return MOE_EINVAL;
+    if ((d->router_t != MOE_F32 && d->router_t != MOE_BF16) ||
+        (d->shared_t != MOE_F32 && d->shared_t != MOE_BF16) ||
+        (d->expert_t != MOE_F32 && d->expert_t != MOE_BF16 && d->expert_t != MOE_Q2B32))
+        return MOE_EINVAL;
+    if (d->n_experts > moe::kMaxE || d->hidden > 8192 || d->inter > 4096 || d->shared_inter > 4096)
+        return MOE_EUNSUPPORTED;
+    const void *req[] = {d->router_w, d->shared_gate_w, d->exp_gate, d->exp_up, d->exp_down,
+                         d->sh_gate,  d->sh_up,         d->sh_down};
+    for (const void *p : req) {
+        if (!p)
+            return MOE_EINVAL;
+        if (!aligned16(p))
+            return MOE_EALIGN;
+    }
+    if (d->router_bias && (reinterpret_cast<uintptr_t>(d->router_bias) & 3u))
+        return MOE_EALIGN;
+    return MOE_OK;
+}
+
+// Rows per decode / few-row launch: x of all rows (plus 2-bit block sums) is
+// staged in LDS, kept within 32 KiB + 1 KiB.
+int max_rows(const moe_layer_desc *d)
+{
+    const int r = 8192 / d->hidden;
+    return r < moe::kMaxRows ? (r < 1 ? 1 : r) : moe::kMaxRows;
+}
+
+Path choose_path(int T)
+{
+    const char *f = std::getenv("MOE_FORCE_PATH");
+    if (f && *f) {
+        if (!std::strcmp(f, "decode"))
+            return kDecode;
+        if (!std::strcmp(f, "fewrow"))
+            return kFewRow;
+        if (!std::strcmp(f, "prefill"))
+            return kPrefill;
+    }
+    if (T == 1)
+        return kDecode;
+    if (T <= moe::kMaxRows)
+        return kFewRow;
+    return kPrefill;
+}
+
+// Rows per launch group of the decode / few-row kernels.
+int group_rows(const moe_layer_desc *d, Path p, int T)
+{
+    if (p == kDecode)
+        return 1;
+    const int r = max_rows(d);
+    return T < r ? T : r;
+}
+
+size_t ws_bytes_for(const moe_layer_desc *d, int T)
+{
+    if (T <= 0)
+        return 256;
+    const Path p = choose_path(T);
+    // the prefill path is served by few-row groups until its grouped kernels run
+    const int R = group_rows(d, p == kPrefill ? kFewRow : p, T);
+    return static_cast<size_t>(moe::decode_ws_size(d, R));
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_strerror(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported size or format";
+    case MOE_EWORKSPACE: return "workspace or destination buffer too small";
+    case MOE_EALIGN: return "pointer not 16-byte aligned";
+    case MOE_EHIP: return "HIP launch or runtime error";
+    case MOE_ENONFINITE: return "non-finite input or value out of fp16 range";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_layer_desc *d, int32_t T)
+{
+    if (validate_desc(d) != MOE_OK || T < 0)
+        return 0;
+    return ws_bytes_for(d, T);
+}
+
+int moe_route(const moe_layer_desc *d, const float *x, int32_t T, int32_t *ids, float *wts, float *gate, void *ws,
+              size_t ws_bytes, void *stream)
+{
+    int rc = validate_desc(d);
+    if (rc != MOE_OK)
+        return rc;
+    if (T < 0)
+        return MOE_EINVAL;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !ids || !wts || !gate || !ws)
+        return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(ids) & 3u) ||
+        (reinterpret_cast<uintptr_t>(wts) & 3u) || (reinterpret_cast<uintptr_t>(gate) & 3u))
+        return MOE_EALIGN;
+    if (ws_bytes < ws_bytes_for(d, T))
+        return MOE_EWORKSPACE;
+    (void)hipGetLastError();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int H = d->hidden, K = d->top_k;
+    const int R = group_rows(d, kFewRow, T);
+    for (int t = 0; t < T; t += R) {
+        const int r = T - t < R ? T - t : R;
+        rc = moe::launch_decode_route(d, x + static_cast<size_t>(t) * H, r, ids + static_cast<size_t>(t) * K,
+                                      wts + static_cast<size_t>(t) * K, gate + t, ws, s);
+        if (rc != MOE_OK)
+            return rc;
+    }
+    return MOE_OK;
+}
+
+int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y, const int32_t *ids_in,
+                const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out, float *gate_out,
+                void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = validate_desc(d);
+    if (rc != MOE_OK)
+        return rc;
+    if (T < 0)
+        return MOE_EINVAL;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !y || !ws)
+        return MOE_EINVAL;
+    if (ids_in && (!wts_in || !gate_in))
+        return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
+        return MOE_EALIGN;
+    const void *small[] = {ids_in, wts_in, gate_in, ids_out, wts_out, gate_out};
+    for (const void *p : small)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u))
+            return MOE_EALIGN;
+    if (ws_bytes < ws_bytes_for(d, T))
+        return MOE_EWORKSPACE;
+    (void)hipGetLastError();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Path path = choose_path(T);
+    const int H = d->hidden, K = d->top_k;
+    const int R = group_rows(d, path == kPrefill ? kFewRow : path, T);
+    for (int t = 0; t < T; t += R) {
+        const int r = T - t < R ? T - t : R;
+        const size_t ok = static_cast<size_t>(t) * K;
+        rc = moe::launch_decode_forward(d, x + static_cast<size_t>(t) * H, r, y + static_cast<size_t>(t) * H,
+                                        ids_in ? ids_in + ok : nullptr, ids_in ? wts_in + ok : nullptr,
+                                        ids_in ? gate_in + t : nullptr, ids_out ? ids_out + ok : nullptr,
+                                        wts_out ? wts_out + ok : nullptr, gate_out ? gate_out + t : nullptr, ws, s);
+        if (rc != MOE_OK)
+            return rc;
+    }
+    return MOE_OK;
+}
+
+size_t moe_sort_workspace_bytes(int32_t T, int32_t K, int32_t E)
+{
+    if (T < 0 || K <= 0 || E <= 0 || E > moe::kMaxE)
+        return 0;
+    return moe::sort_ws_bytes_tke(static_cast<int64_t>(T) * K, E);
+}
+
+int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E, int32_t *counts, int32_t *offsets,
+                       int32_t *perm, void *ws, size_t ws_bytes, void *stream)
+{
+    if (T < 0 || K <= 0 || E <= 0)
+        return MOE_EINVAL;
+    if (E > moe::kMaxE || static_cast<int64_t>(T) * K > 0x7fffffff)
+        return MOE_EUNSUPPORTED;
+    if (!ids || !counts || !offsets || !perm || !ws)
+        return MOE_EINVAL;
+    const void *ps[] = {ids, counts, offsets, perm};
+    for (const void *p : ps)
+        if (reinterpret_cast<uintptr_t>(p) & 3u)
+            return MOE_EALIGN;
+    if (!aligned16(ws))
+        return MOE_EALIGN;
+    if (ws_bytes < moe_sort_workspace_bytes(T, K, E))
+        return MOE_EWORKSPACE;
+    if (T == 0)
+        return MOE_OK;
+    (void)hipGetLastError();
+    return moe::launch_sort_by_expert(ids, T, K, E, counts, offsets, perm, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream)
+{
+    if (!packed || !dst || rows <= 0 || cols <= 0 || cols % 32 != 0)
+        return MOE_EINVAL;
+    if (!aligned16(packed) || !aligned16(dst))
+        return MOE_EALIGN;
+    (void)hipGetLastError();
+    return moe::launch_q2_unpack(packed, rows, cols, dst, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

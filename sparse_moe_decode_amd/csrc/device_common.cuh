@@ -1,0 +1,222 @@
+// Device helpers shared by the gfx950 kernels: weight-format access, wave64
+// reductions and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 16;
+constexpr int kMaxE = 1024;
+constexpr int kMaxRows = 4;   // rows per few-row call
+
+// ------------------------------------------------------------ formats
+//
+// Every matrix is read in 16-byte "chunks" (f32: 4 values, bf16: 8 values)
+// or, for the 2-bit format, in 32-weight blocks (8 bytes of codes plus one
+// dword holding the fp16 scale and min).
+
+struct F32 {
+    static constexpr int kChunk = 4;   // elements per chunk
+};
+struct BF16 {
+    static constexpr int kChunk = 8;
+};
+struct Q2 {
+    static constexpr int kChunk = 32;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp16 bits -> fp32 (exact; fp16 subnormals are kept by the conversion)
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16)
+{
+    _Float16 h;
+    uint16_t b = static_cast<uint16_t>(bits16);
+    __builtin_memcpy(&h, &b, 2);
+    return static_cast<float>(h);
+}
+
+// A dense matrix of type F32/BF16: row-major, `cols` elements per row.
+// A Q2 matrix: codes plane then scale/min plane (see moe_q2_pack).
+struct MatRef {
+    const uint8_t *base;   // matrix start
+    int rows, cols;
+};
+
+// Byte size of one stacked matrix of each format.
+__host__ __device__ inline size_t q2_packed_bytes(int64_t rows, int64_t cols)
+{
+    const uint64_t raw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols) / 8u * 3u;
+    return static_cast<size_t>((raw + 255u) / 256u * 256u);
+}
+
+template <typename W>
+__host__ __device__ inline size_t mat_bytes(int64_t rows, int64_t cols);
+template <>
+__host__ __device__ inline size_t mat_bytes<F32>(int64_t rows, int64_t cols) { return rows * cols * 4; }
+template <>
+__host__ __device__ inline size_t mat_bytes<BF16>(int64_t rows, int64_t cols) { return rows * cols * 2; }
+template <>
+__host__ __device__ inline size_t mat_bytes<Q2>(int64_t rows, int64_t cols) { return q2_packed_bytes(rows, cols); }
+
+// ----------------------------------------------------------- chunk dots
+//
+// dot of chunk `c` of row `r` with a vector v (fp32, in LDS), accumulated
+// into acc[R] for R vectors laid out with stride `vs`. For Q2 `vsum` holds
+// the per-block sums of each vector (stride vss), used for the min term:
+//   sum_j (code_j*s + m) v_j = s * sum_j code_j v_j + m * sum_j v_j.
+
+template <int R>
+__device__ __forceinline__ void chunk_dot(F32, const MatRef &M, int r, int c, const float *v, int vs,
+                                          const float *, int, float (&acc)[R])
+{
+    const float4 w = *reinterpret_cast<const float4 *>(M.base + (static_cast<size_t>(r) * M.cols + c * 4) * 4);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 xv = *reinterpret_cast<const float4 *>(v + q * vs + c * 4);
+        acc[q] = fmaf(w.x, xv.x, acc[q]);
+        acc[q] = fmaf(w.y, xv.y, acc[q]);
+        acc[q] = fmaf(w.z, xv.z, acc[q]);
+        acc[q] = fmaf(w.w, xv.w, acc[q]);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void chunk_dot(BF16, const MatRef &M, int r, int c, const float *v, int vs,
+                                          const float *, int, float (&acc)[R])
+{
+    const uint4 w = *reinterpret_cast<const uint4 *>(M.base + (static_cast<size_t>(r) * M.cols + c * 8) * 2);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(v + q * vs + c * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(v + q * vs + c * 8 + 4);
+        float a = acc[q];
+        a = fmaf(bf16_lo(w.x), x0.x, a);
+        a = fmaf(bf16_hi(w.x), x0.y, a);
+        a = fmaf(bf16_lo(w.y), x0.z, a);
+        a = fmaf(bf16_hi(w.y), x0.w, a);
+        a = fmaf(bf16_lo(w.z), x1.x, a);
+        a = fmaf(bf16_hi(w.z), x1.y, a);
+        a = fmaf(bf16_lo(w.w), x1.z, a);
+        a = fmaf(bf16_hi(w.w), x1.w, a);
+        acc[q] = a;
+    }
+}
+
+// codes of one 32-weight block: two dwords, weight j at bits 2*(j%16) of dword j/16
+template <int R>
+__device__ __forceinline__ void chunk_dot(Q2, const MatRef &M, int r, int b, const float *v, int vs,
+                                          const float *vsum, int vss, float (&acc)[R])
+{
+    const int nb = M.cols >> 5;
+    const uint2 cw = *reinterpret_cast<const uint2 *>(M.base + static_cast<size_t>(r) * (M.cols >> 2) + b * 8);
+    const uint32_t sm = *reinterpret_cast<const uint32_t *>(
+        M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) + (static_cast<size_t>(r) * nb + b) * 4);
+    const float s = f16_to_f32(sm & 0xffffu);
+    const float m = f16_to_f32(sm >> 16);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float *x = v + q * vs + b * 32;
+        float cx = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t d = half ? cw.y : cw.x;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const float4 xv = *reinterpret_cast<const float4 *>(x + half * 16 + j4 * 4);
+                const uint32_t byte = d >> (8 * j4);
+                cx = fmaf(static_cast<float>(byte & 3u), xv.x, cx);
+                cx = fmaf(static_cast<float>((byte >> 2) & 3u), xv.y, cx);
+                cx = fmaf(static_cast<float>((byte >> 4) & 3u), xv.z, cx);
+                cx = fmaf(static_cast<float>((byte >> 6) & 3u), xv.w, cx);
+            }
+        }
+        acc[q] = fmaf(s, cx, fmaf(m, vsum[q * vss + b], acc[q]));
+    }
+}
+
+// ----------------------------------------------------------- reductions
+
+template <typename T>
+__device__ __forceinline__ T lane_group_sum(T v, int width)
+{
+    for (int off = width >> 1; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float a, float c)
+{
+    return a / (1.0f + __expf(-a)) * c;
+}
+
+__device__ __forceinline__ int next_pow2(int v)
+{
+    int p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+// ------------------------------------------------------------ workspace
+//
+// Layout of the decode / few-row workspace (all offsets 256-byte aligned):
+//   control     : counters and flags (256 B)
+//   logits      : [R][E] double
+//   zlogit      : [R] double
+//   slot table  : nslots, slot_expert[S], slot_w[S][R] (S = R*K + 1)
+//   hbuf        : [S][R][Imax] fp32   (weighted SwiGLU activations)
+struct Control {
+    unsigned int route_done;   // last-block ticket of the route kernel
+    unsigned int pad[63];
+};
+
+struct SlotTable {
+    int nslots;
+    int pad[3];
+    int expert[kMaxRows * kMaxK + 1];          // slot 0 = shared expert (-1)
+    float w[kMaxRows * kMaxK + 1][kMaxRows];   // per-row weight (0: row does not use the slot)
+};
+
+struct DecodeWs {
+    Control *ctl;
+    double *logits;
+    double *zlogit;
+    SlotTable *slots;
+    float *hbuf;
+};
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+__host__ __device__ inline size_t decode_ws_bytes(int R, int E, int K, int Imax)
+{
+    const int S = R * K + 1;
+    return align256(sizeof(Control)) + align256(sizeof(double) * R * E) + align256(sizeof(double) * R) +
+           align256(sizeof(SlotTable)) + align256(sizeof(float) * S * R * Imax);
+}
+
+__host__ __device__ inline DecodeWs decode_ws_carve(void *ws, int R, int E, int K, int Imax)
+{
+    (void)K;
+    (void)Imax;
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    DecodeWs w;
+    w.ctl = reinterpret_cast<Control *>(p);
+    p += align256(sizeof(Control));
+    w.logits = reinterpret_cast<double *>(p);
+    p += align256(sizeof(double) * R * E);
+    w.zlogit = reinterpret_cast<double *>(p);
+    p += align256(sizeof(double) * R);
+    w.slots = reinterpret_cast<SlotTable *>(p);
+    p += align256(sizeof(SlotTable));
+    w.hbuf = reinterpret_cast<float *>(p);
+    return w;
+}
+
+}  // namespace moe

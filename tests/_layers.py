@@ -125,3 +125,78 @@ def tolerance_ok(got, ref, atol=1e-4, rtol=2e-3):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     return np.abs(got - ref) <= atol + rtol * np.abs(ref)
+
+
+# ------------------------------------------------------------- GPU side
+
+def gpu_layer_from_config(cfg: mi.LayerConfig, dense=None, stacks=None, renormalize=1):
+    """The same seeded layer on the GPU (library packer for 2-bit experts)."""
+    import sparse_moe_decode_amd as moe
+    dense = dense if dense is not None else mi.dense_weights(cfg)
+    kw = dict(H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t, expert_t=cfg.expert_t,
+              shared_t=cfg.shared_t, router_w=dense["router_w"], gate_vec=dense["gate_vec"],
+              router_bias=dense["router_bias"], sh_gate=dense["sh_gate"], sh_up=dense["sh_up"],
+              sh_down=dense["sh_down"], renormalize=renormalize)
+    if cfg.expert_t == "q2":
+        return moe.Layer(**kw, expert_source=lambda e, m: mi.expert_matrix_f32(cfg, e, m))
+    g, u, d = stacks if stacks is not None else mi.expert_stacks(cfg)
+    return moe.Layer(**kw, exp_gate=g, exp_up=u, exp_down=d)
+
+
+def gpu_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_t="f32", renormalize=1):
+    import sparse_moe_decode_amd as moe
+    kw = dict(H=a["H"], E=a["E"], K=a["K"], I=a["I"], Is=a["Is"], router_t=router_t, expert_t=expert_t,
+              shared_t=shared_t, router_w=a["router_w"], gate_vec=a["gate_vec"], router_bias=a.get("router_bias"),
+              sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"], renormalize=renormalize)
+    if expert_t == "q2":
+        src = {0: a["exp_gate"], 1: a["exp_up"], 2: a["exp_down"]}
+        return moe.Layer(**kw, expert_source=lambda e, m: np.asarray(src[m][e], np.float32))
+    return moe.Layer(**kw, exp_gate=a["exp_gate"], exp_up=a["exp_up"], exp_down=a["exp_down"])
+
+
+def run_calls(layer, x_host: np.ndarray, rows_per_call: int, force_path: str | None = None):
+    """Run x through the layer in back-to-back calls of `rows_per_call` rows on
+    one stream; returns host ids, wts, gate, y."""
+    import torch
+    import sparse_moe_decode_amd as moe
+    T = x_host.shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(x_host, np.float32)).cuda()
+    y = torch.empty((T, layer.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, layer.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, layer.K), dtype=torch.float32, device="cuda")
+    gate = torch.empty((T,), dtype=torch.float32, device="cuda")
+    ws = layer.workspace(min(T, rows_per_call))
+    old = os.environ.get("MOE_FORCE_PATH")
+    if force_path:
+        os.environ["MOE_FORCE_PATH"] = force_path
+    try:
+        for t in range(0, T, rows_per_call):
+            r = min(rows_per_call, T - t)
+            moe.forward(layer.desc, x[t:t + r], y[t:t + r], ws, ids_out=ids[t:t + r], wts_out=wts[t:t + r],
+                        gate_out=gate[t:t + r])
+        torch.cuda.synchronize()
+    finally:
+        if force_path:
+            if old is None:
+                os.environ.pop("MOE_FORCE_PATH", None)
+            else:
+                os.environ["MOE_FORCE_PATH"] = old
+    return ids.cpu().numpy(), wts.cpu().numpy(), gate.cpu().numpy(), y.cpu().numpy()
+
+
+def assert_parity(got, ref, what, sample_rows=None):
+    """ids bit-identical; wts, gate, y within |d| <= 1e-4 + 2e-3 |ref|."""
+    gi, gw, gg, gy = got
+    ri, rw, rg, ry = ref
+    rows = np.arange(len(ri)) if sample_rows is None else np.asarray(sample_rows)
+    bad = np.nonzero(np.any(gi[rows] != ri, axis=1))[0]
+    assert bad.size == 0, f"{what}: router selection differs on rows {rows[bad][:10]}: gpu {gi[rows[bad[0]]]} oracle {ri[bad[0]]}"
+    ok_w = tolerance_ok(gw[rows], rw)
+    assert ok_w.all(), f"{what}: wts out of tolerance, max err {np.abs(gw[rows] - rw).max():.3g}"
+    ok_g = tolerance_ok(gg[rows], rg)
+    assert ok_g.all(), f"{what}: gate out of tolerance, max err {np.abs(gg[rows] - rg).max():.3g}"
+    ok_y = tolerance_ok(gy[rows], ry)
+    err = np.abs(gy[rows].astype(np.float64) - ry)
+    assert ok_y.all(), (f"{what}: {np.count_nonzero(~ok_y)} y values out of tolerance; max abs err "
+                        f"{err.max():.3g}, worst row {rows[np.argmax(err.max(axis=1))]}")
+    return float(err.max()), float((err / (1e-4 + 2e-3 * np.abs(ry))).max())

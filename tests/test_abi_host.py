@@ -1,0 +1,183 @@
+"""Host-only checks of the C ABI: the library loads and exports every entry
+point of include/moe.h, validation returns the documented codes before any
+launch, and the host packer equals the oracle's own quantizer byte for byte.
+No GPU work is issued here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_moe_decode_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function():
+    names = _header_functions()
+    assert set(names) == set(moe.EXPORTS)
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_strerror():
+    assert moe.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert moe.strerror(code) and moe.strerror(code) != "unknown status"
+    assert moe.strerror(-99) == "unknown status"
+
+
+def _fake_desc(**kw):
+    a = 0x10000  # aligned placeholders: never dereferenced by these host-only calls
+    d = dict(hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, renormalize=1,
+             router_t=moe.MOE_BF16, expert_t=moe.MOE_BF16, shared_t=moe.MOE_BF16, reserved=0,
+             router_w=a, router_bias=None, shared_gate_w=a, exp_gate=a, exp_up=a, exp_down=a,
+             sh_gate=a, sh_up=a, sh_down=a)
+    d.update(kw)
+    return moe.LayerDesc(**d)
+
+
+def _fwd(desc, x=0x20000, T=1, y=0x30000, ws=0x40000, ws_bytes=1 << 30, ids_in=None, wts_in=None, gate_in=None):
+    return moe.lib().moe_forward(C.byref(desc), x, T, y, ids_in, wts_in, gate_in, None, None, None, ws,
+                                 ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=0), moe.MOE_EINVAL),
+    (dict(hidden=2050), moe.MOE_EINVAL),            # not a multiple of 32
+    (dict(inter=500), moe.MOE_EINVAL),
+    (dict(top_k=0), moe.MOE_EINVAL),
+    (dict(top_k=513), moe.MOE_EINVAL),              # K > E
+    (dict(top_k=17), moe.MOE_EINVAL),               # K > 16
+    (dict(renormalize=2), moe.MOE_EINVAL),
+    (dict(router_t=moe.MOE_Q2B32), moe.MOE_EINVAL),
+    (dict(shared_t=7), moe.MOE_EINVAL),
+    (dict(reserved=1), moe.MOE_EINVAL),
+    (dict(router_w=None), moe.MOE_EINVAL),
+    (dict(exp_down=None), moe.MOE_EINVAL),
+    (dict(exp_up=0x10008), moe.MOE_EALIGN),
+    (dict(router_bias=0x10002), moe.MOE_EALIGN),
+    (dict(n_experts=2048), moe.MOE_EUNSUPPORTED),
+    (dict(hidden=16384), moe.MOE_EUNSUPPORTED),
+])
+def test_descriptor_validation(kw, code):
+    d = _fake_desc(**kw)
+    assert _fwd(d) == code
+    assert moe.lib().moe_route(C.byref(d), 0x20000, 1, 0x50000, 0x60000, 0x70000, 0x40000, 1 << 30, None) == code
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 1) == 0
+
+
+def test_call_validation():
+    d = _fake_desc()
+    assert _fwd(d, T=-1) == moe.MOE_EINVAL
+    assert _fwd(d, T=0) == moe.MOE_OK                       # no-op
+    assert _fwd(d, x=None) == moe.MOE_EINVAL
+    assert _fwd(d, y=None) == moe.MOE_EINVAL
+    assert _fwd(d, ws=None) == moe.MOE_EINVAL
+    assert _fwd(d, x=0x20004) == moe.MOE_EALIGN
+    assert _fwd(d, y=0x30008) == moe.MOE_EALIGN
+    assert _fwd(d, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _fwd(d, ids_in=0x50000) == moe.MOE_EINVAL         # routing given without weights
+    need = moe.lib().moe_workspace_bytes(C.byref(d), 1)
+    assert need > 0
+    assert _fwd(d, ws_bytes=need - 1) == moe.MOE_EWORKSPACE
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 2048) >= need
+
+
+def test_sort_and_unpack_validation():
+    L = moe.lib()
+    assert L.moe_sort_by_expert(0x1000, 4, 0, 8, 0x2000, 0x3000, 0x4000, 0x5000, 1 << 20, None) == moe.MOE_EINVAL
+    assert L.moe_sort_by_expert(0x1000, 4, 2, 2048, 0x2000, 0x3000, 0x4000, 0x5000, 1 << 20, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_sort_by_expert(0x1002, 4, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 1 << 20, None) == moe.MOE_EALIGN
+    assert L.moe_sort_by_expert(0x1000, 4, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 1, None) == moe.MOE_EWORKSPACE
+    assert L.moe_sort_by_expert(0x1000, 0, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 1 << 20, None) == moe.MOE_OK
+    assert L.moe_sort_workspace_bytes(2048, 10, 512) > 0
+    assert L.moe_q2_unpack(0x1000, 4, 48, 0x2000, None) == moe.MOE_EINVAL
+    assert L.moe_q2_unpack(0x1008, 4, 64, 0x2000, None) == moe.MOE_EALIGN
+    assert L.moe_q2_unpack(None, 4, 64, 0x2000, None) == moe.MOE_EINVAL
+
+
+# ---------------------------------------------------------------- packer
+
+def _decode_physical(packed, rows, cols):
+    """Split a packed matrix by the layout documented in include/moe.h."""
+    nc = rows * cols // 4
+    codes = packed[:nc].reshape(rows, cols // 4)
+    sm = packed[nc:nc + rows * cols // 8].view(np.uint16).reshape(rows, cols // 32, 2)
+    return codes, sm[..., 0], sm[..., 1]
+
+
+def test_packed_bytes_formula():
+    assert moe.q2_packed_bytes(512, 2048) == 393216
+    assert moe.q2_packed_bytes(2048, 512) == 393216
+    assert moe.q2_packed_bytes(1, 32) == 256
+    assert moe.q2_packed_bytes(3, 64) == 256
+    assert moe.q2_packed_bytes(1, 48) == 0
+    assert moe.q2_packed_bytes(0, 64) == 0
+
+
+def _adversarial_blocks(rng):
+    blocks = []
+    blocks.append(np.full(32, 0.0123, np.float32))                       # constant, not fp16-exact
+    blocks.append(np.full(32, 0.5, np.float32))                          # constant, fp16-exact
+    blocks.append(np.full(32, 0.99999, np.float32))                      # min rounds up -> negative step
+    blocks.append((np.arange(32) % 4 * 2.0 ** -6 - 2.0 ** -5).astype(np.float32))   # exact codes
+    b = np.zeros(32, np.float32)
+    b[0] = 1e-7                                                          # subnormal fp16 step
+    blocks.append(b)
+    blocks.append((rng.standard_normal(32) * 1e-6).astype(np.float32))   # tiny range
+    blocks.append((rng.standard_normal(32) * 100).astype(np.float32))    # large range
+    # values landing exactly half-way between codes
+    s, m = 2.0 ** -7, -0.25
+    b = (m + s * np.array([0, 3] + [0.5, 1.5, 2.5] * 10)).astype(np.float32)
+    blocks.append(b)
+    blocks.append(np.linspace(-3e4, 3e4, 32, dtype=np.float32))         # near the fp16 range
+    return np.stack(blocks)
+
+
+def test_packer_equals_oracle_quantizer():
+    rng = np.random.default_rng(21)
+    mats = [
+        (rng.standard_normal((64, 512)) * 0.02).astype(np.float32),
+        (rng.standard_normal((16, 2048)) * 0.02).astype(np.float32),
+        _adversarial_blocks(rng).reshape(-1, 32),
+        _adversarial_blocks(rng).reshape(3, 96),
+        (rng.uniform(-1, 1, (8, 256)) * 2.0 ** rng.integers(-20, 10, (8, 1))).astype(np.float32),
+    ]
+    for w in mats:
+        rows, cols = w.shape
+        packed = moe.q2_pack(w)
+        assert packed.nbytes == moe.q2_packed_bytes(rows, cols)
+        codes, scale, minv = _decode_physical(packed, rows, cols)
+        q = oracle.q2_quantize(w)
+        np.testing.assert_array_equal(codes, q.codes)
+        np.testing.assert_array_equal(scale, q.scale)
+        np.testing.assert_array_equal(minv, q.minv)
+        used = rows * cols * 3 // 8
+        assert np.all(packed[used:] == 0)
+
+
+def test_packer_rejects_bad_input():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 3] = np.nan
+    with pytest.raises(moe.MoEError) as e:
+        moe.q2_pack(w)
+    assert e.value.status == moe.MOE_ENONFINITE
+    w[1, 3] = 1e6                                                # min/scale out of fp16 range
+    with pytest.raises(moe.MoEError) as e:
+        moe.q2_pack(w)
+    assert e.value.status == moe.MOE_ENONFINITE
+    L = moe.lib()
+    src = np.zeros((2, 64), np.float32)
+    dst = np.zeros(16, np.uint8)
+    assert L.moe_q2_pack(src.ctypes.data, 2, 64, dst.ctypes.data, 16) == moe.MOE_EWORKSPACE
+    assert L.moe_q2_pack(src.ctypes.data, 2, 48, dst.ctypes.data, 1 << 20) == moe.MOE_EINVAL

@@ -1,0 +1,359 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: router ids bit-identical (ordered), wts / gate / y within
+|gpu - oracle| <= 1e-4 + 2e-3 |oracle| elementwise, 2-bit unpack bit-exact,
+grouping (counting sort) bit-exact. Full-size workloads run in the same
+launch configuration the benchmark times (back-to-back calls on one stream);
+routing is checked on every row, y on every row the oracle finishes quickly.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from _layers import (assert_parity, gpu_layer_from_arrays, gpu_layer_from_config, load_hand_fixture,
+                     oracle_layer_from_arrays, oracle_layer_from_config, run_calls, tolerance_ok)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_moe_decode_amd as moe
+    moe.lib()   # fails loudly if the library is not built
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_ref(L, x):
+    ids, wts, gate, y, y64 = L.forward(x)
+    return ids, wts, gate, y64
+
+
+def _random_arrays(rng, H, E, K, I, Is, rstd=0.05, estd=0.05):
+    return dict(H=H, E=E, K=K, I=I, Is=Is,
+                router_w=(rng.standard_normal((E, H)) * rstd).astype(np.float32),
+                gate_vec=(rng.standard_normal(H) * rstd).astype(np.float32), router_bias=None,
+                exp_gate=(rng.standard_normal((E, I, H)) * estd).astype(np.float32),
+                exp_up=(rng.standard_normal((E, I, H)) * estd).astype(np.float32),
+                exp_down=(rng.standard_normal((E, H, I)) * estd).astype(np.float32),
+                sh_gate=(rng.standard_normal((Is, H)) * estd).astype(np.float32),
+                sh_up=(rng.standard_normal((Is, H)) * estd).astype(np.float32),
+                sh_down=(rng.standard_normal((H, Is)) * estd).astype(np.float32))
+
+
+# ------------------------------------------------------------- small cases
+
+def test_hand_fixture():
+    _say("case: hand fixture H=32 E=4 K=2")
+    a, exp = load_hand_fixture()
+    G = gpu_layer_from_arrays(a)
+    ids, wts, gate, y = run_calls(G, a["x"], 1)
+    np.testing.assert_array_equal(ids[0], exp["ids"])
+    assert tolerance_ok(wts[0], exp["wts"]).all()
+    assert tolerance_ok(gate[0], exp["gate"]).all()
+    assert tolerance_ok(y[0], exp["y"]).all(), (y[0][:4], exp["y"][:4])
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4])
+def test_tiny_fp32_workload(rows):
+    _say(f"case: tiny fp32 workload, {rows} rows per call")
+    cfg = mi.CONFIGS[0]
+    dense = mi.dense_weights(cfg)
+    stacks = mi.expert_stacks(cfg)
+    G = gpu_layer_from_config(cfg, dense, stacks)
+    L = oracle_layer_from_config(cfg, dense=dense, stacks=stacks)
+    x = mi.activations(cfg, T=64 + rows - 1)
+    got = run_calls(G, x, rows)
+    assert_parity(got, _oracle_ref(L, x), f"tiny rows={rows}")
+
+
+def test_route_only_entry_point():
+    _say("case: moe_route on the tiny workload")
+    cfg = mi.CONFIGS[0]
+    dense = mi.dense_weights(cfg)
+    G = gpu_layer_from_config(cfg, dense, mi.expert_stacks(cfg))
+    L = oracle_layer_from_config(cfg, dense=dense, experts=[])
+    x = mi.activations(cfg, T=37)
+    ids, wts, gate = G.route(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    ri, rw, rg, _ = L.route(x)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ri)
+    assert tolerance_ok(wts.cpu().numpy(), rw).all()
+    assert tolerance_ok(gate.cpu().numpy(), rg).all()
+
+
+def test_duplicate_router_rows_tie_on_gpu():
+    """Bit-equal logits from duplicated router rows: the lower id must win
+    on the GPU exactly as in the oracle, at every boundary position."""
+    _say("case: exact-tie fixture")
+    rng = np.random.default_rng(31)
+    H, E, K = 256, 64, 6
+    a = _random_arrays(rng, H, E, K, 64, 64)
+    # pairs of identical rows across the whole expert range
+    for lo, hi in [(1, 40), (5, 6), (10, 63), (20, 21), (33, 50)]:
+        a["router_w"][hi] = a["router_w"][lo]
+    x = rng.standard_normal((200, H)).astype(np.float32)
+    L = oracle_layer_from_arrays(a)
+    ri, _, _, logits = L.route(x)
+    G = gpu_layer_from_arrays(a)
+    got = run_calls(G, x, 1)
+    np.testing.assert_array_equal(got[0], ri)
+    assert_parity(got, _oracle_ref(L, x), "tie fixture")
+
+
+@pytest.mark.parametrize("case", ["k_equals_e", "single_expert", "no_renorm", "bias", "zero_x", "wide"])
+def test_edge_shapes(case):
+    _say(f"case: edge {case}")
+    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    renorm = 1
+    if case == "k_equals_e":
+        a = _random_arrays(rng, 64, 8, 8, 32, 32)
+    elif case == "single_expert":
+        a = _random_arrays(rng, 96, 1, 1, 64, 32)
+    elif case == "no_renorm":
+        a = _random_arrays(rng, 128, 32, 5, 64, 96)
+        renorm = 0
+    elif case == "bias":
+        a = _random_arrays(rng, 128, 48, 7, 32, 64)
+        a["router_bias"] = rng.standard_normal(48).astype(np.float32)
+    elif case == "zero_x":
+        a = _random_arrays(rng, 64, 16, 4, 32, 32)
+    else:   # wide: K = 16, E = 1024, odd intermediate sizes
+        a = _random_arrays(rng, 256, 1024, 16, 96, 160, rstd=0.1)
+    T = 9
+    x = rng.standard_normal((T, a["H"])).astype(np.float32)
+    if case == "zero_x":
+        x[:] = 0
+    L = oracle_layer_from_arrays(a, renormalize=renorm)
+    G = gpu_layer_from_arrays(a, renormalize=renorm)
+    ref = _oracle_ref(L, x)
+    for rows in (1, 3, 4):
+        assert_parity(run_calls(G, x, rows), ref, f"{case} rows={rows}")
+
+
+def test_bf16_and_q2_small_shapes():
+    """bf16 router/shared with bf16 and 2-bit experts at small, ragged sizes."""
+    rng = np.random.default_rng(41)
+    a = _random_arrays(rng, 320, 24, 5, 96, 64, rstd=0.05, estd=0.05)
+    b = dict(a)
+    for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+        b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    x = rng.standard_normal((11, 320)).astype(np.float32)
+    _say("case: small bf16 experts")
+    L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    ref = _oracle_ref(L, x)
+    for rows in (1, 2, 4):
+        assert_parity(run_calls(G, x, rows), ref, f"bf16 rows={rows}")
+    _say("case: small 2-bit experts")
+    import oracle
+    q = dict(b)
+    q["exp_gate"] = [oracle.q2_quantize(m) for m in a["exp_gate"]]
+    q["exp_up"] = [oracle.q2_quantize(m) for m in a["exp_up"]]
+    q["exp_down"] = [oracle.q2_quantize(m) for m in a["exp_down"]]
+    Lq = oracle_layer_from_arrays(q, router_t="bf16", expert_t="q2", shared_t="bf16")
+    Gq = gpu_layer_from_arrays(dict(b, exp_gate=a["exp_gate"], exp_up=a["exp_up"], exp_down=a["exp_down"]),
+                               router_t="bf16", expert_t="q2", shared_t="bf16")
+    ref = _oracle_ref(Lq, x)
+    for rows in (1, 3):
+        assert_parity(run_calls(Gq, x, rows), ref, f"q2 rows={rows}")
+
+
+def test_given_routing_entry():
+    """moe_forward with ids_in/wts_in/gate_in uses the routing as given."""
+    _say("case: caller-supplied routing")
+    rng = np.random.default_rng(51)
+    a = _random_arrays(rng, 128, 16, 3, 64, 64)
+    x = rng.standard_normal((4, 128)).astype(np.float32)
+    L = oracle_layer_from_arrays(a)
+    ri, rw, rg, y, y64 = L.forward(x)
+    G = gpu_layer_from_arrays(a)
+    import sparse_moe_decode_amd as moe
+    xt = torch.from_numpy(x).cuda()
+    ids = torch.from_numpy(ri).cuda()
+    wts = torch.from_numpy(rw.astype(np.float32)).cuda()
+    gate = torch.from_numpy(rg.astype(np.float32)).cuda()
+    for rows in (1, 2, 4):
+        out = torch.empty((4, 128), dtype=torch.float32, device="cuda")
+        ws = G.workspace(rows)
+        for t in range(0, 4, rows):
+            moe.forward(G.desc, xt[t:t + rows], out[t:t + rows], ws, ids_in=ids[t:t + rows],
+                        wts_in=wts[t:t + rows], gate_in=gate[t:t + rows])
+        torch.cuda.synchronize()
+        assert tolerance_ok(out.cpu().numpy(), y64).all()
+
+
+# ------------------------------------------------------------ 2-bit format
+
+def test_q2_unpack_bit_exact_random_bytes():
+    """Random codes and random finite fp16 scale/min patterns (subnormals
+    included): the device unpack equals the oracle's dequantizer bit for bit."""
+    _say("case: q2 unpack random bytes")
+    import oracle
+    import sparse_moe_decode_amd as moe
+    rng = np.random.default_rng(61)
+    rows, cols = 96, 1024
+    nb = cols // 32
+    codes = rng.integers(0, 256, (rows, cols // 4), dtype=np.uint8)
+    bits = rng.integers(0, 0x7c00, (rows, nb, 2), dtype=np.uint16)     # finite magnitudes
+    bits |= (rng.integers(0, 2, (rows, nb, 2), dtype=np.uint16) << 15)
+    packed = np.zeros(moe.q2_packed_bytes(rows, cols), np.uint8)
+    packed[: rows * cols // 4] = codes.reshape(-1)
+    packed[rows * cols // 4: rows * cols * 3 // 8] = bits.reshape(-1).view(np.uint8)
+    ref = oracle.q2_dequantize(oracle.Q2(codes, bits[..., 0].copy(), bits[..., 1].copy(), rows, cols))
+    dev = torch.from_numpy(packed).cuda()
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    moe.q2_unpack(dev, rows, cols, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_q2_unpack_of_packed_expert_weights():
+    _say("case: q2 unpack of packed expert matrices")
+    import oracle
+    import sparse_moe_decode_amd as moe
+    cfg = mi.CONFIGS[2]
+    for e, m in [(0, mi.MAT_GATE), (7, mi.MAT_DOWN)]:
+        w = mi.expert_matrix_f32(cfg, e, m)
+        rows, cols = w.shape
+        dev = torch.from_numpy(moe.q2_pack(w)).cuda()
+        out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+        moe.q2_unpack(dev, rows, cols, out)
+        torch.cuda.synchronize()
+        ref = oracle.q2_dequantize(oracle.q2_quantize(w))
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- grouping
+
+@pytest.mark.parametrize("T,K,E,skew", [(2048, 10, 512, True), (5, 3, 8, False), (1, 1, 1, False),
+                                        (3000, 16, 1024, True), (777, 10, 512, False)])
+def test_sort_by_expert(T, K, E, skew):
+    _say(f"case: sort T={T} K={K} E={E}")
+    import sparse_moe_decode_amd as moe
+    rng = np.random.default_rng(T * 31 + K)
+    p = rng.dirichlet(np.full(E, 0.3 if skew else 5.0))
+    ids = np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    dev = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(moe.sort_workspace_bytes(T, K, E), dtype=torch.uint8, device="cuda")
+    for _ in range(2):   # the second call checks the self-resetting ticket
+        moe.sort_by_expert(dev, E, counts, offsets, perm, ws)
+        torch.cuda.synchronize()
+        flat = ids.reshape(-1)
+        ref_perm = np.argsort(flat, kind="stable")
+        ref_counts = np.bincount(flat, minlength=E)
+        np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts)
+        np.testing.assert_array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(ref_counts)]))
+        np.testing.assert_array_equal(perm.cpu().numpy(), ref_perm)
+
+
+# ------------------------------------------------------- full-size workloads
+
+@pytest.fixture(scope="module")
+def decode_bf16():
+    cfg = mi.CONFIGS[1]
+    dense = mi.dense_weights(cfg)
+    stacks = mi.expert_stacks(cfg)
+    return cfg, dense, stacks, gpu_layer_from_config(cfg, dense, stacks)
+
+
+@pytest.fixture(scope="module")
+def decode_q2():
+    cfg = mi.CONFIGS[2]
+    dense = mi.dense_weights(cfg)
+    return cfg, dense, gpu_layer_from_config(cfg, dense)
+
+
+def _oracle_rows(cfg, dense, x, ids_gpu, rows, stacks=None):
+    """Oracle on a sample of rows, with only the experts those rows need."""
+    need = set(np.unique(ids_gpu[rows]).tolist())
+    L = oracle_layer_from_config(cfg, dense=dense, experts=need, stacks=stacks)
+    return _oracle_ref(L, x[rows])
+
+
+def test_decode_bf16_full(decode_bf16):
+    cfg, dense, stacks, G = decode_bf16
+    _say(f"case: {cfg.name} T={cfg.T} one row per call")
+    x = mi.activations(cfg)
+    got = run_calls(G, x, 1)
+    Lr = oracle_layer_from_config(cfg, dense=dense, experts=[], stacks=stacks)
+    ri, rw, rg, _ = Lr.route(x)
+    np.testing.assert_array_equal(got[0], ri)
+    rows = np.arange(0, cfg.T, 4)
+    ref = _oracle_rows(cfg, dense, x, got[0], rows, stacks)
+    err = assert_parity(got, ref, cfg.name, rows)
+    _say(f"{cfg.name}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
+def test_decode_q2_full(decode_q2):
+    cfg, dense, G = decode_q2
+    _say(f"case: {cfg.name} T={cfg.T} one row per call")
+    x = mi.activations(cfg)
+    got = run_calls(G, x, 1)
+    Lr = oracle_layer_from_config(cfg, dense=dense, experts=[])
+    ri, rw, rg, _ = Lr.route(x)
+    np.testing.assert_array_equal(got[0], ri)
+    rows = np.arange(0, cfg.T, 5)
+    ref = _oracle_rows(cfg, dense, x, got[0], rows)
+    err = assert_parity(got, ref, cfg.name, rows)
+    _say(f"{cfg.name}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
+@pytest.mark.parametrize("R", [2, 3])
+def test_fewrow_q2_full(R):
+    cfg = mi.CONFIGS[3].with_(rows_per_call=R)
+    _say(f"case: {cfg.name} R={R}")
+    dense = mi.dense_weights(cfg)
+    G = gpu_layer_from_config(cfg, dense)
+    calls = 500 if R == 2 else 333
+    x = mi.activations(cfg, T=calls * R, instance=R)
+    got = run_calls(G, x, R)
+    Lr = oracle_layer_from_config(cfg, dense=dense, experts=[])
+    ri, _, _, _ = Lr.route(x)
+    np.testing.assert_array_equal(got[0], ri)
+    rows = np.arange(0, x.shape[0], 6)
+    ref = _oracle_rows(cfg, dense, x, got[0], rows)
+    assert_parity(got, ref, f"{cfg.name} R={R}", rows)
+    # rows of a few-row call equal the same rows decoded one at a time
+    single = run_calls(G, x[:60], 1)
+    np.testing.assert_array_equal(single[0], got[0][:60])
+    assert tolerance_ok(got[3][:60], single[3]).all()
+
+
+def test_prefill_q2_full():
+    cfg = mi.CONFIGS[4]
+    _say(f"case: {cfg.name} T={cfg.T}")
+    dense = mi.dense_weights(cfg)
+    G = gpu_layer_from_config(cfg, dense)
+    x = mi.activations(cfg)
+    got = run_calls(G, x, cfg.T)
+    Lr = oracle_layer_from_config(cfg, dense=dense, experts=[])
+    ri, _, _, _ = Lr.route(x)
+    np.testing.assert_array_equal(got[0], ri)
+    rows = np.arange(0, cfg.T, 8)
+    ref = _oracle_rows(cfg, dense, x, got[0], rows)
+    err = assert_parity(got, ref, cfg.name, rows)
+    _say(f"{cfg.name}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
+def test_determinism(decode_q2):
+    cfg, dense, G = decode_q2
+    _say("case: run-to-run determinism")
+    x = mi.activations(cfg, T=64)
+    a = run_calls(G, x, 1)
+    b = run_calls(G, x, 1)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
