@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X sparse MoE layer: decode tokens/s and % of HBM roofline.
+
+Workload (default): real-shape decode with bf16 weights - hidden 2048, 512
+routed experts, top-10 renormalized, expert intermediate 512, one shared
+expert with a sigmoid gate, 1000 seeded tokens, one token per call, calls
+back to back on one stream. A step is one pass of the 1000-token stream
+through the layer. Dense weights (router, gate vector, shared expert) rotate
+over 48 layer instances so they are re-read from HBM as in a 48-layer model;
+routed experts (3.2 GB) are shared by the instances. The calls are captured
+once into a HIP graph and replayed; the timed region is K replays bracketed
+by device synchronizations and HIP events on the replay stream.
+
+Prints one JSON line. `roofline` covers the decode layer kernel(s):
+algorithmic bytes per call (selected experts, shared expert, router, gate
+vector, x, y, routing outputs) / measured time per call. `cpu_baseline` is
+the plain double-precision CPU oracle on a bounded sample of the same tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+# ------------------------------------------------------------ byte models
+
+def wbytes(fmt: str, rows: int, cols: int) -> int:
+    if fmt == "f32":
+        return rows * cols * 4
+    if fmt == "bf16":
+        return rows * cols * 2
+    return rows * cols * 3 // 8        # 2-bit blocks: 12 bytes per 32 weights
+
+
+def expert_bytes(cfg) -> int:
+    return 2 * wbytes(cfg.expert_t, cfg.I, cfg.H) + wbytes(cfg.expert_t, cfg.H, cfg.I)
+
+
+def dense_bytes(cfg) -> int:
+    return (wbytes(cfg.router_t, cfg.E, cfg.H) + wbytes(cfg.router_t, 1, cfg.H)
+            + 2 * wbytes(cfg.shared_t, cfg.Is, cfg.H) + wbytes(cfg.shared_t, cfg.H, cfg.Is)
+            + (cfg.E * 4 if cfg.bias_std > 0 else 0))
+
+
+def call_bytes(cfg, rows: int, n_union: float) -> float:
+    """Algorithmic bytes of one call: each distinct selected expert once, the
+    dense weights once, x and y, and the routing outputs."""
+    return (n_union * expert_bytes(cfg) + dense_bytes(cfg) + 2 * rows * cfg.H * 4
+            + rows * (cfg.K * 8 + 4))
+
+
+# ------------------------------------------------------------- workload
+
+class Workload:
+    """Device-resident layer instances, the token stream and a captured graph."""
+
+    def __init__(self, cfg, rows_per_call: int, ncalls: int, rotate: int, x_instance: int = 0):
+        import torch
+
+        self.cfg, self.R, self.ncalls, self.rotate = cfg, rows_per_call, ncalls, rotate
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from _layers import gpu_layer_from_config
+        self.dense0 = mi.dense_weights(cfg)
+        self.stacks = mi.expert_stacks(cfg) if cfg.expert_t != "q2" else None
+        base = gpu_layer_from_config(cfg, self.dense0, self.stacks)
+        self.layers = [base]
+        for i in range(1, rotate):
+            d = mi.dense_weights(mi.layer_instance(cfg, i))
+            self.layers.append(base.with_dense(**d))
+        T = rows_per_call * ncalls
+        self.x_host = mi.activations(cfg, T=T, instance=x_instance)
+        self.x = torch.from_numpy(self.x_host).cuda()
+        self.y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+        self.ids = torch.empty((T, cfg.K), dtype=torch.int32, device="cuda")
+        self.wts = torch.empty((T, cfg.K), dtype=torch.float32, device="cuda")
+        self.gate = torch.empty((T,), dtype=torch.float32, device="cuda")
+        self.ws = base.workspace(rows_per_call)
+        self.graph = None
+
+    def run_calls(self):
+        import sparse_moe_decode_amd as moe
+        R = self.R
+        for c in range(self.ncalls):
+            L = self.layers[c % self.rotate]
+            s = slice(c * R, (c + 1) * R)
+            moe.forward(L.desc, self.x[s], self.y[s], self.ws, ids_out=self.ids[s], wts_out=self.wts[s],
+                        gate_out=self.gate[s])
+
+    def capture(self):
+        import torch
+        self.run_calls()                       # eager pass (also warms up the code objects)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_calls()
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def step(self):
+        self.graph.replay()
+
+    def union_sizes(self):
+        ids = self.ids.cpu().numpy().reshape(self.ncalls, self.R * self.cfg.K)
+        return np.array([len(np.unique(r)) for r in ids], np.float64)
+
+
+def time_steps(wl, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        wl.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def traffic_for(kernel_key: str, cfg_name: str):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel_key}:{cfg_name}")
+    if not rec:
+        return None
+    if rec.get("source_sha") != source_sha():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, seconds: float):
+    """The CPU oracle, as it stands, on the first tokens of the stream with all
+    available host cores (OpenMP over tokens), for about `seconds`."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from _layers import oracle_layer_from_config
+    cfg = wl.cfg
+    L = oracle_layer_from_config(cfg, dense=wl.dense0, stacks=wl.stacks)
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    oracle.set_threads(cores)
+    threads = oracle.max_threads()
+    done, chunk = 0, 4 * threads
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and done < wl.x_host.shape[0]:
+        n = min(chunk, wl.x_host.shape[0] - done)
+        L.forward(wl.x_host[done:done + n])
+        done += n
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} tokens of the {cfg.name} stream (layer instance 0), {dt:.1f} s, "
+                      f"double-precision oracle, OpenMP over tokens; CPU: {cpu}"}
+
+
+# ------------------------------------------------------------------ main
+
+def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0):
+    wl = Workload(cfg, rows, ncalls, rotate, x_instance)
+    wl.capture()
+    ms, wall = time_steps(wl, steps, warmup)
+    return wl, ms, wall
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rotate", type=int, default=48, help="layer instances for the dense weights")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single "
+              f"MI355X in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_moe_decode_amd as moe
+    moe.lib()                                     # fails loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    cfg = mi.CONFIGS[1]
+    print(f"[bench] building {cfg.name} workload, {args.rotate} dense-weight instances", file=sys.stderr, flush=True)
+    wl, ms, wall = measure(cfg, 1, cfg.T, args.rotate, args.steps, args.warmup)
+    tokens = cfg.T
+    tok_s = tokens / (ms / 1e3)
+    per_call_s = ms / 1e3 / tokens
+    bytes_call = call_bytes(cfg, 1, cfg.K + 0.0)
+    achieved = bytes_call / per_call_s / 1e9
+    print(f"[bench] {cfg.name}: {ms:.3f} ms/step, {tok_s:.0f} tok/s, {achieved:.0f} GB/s", file=sys.stderr,
+          flush=True)
+
+    extra = {}
+    if args.rotate != 1:
+        wl1, ms1, _ = measure(cfg, 1, 200, 1, args.steps, args.warmup)
+        extra["decode_bf16_single_instance"] = {
+            "tokens_per_s": round(200 / (ms1 / 1e3), 1),
+            "us_per_token": round(ms1 * 1e3 / 200, 3),
+            "GBps": round(call_bytes(cfg, 1, cfg.K) / (ms1 / 1e3 / 200) / 1e9, 1)}
+        del wl1
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        for key, idx, rows, ncalls in [("decode_q2", 2, 1, 1000), ("fewrow_q2_R2", 3, 2, 500),
+                                       ("fewrow_q2_R3", 3, 3, 333), ("prefill_q2", 4, 2048, 1)]:
+            c = mi.CONFIGS[idx].with_(rows_per_call=rows)
+            print(f"[bench] {key}", file=sys.stderr, flush=True)
+            w2, m2, _ = measure(c, rows, ncalls, args.rotate if rows < 2048 else 1,
+                                max(2, args.steps // 2), 1, x_instance=rows if idx == 3 else 0)
+            u = w2.union_sizes()
+            per_call = m2 / 1e3 / ncalls
+            rec = {"ms_per_step": round(m2, 4), "calls": ncalls, "rows_per_call": rows,
+                   "rows_per_s": round(rows * ncalls / (m2 / 1e3), 1), "us_per_call": round(per_call * 1e6, 3)}
+            if rows < 2048:
+                b = float(np.mean([call_bytes(c, rows, n) for n in u]))
+                rec.update({"bytes_per_call": round(b), "mean_expert_union": round(float(u.mean()), 3),
+                            "GBps": round(b / per_call / 1e9, 1),
+                            "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4)})
+            else:
+                flops = 2.0 * rows * (cfg.K * 3 * cfg.H * cfg.I + 3 * cfg.H * cfg.Is + cfg.E * cfg.H)
+                rec.update({"useful_GFLOP": round(flops / 1e9, 2),
+                            "TFLOPs": round(flops / per_call / 1e12, 2),
+                            "mfma_frac": round(flops / per_call / 1e12 / BF16_PEAK_TFLOPS, 4)})
+            extra[key] = rec
+            del w2
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": "MoE-layer decode tokens/s and % of HBM roofline (expert bytes read/s)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bf16: Qwen3-Next-shape MoE layer, hidden 2048, 512 experts, top-10, "
+                               "inter 512, shared expert 512 + sigmoid gate, bf16 weights, fp32 activations; "
+                               "1000 tokens, 1 token per call",
+                   "global_batch": 1, "seq_len": 1, "tokens_per_step": tokens,
+                   "dense_weight_instances": args.rotate, "timing": "HIP graph replay of 1000 calls"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("decode", cfg.name),
+                     "bytes_per_call": bytes_call, "us_per_call": round(per_call_s * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

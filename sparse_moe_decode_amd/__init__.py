@@ -199,6 +199,30 @@ class Layer:
                               _ptr(self.exp_gate), _ptr(self.exp_up), _ptr(self.exp_down),
                               _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down))
 
+    def with_dense(self, *, router_w, gate_vec, router_bias, sh_gate, sh_up, sh_down) -> "Layer":
+        """Another layer of the same shape that shares this layer's routed
+        experts but has its own router, gate vector and shared expert."""
+        import torch
+        other = object.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+
+        def up(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(self.device)
+
+        other.router_w, other.gate_vec = up(router_w), up(gate_vec)
+        other.router_bias = up(None if router_bias is None else np.asarray(router_bias, np.float32))
+        other.sh_gate, other.sh_up, other.sh_down = up(sh_gate), up(sh_up), up(sh_down)
+        d = LayerDesc()
+        C.memmove(C.byref(d), C.byref(self.desc), C.sizeof(LayerDesc))
+        d.router_w, d.shared_gate_w = _ptr(other.router_w), _ptr(other.gate_vec)
+        d.router_bias = _ptr(other.router_bias)
+        d.sh_gate, d.sh_up, d.sh_down = _ptr(other.sh_gate), _ptr(other.sh_up), _ptr(other.sh_down)
+        other.desc = d
+        return other
+
     def _pack_stack(self, source, mat, rows, cols):
         import torch
         from concurrent.futures import ThreadPoolExecutor

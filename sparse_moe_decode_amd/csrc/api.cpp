@@ -49,12 +49,15 @@ int validate_desc(const moe_layer_desc *d)
     return MOE_OK;
 }
 
-// Rows per decode / few-row launch: x of all rows (plus 2-bit block sums) is
-// staged in LDS, kept within 32 KiB + 1 KiB.
+// Rows per decode / few-row launch: the gate/up kernel stages x of all rows
+// (plus 2-bit block sums) and their router logits in LDS; keep that, with the
+// kernel's static routing state, within 60 KiB.
 int max_rows(const moe_layer_desc *d)
 {
-    const int r = 8192 / d->hidden;
-    return r < moe::kMaxRows ? (r < 1 ? 1 : r) : moe::kMaxRows;
+    for (int r = moe::kMaxRows; r > 1; --r)
+        if (moe::gateup_lds_bytes(r, d->hidden, d->n_experts) + 4096 <= 60u * 1024u)
+            return r;
+    return 1;
 }
 
 Path choose_path(int T)

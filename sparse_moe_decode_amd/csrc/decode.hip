@@ -1,21 +1,25 @@
 // Decode (1 row) and few-row (2..4 rows) path of the sparse MoE layer on gfx950.
 //
-// Three launches per call, all on the caller's stream:
-//   k_route   router logits (fp64 accumulation) + shared-gate logit, then the
-//             last-arriving workgroup runs the wave-level top-K, the softmax
-//             weights, the sigmoid gate and builds the slot table (the union
-//             of the rows' experts; slot 0 is the shared expert, weighted by
-//             the gate - the "extra slot" design of the Research notes page,
-//             section 1, "Metal").
-//   k_gateup  one wave per (slot, intermediate channel): gate and up rows
-//             read once with 16-byte loads, dotted with every row's x,
-//             SwiGLU, scaled by the row's route weight -> hbuf.
-//   k_down    each wave owns output rows j and sums D_s[j] . hbuf_s over all
-//             slots: the weighted combine happens inside the dot, no partial
-//             results leave the chip, every y element is written once.
-// Each selected expert is read exactly once per call, whatever the number of
-// rows that selected it (the few-row idea of the Research notes page,
-// section 1, MTP "Verify" entry).
+// Four launches per call on the caller's stream; kernel boundaries are the
+// only synchronization (no cross-workgroup fences, counters or spin waits):
+//   k_dense          the routing-independent work: router logits in fp64
+//                    (products of bf16/fp32 weights with fp32 activations are
+//                    exact in double) plus the shared-gate logit, and the
+//                    shared expert's SwiGLU activations.
+//   k_route          one workgroup: exact top-K per row (one wave per row),
+//                    softmax weights over the selection, sigmoid gate, and the
+//                    slot table - the union of the rows' experts, slot 0 being
+//                    the shared expert weighted by the gate (router, top-k and
+//                    shared gate as one step, the shared expert as an extra
+//                    slot: Research notes page, section 1, "Metal").
+//   k_gateup_routed  two intermediate channels per wave of one selected
+//                    expert: gate and up rows streamed with 16-byte loads,
+//                    SwiGLU, scaled by the row's route weight.
+//   k_down           one output row per wave: D_s[j] . h'_s summed over all
+//                    slots, so the weighted combine happens inside the dot
+//                    product and each y element is written once.
+// Each distinct selected expert is read once per call, however many rows
+// selected it (the few-row verify idea of the same page, section 1).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -26,313 +30,417 @@
 
 namespace moe {
 
-// ============================================================== route
+// ================================================================ routing
 
-struct RouteArgs {
-    const float *x;          // [R][H]
-    int H, E, K, renorm;
-    const uint8_t *router_w; // [E][H]
-    const float *bias;       // [E] or null
-    const uint8_t *gate_w;   // [H]
-    int32_t *ids_out;        // [R][K] or null
-    float *wts_out;          // [R][K] or null
-    float *gate_out;         // [R] or null
-    DecodeWs ws;
-    int rows_per_wave;
+// Routing state of up to kMaxRows rows, in LDS.
+struct RouteLds {
+    int sel_e[kMaxRows][kMaxK];
+    double sel_l[kMaxRows][kMaxK];
+    float sel_w[kMaxRows][kMaxK];
+    double ex[kMaxRows][kMaxK];
+    int cand[kMaxRows][kWave];
+    float g[kMaxRows];
+    SlotTable slots;
 };
 
-// fp64 dot of router row `row` with each staged x row. Products of a bf16 or
-// fp32 weight with an fp32 activation are exact in double.
-template <int R>
-__device__ __forceinline__ void router_dot(F32, const uint8_t *row, int H, const float *xs, int lane,
-                                           double (&acc)[R])
+// Order-preserving integer key of a float: a > b iff key(a) > key(b).
+__device__ __forceinline__ uint32_t f32_key(float v)
 {
-    const int nch = H >> 2;
-    for (int c = lane; c < nch; c += kWave) {
-        const float4 w = *reinterpret_cast<const float4 *>(row + c * 16);
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 xv = *reinterpret_cast<const float4 *>(xs + q * H + c * 4);
-            acc[q] = fma(static_cast<double>(w.x), static_cast<double>(xv.x), acc[q]);
-            acc[q] = fma(static_cast<double>(w.y), static_cast<double>(xv.y), acc[q]);
-            acc[q] = fma(static_cast<double>(w.z), static_cast<double>(xv.z), acc[q]);
-            acc[q] = fma(static_cast<double>(w.w), static_cast<double>(xv.w), acc[q]);
-        }
-    }
+    const uint32_t u = __float_as_uint(v + 0.0f);   // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int R>
-__device__ __forceinline__ void router_dot(BF16, const uint8_t *row, int H, const float *xs, int lane,
-                                           double (&acc)[R])
+// Top-K of one row of E logits (double, in LDS) by one wave, under the order
+// "logit desc, then id asc". Writes rl.sel_e[q][0..K) and rl.sel_l[q][0..K)
+// in that order. Expert e = lane + 64*m is element m of lane `lane`.
+//  1. Each lane's maximum; the K-th largest lane maximum M is at most the
+//     K-th largest logit (the K lanes above it hold K distinct logits >= M).
+//  2. Candidates: logits whose fp32 rounding is >= fp32(M). Rounding to fp32
+//     is monotone, so every logit of the true top K is a candidate and every
+//     non-candidate is below M, hence below the K-th largest.
+//  3. The candidates are ranked exactly (fp64 compare, then id).
+// The threshold is found by a bitwise binary search whose counts are
+// wave-wide ballots; broadcasts use readlane.
+__device__ inline void wave_select(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
 {
-    const int nch = H >> 3;
-    for (int c = lane; c < nch; c += kWave) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(row + c * 16);
-        const float wf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    constexpr int PL = kMaxE / kWave;
+    const int npl = (E + kWave - 1) / kWave;
+    uint32_t key[PL];
+    uint32_t mk = 0;   // 0 is below every real key
 #pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8);
-            const float4 x1 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8 + 4);
-            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[q] = fma(static_cast<double>(wf[i]), static_cast<double>(xv[i]), acc[q]);
-        }
-    }
-}
-
-// Selection for one row by one wave: K rounds of a wave-wide argmax over
-// (logit desc, id asc). Returns the selected ids / logits in every lane.
-__device__ inline void wave_topk(const double *logits, int E, int K, int lane, int (&sel_id)[kMaxK],
-                                 double (&sel_l)[kMaxK], double &sum_all_exp_shift, bool need_all)
-{
-    constexpr int kPerLane = kMaxE / kWave;   // 16
-    double lv[kPerLane];
-#pragma unroll
-    for (int m = 0; m < kPerLane; ++m) {
+    for (int m = 0; m < PL; ++m) {
         const int e = lane + m * kWave;
-        lv[m] = e < E ? logits[e] : -DBL_MAX;
+        key[m] = 0;
+        if (m < npl && e < E) {
+            key[m] = f32_key(static_cast<float>(lg[e]));
+            mk = key[m] > mk ? key[m] : mk;
+        }
     }
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-        double bv = -DBL_MAX;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int m = 0; m < kPerLane; ++m) {
-            const int e = lane + m * kWave;
-            if (e < E && !((taken >> m) & 1u) && (lv[m] > bv || (lv[m] == bv && e < bi))) {
-                bv = lv[m];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            const double ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        sel_id[k] = bi;
-        sel_l[k] = bv;
-        if ((bi & (kWave - 1)) == lane)
-            taken |= 1u << (bi / kWave);
+    uint32_t t = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        if (__popcll(__ballot(mk >= c)) >= K)
+            t = c;
     }
-    sum_all_exp_shift = 0.0;
-    if (need_all) {
-        double s = 0.0;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int C = 0;
 #pragma unroll
-        for (int m = 0; m < kPerLane; ++m) {
-            const int e = lane + m * kWave;
-            if (e < E)
-                s += exp(lv[m] - sel_l[0]);
+    for (int m = 0; m < PL; ++m) {
+        if (m >= npl)
+            break;
+        const bool cand = key[m] >= t && key[m] != 0;
+        const unsigned long long mask = __ballot(cand);
+        const int pos = C + __popcll(mask & lt);
+        if (cand && pos < kWave)
+            rl.cand[q][pos] = lane + m * kWave;
+        C += __popcll(mask);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (C <= kWave) {
+        const int e = lane < C ? rl.cand[q][lane] : 0;
+        const double v = lane < C ? lg[e] : 0.0;
+        const long long vb = __double_as_longlong(v);
+        const int vlo = static_cast<int>(vb & 0xffffffff), vhi = static_cast<int>(vb >> 32);
+        int rank = 0;
+        for (int j = 0; j < C; ++j) {
+            const unsigned long long bj =
+                (static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(vhi, j))) << 32) |
+                static_cast<uint32_t>(__builtin_amdgcn_readlane(vlo, j));
+            const double vj = __longlong_as_double(static_cast<long long>(bj));
+            const int ej = __builtin_amdgcn_readlane(e, j);
+            rank += (vj > v) | ((vj == v) & (ej < e));
         }
-        for (int off = kWave / 2; off > 0; off >>= 1)
-            s += __shfl_xor(s, off, kWave);
-        sum_all_exp_shift = s;
+        if (lane < C && rank < K) {
+            rl.sel_e[q][rank] = e;
+            rl.sel_l[q][rank] = v;
+        }
+        return;
+    }
+    // many candidates (massive exact ties): rank each against all logits
+    for (int m = 0; m < npl; ++m) {
+        const int e = lane + m * kWave;
+        if (e >= E || key[m] < t)
+            continue;
+        const double v = lg[e];
+        int rank = 0;
+        for (int e2 = 0; e2 < E; ++e2) {
+            const double o = lg[e2];
+            rank += (o > v) | ((o == v) & (e2 < e));
+        }
+        if (rank < K) {
+            rl.sel_e[q][rank] = e;
+            rl.sel_l[q][rank] = v;
+        }
     }
 }
 
-// Slot table from per-row selections held in LDS (sel_e/sel_w [R][K], g[R]).
-template <int R>
-__device__ inline void build_slots(SlotTable *st, const int *sel_e, const float *sel_w, const float *g, int K,
-                                   int lane)
+// Route weights of row q by the wave that selected it, in selection order:
+// w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the selection
+// (renormalized) or over all E logits; the gate sigmoid(z_q).
+__device__ inline void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
+                                    int lane)
 {
+    __builtin_amdgcn_wave_barrier();
+    const double l0 = rl.sel_l[q][0];
+    double v = 0.0;
+    if (lane < K) {
+        v = exp(rl.sel_l[q][lane] - l0);
+        rl.ex[q][lane] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    double denom = 0.0;
+    if (renorm) {
+        for (int j = 0; j < K; ++j)
+            denom += rl.ex[q][j];
+    } else {
+        double s = 0.0;
+        for (int e = lane; e < E; e += kWave)
+            s += exp(lg[e] - l0);
+        denom = lane_group_sum(s, kWave);
+    }
+    if (lane < K)
+        rl.sel_w[q][lane] = static_cast<float>(v / denom);
+    if (lane == 0)
+        rl.g[q] = static_cast<float>(1.0 / (1.0 + exp(-z)));
+}
+
+// Union of the rows' selections: slot 0 is the shared expert (weight g),
+// slots 1.. are the distinct routed experts in order of first appearance
+// (row-major over [R][K]); the weight of a slot for row q is that row's route
+// weight of the expert (0 if the row did not select it). Run by one wave.
+template <int R>
+__device__ inline void build_slots(RouteLds &rl, int K, int lane)
+{
+    if (R == 1) {
+        if (lane < K) {
+            rl.slots.expert[lane + 1] = rl.sel_e[0][lane];
+            rl.slots.w[lane + 1][0] = rl.sel_w[0][lane];
+        }
+        if (lane == 0) {
+            rl.slots.nslots = K + 1;
+            rl.slots.expert[0] = -1;
+            rl.slots.w[0][0] = rl.g[0];
+        }
+        return;
+    }
     const int RK = R * K;
+    const int lq = lane / K, lk = lane - lq * K;
     bool first = false;
     int e = -1;
     if (lane < RK) {
-        e = sel_e[lane];
+        e = rl.sel_e[lq][lk];
         first = true;
-        for (int j = 0; j < lane; ++j)
-            if (sel_e[j] == e)
-                first = false;
+        for (int q = 0; q <= lq; ++q) {
+            const int kend = q < lq ? K : lk;
+            for (int k = 0; k < kend; ++k)
+                first = first && rl.sel_e[q][k] != e;
+        }
     }
     const unsigned long long mask = __ballot(first);
     const int slot = 1 + __popcll(mask & ((1ull << lane) - 1ull));
     if (first) {
-        st->expert[slot] = e;
+        rl.slots.expert[slot] = e;
 #pragma unroll
         for (int q = 0; q < R; ++q) {
             float w = 0.0f;
             for (int k = 0; k < K; ++k)
-                if (sel_e[q * K + k] == e)
-                    w = sel_w[q * K + k];
-            st->w[slot][q] = w;
+                if (rl.sel_e[q][k] == e)
+                    w += rl.sel_w[q][k];
+            rl.slots.w[slot][q] = w;
         }
     }
     if (lane == 0) {
-        st->nslots = 1 + __popcll(mask);
-        st->expert[0] = -1;
+        rl.slots.nslots = 1 + __popcll(mask);
+        rl.slots.expert[0] = -1;
 #pragma unroll
         for (int q = 0; q < R; ++q)
-            st->w[0][q] = g[q];
+            rl.slots.w[0][q] = rl.g[q];
     }
 }
 
-template <int R, typename RT>
-__global__ void __launch_bounds__(256) k_route(RouteArgs a)
-{
-    extern __shared__ float xs[];   // [R][H]
-    const int tid = threadIdx.x;
-    for (int i = tid; i < R * a.H / 4; i += blockDim.x)
-        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(a.x)[i];
-    __syncthreads();
-
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int gwave = blockIdx.x * (blockDim.x / kWave) + wave;
-    const size_t rb = static_cast<size_t>(a.H) * (RT::kChunk == 4 ? 4 : 2);
-    for (int i = 0; i < a.rows_per_wave; ++i) {
-        const int e = gwave * a.rows_per_wave + i;
-        if (e > a.E)
-            break;
-        const uint8_t *row = e < a.E ? a.router_w + e * rb : a.gate_w;
-        double acc[R];
-#pragma unroll
-        for (int q = 0; q < R; ++q)
-            acc[q] = 0.0;
-        router_dot<R>(RT{}, row, a.H, xs, lane, acc);
-#pragma unroll
-        for (int q = 0; q < R; ++q)
-            acc[q] = lane_group_sum(acc[q], kWave);
-        if (lane == 0) {
-#pragma unroll
-            for (int q = 0; q < R; ++q) {
-                if (e < a.E)
-                    a.ws.logits[q * a.E + e] = acc[q] + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
-                else
-                    a.ws.zlogit[q] = acc[q];
-            }
-        }
-    }
-
-    // Last-arriving workgroup does the selection.
-    __shared__ int is_last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned int t = atomicAdd(&a.ws.ctl->route_done, 1u);
-        is_last = (t == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
-
-    __shared__ int sel_e[kMaxRows * kMaxK];
-    __shared__ float sel_w[kMaxRows * kMaxK];
-    __shared__ float gq[kMaxRows];
-    if (wave < R) {
-        const int q = wave;
-        int ids[kMaxK];
-        double ls[kMaxK];
-        double sum_all;
-        const double *lg = a.ws.logits + q * a.E;
-        wave_topk(lg, a.E, a.K, lane, ids, ls, sum_all, a.renorm == 0);
-        double denom = 0.0;
-        if (a.renorm) {
-            for (int k = 0; k < a.K; ++k)
-                denom += exp(ls[k] - ls[0]);
-        } else {
-            denom = sum_all;
-        }
-        const double z = __builtin_nontemporal_load(&a.ws.zlogit[q]);
-        const float g = static_cast<float>(1.0 / (1.0 + exp(-z)));
-        for (int k = 0; k < a.K; ++k) {
-            if (lane == k) {
-                const float w = static_cast<float>(exp(ls[k] - ls[0]) / denom);
-                sel_e[q * a.K + k] = ids[k];
-                sel_w[q * a.K + k] = w;
-                if (a.ids_out)
-                    a.ids_out[q * a.K + k] = ids[k];
-                if (a.wts_out)
-                    a.wts_out[q * a.K + k] = w;
-            }
-        }
-        if (lane == 0) {
-            gq[q] = g;
-            if (a.gate_out)
-                a.gate_out[q] = g;
-        }
-    }
-    __syncthreads();
-    if (wave == 0)
-        build_slots<R>(a.ws.slots, sel_e, sel_w, gq, a.K, lane);
-    if (tid == 0)
-        a.ws.ctl->route_done = 0u;   // every other workgroup has finished with it
-}
-
-// Slot table from routing supplied by the caller.
-// Ids outside [0, E) contribute nothing (they become expert 0 with weight 0).
-template <int R>
-__global__ void __launch_bounds__(64) k_slots_from_routing(const int32_t *ids, const float *wts, const float *gate,
-                                                           int K, int E, SlotTable *st)
-{
-    __shared__ int sel_e[kMaxRows * kMaxK];
-    __shared__ float sel_w[kMaxRows * kMaxK];
-    __shared__ float gq[kMaxRows];
-    const int lane = threadIdx.x;
-    if (lane < R * K) {
-        const int e = ids[lane];
-        const bool ok = e >= 0 && e < E;
-        sel_e[lane] = ok ? e : 0;
-        sel_w[lane] = ok ? wts[lane] : 0.0f;
-    }
-    if (lane < R)
-        gq[lane] = gate[lane];
-    __syncthreads();
-    build_slots<R>(st, sel_e, sel_w, gq, K, lane);
-}
-
-// ============================================================ gate/up
-
-struct GateUpArgs {
-    const float *x;   // [R][H]
-    int H, I, Is, Imax;
-    const uint8_t *eg, *eu;   // routed gate/up stacks
-    size_t estride;           // bytes per routed [I][H] matrix
-    const uint8_t *sg, *su;   // shared gate/up
-    DecodeWs ws;
-    int units;                // Is + R*K*I
-    int ch_per_wave;
+struct RouteArgs {
+    const double *logits;      // [R][E]
+    const double *zlogit;      // [R]
+    int E, K, renorm;
+    const int32_t *ids_in;     // [R][K] or null: routing given by the caller
+    const float *wts_in, *gate_in;
+    int32_t *ids_out;          // optional outputs
+    float *wts_out, *gate_out;
+    SlotTable *slots;          // published for the expert kernels (or null)
 };
 
-template <int R, typename W>
-__device__ __forceinline__ void gateup_unit(const MatRef &G, const MatRef &U, int ch, const float *xs, int H,
-                                            const float *xsum, int lane, float (&a)[R], float (&c)[R])
+// One workgroup: routing of R rows (wave q selects row q), then the slot
+// table. With caller-supplied routing only the slot table is built (ids
+// outside [0, E) become expert 0 with weight 0).
+template <int R>
+__global__ void __launch_bounds__(256) k_route(RouteArgs a)
 {
-    const int nch = H / W::kChunk;
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        a[q] = 0.0f;
-        c[q] = 0.0f;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    double *lg = reinterpret_cast<double *>(lds_raw);   // [R][lgs]
+    __shared__ RouteLds rl;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    if (a.ids_in) {
+        if (tid < R * a.K) {
+            const int q = tid / a.K, k = tid % a.K;
+            const int e = a.ids_in[tid];
+            const bool ok = e >= 0 && e < a.E;
+            rl.sel_e[q][k] = ok ? e : 0;
+            rl.sel_w[q][k] = ok ? a.wts_in[tid] : 0.0f;
+        }
+        if (tid < R)
+            rl.g[tid] = a.gate_in[tid];
+        __syncthreads();
+    } else {
+        const int lgs = (a.E + 1) & ~1;
+        for (int i = tid; i < R * a.E; i += blockDim.x)
+            lg[(i / a.E) * lgs + i % a.E] = a.logits[i];
+        __syncthreads();
+        if (wave < R) {
+            wave_select(lg + wave * lgs, a.E, a.K, wave, rl, lane);
+            wave_weights(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane);
+        }
+        __syncthreads();
+        if (tid < R * a.K) {
+            const int q = tid / a.K, k = tid % a.K;
+            if (a.ids_out)
+                a.ids_out[tid] = rl.sel_e[q][k];
+            if (a.wts_out)
+                a.wts_out[tid] = rl.sel_w[q][k];
+        }
+        if (tid < R && a.gate_out)
+            a.gate_out[tid] = rl.g[tid];
     }
-    for (int k = lane; k < nch; k += kWave) {
-        chunk_dot<R>(W{}, G, ch, k, xs, H, xsum, H >> 5, a);
-        chunk_dot<R>(W{}, U, ch, k, xs, H, xsum, H >> 5, c);
-    }
+    if (wave == 0 && a.slots) {
+        build_slots<R>(rl, a.K, lane);
+        __builtin_amdgcn_wave_barrier();
+        const int ns = rl.slots.nslots;
+        if (lane == 0)
+            a.slots->nslots = ns;
+        for (int i = lane; i < ns; i += kWave) {
+            a.slots->expert[i] = rl.slots.expert[i];
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-        a[q] = lane_group_sum(a[q], kWave);
-        c[q] = lane_group_sum(c[q], kWave);
+            for (int q = 0; q < R; ++q)
+                a.slots->w[i][q] = rl.slots.w[i][q];
+        }
     }
 }
 
-template <int R, typename ET, typename ST>
-__global__ void __launch_bounds__(256) k_gateup(GateUpArgs p)
+// ============================================================ gate / up
+
+struct GateUpArgs {
+    const float *x;            // [R][H]
+    int H, I, Is, Imax;
+    const uint8_t *eg, *eu;    // routed gate/up stacks
+    size_t estride;            // bytes per routed [I][H] matrix
+    const uint8_t *sg, *su;    // shared gate/up
+    const SlotTable *slots;
+    float *hbuf;               // [S][R][Imax]
+    int ch_per_wg;             // channels per workgroup (two per wave)
+    int wg_per_slot;           // workgroups per routed slot
+};
+
+constexpr int kGuWaves = 4;
+constexpr int kGuMaxChunks = 4;   // chunks per lane in flight per row
+
+// Raw row chunks of one channel (gate and up), kGuMaxChunks per lane.
+template <typename W>
+struct RowChunks {
+    uint4 g[kGuMaxChunks], u[kGuMaxChunks];
+};
+template <>
+struct RowChunks<Q2> {
+    uint2 gc[kGuMaxChunks], uc[kGuMaxChunks];
+    uint32_t gs[kGuMaxChunks], us[kGuMaxChunks];
+};
+
+template <typename W>
+__device__ __forceinline__ void load_rows(W, const MatRef &G, const MatRef &U, int ch, int base, int lane, int nch,
+                                          RowChunks<W> &r)
 {
-    extern __shared__ float smem[];
-    float *xs = smem;                   // [R][H]
-    float *xsum = smem + R * p.H;       // [R][H/32] (block sums, 2-bit weights only)
-    const int tid = threadIdx.x;
-    for (int i = tid; i < R * p.H / 4; i += blockDim.x)
-        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(p.x)[i];
+    constexpr int esz = W::kChunk == 4 ? 4 : 2;   // f32 / bf16 element bytes
+#pragma unroll
+    for (int u = 0; u < kGuMaxChunks; ++u) {
+        const int k = base + u * kWave + lane;
+        if (k < nch) {
+            r.g[u] = *reinterpret_cast<const uint4 *>(G.base + (static_cast<size_t>(ch) * G.cols + k * W::kChunk) * esz);
+            r.u[u] = *reinterpret_cast<const uint4 *>(U.base + (static_cast<size_t>(ch) * U.cols + k * W::kChunk) * esz);
+        }
+    }
+}
+__device__ __forceinline__ void load_rows(Q2, const MatRef &G, const MatRef &U, int ch, int base, int lane, int nch,
+                                          RowChunks<Q2> &r)
+{
+    const int nb = G.cols >> 5;
+#pragma unroll
+    for (int u = 0; u < kGuMaxChunks; ++u) {
+        const int b = base + u * kWave + lane;
+        if (b < nch) {
+            r.gc[u] = *reinterpret_cast<const uint2 *>(G.base + static_cast<size_t>(ch) * (G.cols >> 2) + b * 8);
+            r.uc[u] = *reinterpret_cast<const uint2 *>(U.base + static_cast<size_t>(ch) * (U.cols >> 2) + b * 8);
+            r.gs[u] = *reinterpret_cast<const uint32_t *>(G.base + static_cast<size_t>(G.rows) * (G.cols >> 2) +
+                                                          (static_cast<size_t>(ch) * nb + b) * 4);
+            r.us[u] = *reinterpret_cast<const uint32_t *>(U.base + static_cast<size_t>(U.rows) * (U.cols >> 2) +
+                                                          (static_cast<size_t>(ch) * nb + b) * 4);
+        }
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void dot_chunk(F32, const uint4 &w, int k, const float *xs, int H, float (&acc)[R])
+{
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 xv = *reinterpret_cast<const float4 *>(xs + q * H + k * 4);
+        acc[q] = fmaf(__uint_as_float(w.x), xv.x, acc[q]);
+        acc[q] = fmaf(__uint_as_float(w.y), xv.y, acc[q]);
+        acc[q] = fmaf(__uint_as_float(w.z), xv.z, acc[q]);
+        acc[q] = fmaf(__uint_as_float(w.w), xv.w, acc[q]);
+    }
+}
+template <int R>
+__device__ __forceinline__ void dot_chunk(BF16, const uint4 &w, int k, const float *xs, int H, float (&acc)[R])
+{
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(xs + q * H + k * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(xs + q * H + k * 8 + 4);
+        float a = acc[q];
+        a = fmaf(bf16_lo(w.x), x0.x, a);
+        a = fmaf(bf16_hi(w.x), x0.y, a);
+        a = fmaf(bf16_lo(w.y), x0.z, a);
+        a = fmaf(bf16_hi(w.y), x0.w, a);
+        a = fmaf(bf16_lo(w.z), x1.x, a);
+        a = fmaf(bf16_hi(w.z), x1.y, a);
+        a = fmaf(bf16_lo(w.w), x1.z, a);
+        a = fmaf(bf16_hi(w.w), x1.w, a);
+        acc[q] = a;
+    }
+}
+// one 32-weight block: s * sum_j code_j x_j + m * sum_j x_j
+template <int R>
+__device__ __forceinline__ void dot_block(const uint2 &cw, uint32_t sm, int b, const float *xs, int H,
+                                          const float *xsum, float (&acc)[R])
+{
+    const float s = f16_to_f32(sm & 0xffffu);
+    const float m = f16_to_f32(sm >> 16);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float *x = xs + q * H + b * 32;
+        float cx = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t d = half ? cw.y : cw.x;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const float4 xv = *reinterpret_cast<const float4 *>(x + half * 16 + j4 * 4);
+                const uint32_t byte = d >> (8 * j4);
+                cx = fmaf(static_cast<float>(byte & 3u), xv.x, cx);
+                cx = fmaf(static_cast<float>((byte >> 2) & 3u), xv.y, cx);
+                cx = fmaf(static_cast<float>((byte >> 4) & 3u), xv.z, cx);
+                cx = fmaf(static_cast<float>((byte >> 6) & 3u), xv.w, cx);
+            }
+        }
+        acc[q] = fmaf(s, cx, fmaf(m, xsum[q * (H >> 5) + b], acc[q]));
+    }
+}
+
+template <int R, typename W>
+__device__ __forceinline__ void dot_rows(W, const RowChunks<W> &r, int base, int lane, int nch, const float *xs,
+                                         int H, const float *, float (&a)[R], float (&c)[R])
+{
+#pragma unroll
+    for (int u = 0; u < kGuMaxChunks; ++u) {
+        const int k = base + u * kWave + lane;
+        if (k < nch) {
+            dot_chunk<R>(W{}, r.g[u], k, xs, H, a);
+            dot_chunk<R>(W{}, r.u[u], k, xs, H, c);
+        }
+    }
+}
+template <int R>
+__device__ __forceinline__ void dot_rows(Q2, const RowChunks<Q2> &r, int base, int lane, int nch, const float *xs,
+                                         int H, const float *xsum, float (&a)[R], float (&c)[R])
+{
+#pragma unroll
+    for (int u = 0; u < kGuMaxChunks; ++u) {
+        const int b = base + u * kWave + lane;
+        if (b < nch) {
+            dot_block<R>(r.gc[u], r.gs[u], b, xs, H, xsum, a);
+            dot_block<R>(r.uc[u], r.us[u], b, xs, H, xsum, c);
+        }
+    }
+}
+
+// x of all rows into LDS, plus per-32 block sums when W is the 2-bit format.
+template <int R, typename W>
+__device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float *xsum)
+{
+    for (int i = threadIdx.x; i < R * H / 4; i += blockDim.x)
+        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(x)[i];
     __syncthreads();
-    if (ET::kChunk == 32) {
-        for (int i = tid; i < R * (p.H >> 5); i += blockDim.x) {
+    if (W::kChunk == 32) {
+        for (int i = threadIdx.x; i < R * (H >> 5); i += blockDim.x) {
             float s = 0.0f;
             for (int j = 0; j < 32; ++j)
                 s += xs[i * 32 + j];
@@ -340,243 +448,558 @@ __global__ void __launch_bounds__(256) k_gateup(GateUpArgs p)
         }
         __syncthreads();
     }
-    const int lane = tid & (kWave - 1);
-    const int gwave = blockIdx.x * (blockDim.x / kWave) + tid / kWave;
-    const SlotTable *st = p.ws.slots;
-    const int nslots = st->nslots;
-    for (int i = 0; i < p.ch_per_wave; ++i) {
-        const int u = gwave * p.ch_per_wave + i;
-        if (u >= p.units)
-            break;
-        int slot, ch;
-        if (u < p.Is) {
-            slot = 0;
-            ch = u;
-        } else {
-            slot = 1 + (u - p.Is) / p.I;
-            ch = (u - p.Is) % p.I;
-        }
-        if (slot >= nslots)
-            break;
-        float a[R], c[R];
-        if (slot == 0) {
-            const MatRef G{p.sg, p.Is, p.H}, U{p.su, p.Is, p.H};
-            gateup_unit<R, ST>(G, U, ch, xs, p.H, xsum, lane, a, c);
-        } else {
-            const int e = st->expert[slot];
-            const MatRef G{p.eg + e * p.estride, p.I, p.H}, U{p.eu + e * p.estride, p.I, p.H};
-            gateup_unit<R, ET>(G, U, ch, xs, p.H, xsum, lane, a, c);
-        }
-        if (lane < R) {
-            float hv = 0.0f;
+}
+
+// h'[slot][q][ch] = w_q * silu(a) * c for one channel, from lane partials.
+template <int R>
+__device__ __forceinline__ void finish_channel(const GateUpArgs &p, int slot, int ch, float (&a)[R], float (&c)[R],
+                                               const float (&wq)[R], int lane)
+{
 #pragma unroll
-            for (int q = 0; q < R; ++q)
-                if (q == lane)
-                    hv = silu_mul(a[q], c[q]) * st->w[slot][q];
-            p.ws.hbuf[(static_cast<size_t>(slot) * R + lane) * p.Imax + ch] = hv;
-        }
+    for (int q = 0; q < R; ++q) {
+        a[q] = lane_group_sum(a[q], kWave);
+        c[q] = lane_group_sum(c[q], kWave);
+    }
+    if (lane < R) {
+        float hv = 0.0f;
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            if (q == lane)
+                hv = silu_mul(a[q], c[q]) * wq[q];
+        p.hbuf[(static_cast<size_t>(slot) * R + lane) * p.Imax + ch] = hv;
     }
 }
 
-// ============================================================== down
+// The two channels ch, ch+1 of this wave. When a row fits one chunk set
+// (H <= 256 * chunk), both channels' rows are requested before x is staged,
+// so the weight stream overlaps the staging; wider rows stream in steps.
+template <int R, typename W>
+__device__ __forceinline__ void gateup_two(const GateUpArgs &p, const MatRef &G, const MatRef &U, int slot, int ch,
+                                           int n, const float (&wq)[R], float *xs, float *xsum)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nck = p.H / W::kChunk;
+    float a[R], c[R], a2[R], c2[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        a[q] = c[q] = a2[q] = c2[q] = 0.0f;
+    if (nck <= kWave * kGuMaxChunks) {
+        RowChunks<W> r0, r1;
+        if (ch < n)
+            load_rows(W{}, G, U, ch, 0, lane, nck, r0);
+        if (ch + 1 < n)
+            load_rows(W{}, G, U, ch + 1, 0, lane, nck, r1);
+        stage_x<R, W>(p.x, p.H, xs, xsum);
+        if (ch < n) {
+            dot_rows<R>(W{}, r0, 0, lane, nck, xs, p.H, xsum, a, c);
+            finish_channel<R>(p, slot, ch, a, c, wq, lane);
+        }
+        if (ch + 1 < n) {
+            dot_rows<R>(W{}, r1, 0, lane, nck, xs, p.H, xsum, a2, c2);
+            finish_channel<R>(p, slot, ch + 1, a2, c2, wq, lane);
+        }
+        return;
+    }
+    stage_x<R, W>(p.x, p.H, xs, xsum);
+    for (int i = 0; i < 2; ++i) {
+        const int cc = ch + i;
+        if (cc >= n)
+            break;
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            a[q] = c[q] = 0.0f;
+        for (int base = 0; base < nck; base += kWave * kGuMaxChunks) {
+            RowChunks<W> part;
+            load_rows(W{}, G, U, cc, base, lane, nck, part);
+            dot_rows<R>(W{}, part, base, lane, nck, xs, p.H, xsum, a, c);
+        }
+        finish_channel<R>(p, slot, cc, a, c, wq, lane);
+    }
+}
 
-struct DownArgs {
-    float *y;   // [R][H]
-    int H, I, Is, Imax;
-    const uint8_t *ed;        // routed down stack
-    size_t estride;           // bytes per routed [H][I] matrix
-    const uint8_t *sd;        // shared down
-    DecodeWs ws;
-    int group;                // slots staged in LDS at a time
+// Routed experts: workgroup b covers channels of slot 1 + b / wg_per_slot.
+template <int R, typename ET>
+__global__ void __launch_bounds__(kGuWaves * kWave) k_gateup_routed(GateUpArgs p)
+{
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    float *xs = reinterpret_cast<float *>(lds_raw);   // [R][H]
+    float *xsum = xs + R * p.H;                       // [R][H/32]
+    const int slot = 1 + blockIdx.x / p.wg_per_slot;
+    const int ch0 = (blockIdx.x % p.wg_per_slot) * p.ch_per_wg;
+    const int nslots = p.slots->nslots;
+    if (slot >= nslots)
+        return;
+    const int e = p.slots->expert[slot];
+    const MatRef G{p.eg + e * p.estride, p.I, p.H}, U{p.eu + e * p.estride, p.I, p.H};
+    float w[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        w[q] = p.slots->w[slot][q];
+    gateup_two<R, ET>(p, G, U, slot, ch0 + (threadIdx.x / kWave) * 2, p.I, w, xs, xsum);
+}
+
+// ================================================================= dense
+
+struct LogitArgs {
+    const float *x;          // [R][H]
+    int H, E;
+    const uint8_t *router_w; // [E][H]
+    const float *bias;       // [E] or null
+    const uint8_t *gate_w;   // [H]
+    double *logits;          // [R][E]
+    double *zlogit;          // [R]
 };
 
-constexpr int kDownRowsPerWave = 4;
-
-// Partial dots of rows j0 .. j0+3 of matrix M with the staged h of one slot.
-template <int R, typename W>
-__device__ __forceinline__ void down_slot(const MatRef &M, int j0, const float *h, const float *hs, int Imax,
-                                          int lane, float (&acc)[kDownRowsPerWave][R])
+template <int R>
+__device__ __forceinline__ void router_chunk(F32, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
 {
-    const int nch = M.cols / W::kChunk;
-    const int lpr = nch >= kWave ? kWave : next_pow2(nch);
-    const int rpi = kWave / lpr;
-    const int lr = lane / lpr;
-    const int lc = lane % lpr;
+    const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
 #pragma unroll
-    for (int t = 0; t < kDownRowsPerWave; ++t) {
-        if (t * rpi >= kDownRowsPerWave)
-            break;
-        const int j = j0 + t * rpi + lr;
-        if (j >= M.rows || t * rpi + lr >= kDownRowsPerWave)
-            continue;
-        for (int c = lc; c < nch; c += lpr)
-            chunk_dot<R>(W{}, M, j, c, h, Imax, hs, Imax >> 5, acc[t]);
+    for (int q = 0; q < R; ++q) {
+        const float4 xv = *reinterpret_cast<const float4 *>(xs + q * H + c * 4);
+        acc[q] = fma(static_cast<double>(w[0]), static_cast<double>(xv.x), acc[q]);
+        acc[q] = fma(static_cast<double>(w[1]), static_cast<double>(xv.y), acc[q]);
+        acc[q] = fma(static_cast<double>(w[2]), static_cast<double>(xv.z), acc[q]);
+        acc[q] = fma(static_cast<double>(w[3]), static_cast<double>(xv.w), acc[q]);
     }
 }
 
-template <int R, typename W>
-__device__ __forceinline__ void down_reduce_store(int n, int lane, float (&acc)[kDownRowsPerWave][R],
-                                                  float *ybuf /* [rows][R] */, bool add)
+template <int R>
+__device__ __forceinline__ void router_chunk(BF16, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
 {
-    const int nch = n / W::kChunk;
-    const int lpr = nch >= kWave ? kWave : next_pow2(nch);
-    const int rpi = kWave / lpr;
-    const int lr = lane / lpr;
-    const int lc = lane % lpr;
+    const float wf[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
 #pragma unroll
-    for (int t = 0; t < kDownRowsPerWave; ++t) {
-        if (t * rpi >= kDownRowsPerWave)
-            break;
+    for (int q = 0; q < R; ++q) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8 + 4);
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[q] = fma(static_cast<double>(wf[i]), static_cast<double>(xv[i]), acc[q]);
+    }
+}
+
+constexpr int kLgPrefetch = 4;   // 16-byte chunks per lane loaded before x is staged
+
+// Routing-independent work of a call: router logits (workgroups [0, n_lg_wg),
+// one row per wave, row E being the shared-gate vector) and the shared
+// expert's SwiGLU activations (workgroups n_lg_wg.., unweighted; the gate
+// multiplies them in the down pass).
+template <int R, typename RT, typename ST>
+__global__ void __launch_bounds__(256) k_dense(LogitArgs a, GateUpArgs p, int n_lg_wg)
+{
+    extern __shared__ float xs[];   // [R][H]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    if (static_cast<int>(blockIdx.x) >= n_lg_wg) {
+        const MatRef G{p.sg, p.Is, p.H}, U{p.su, p.Is, p.H};
+        const int ch = (blockIdx.x - n_lg_wg) * p.ch_per_wg + (tid / kWave) * 2;
+        float one[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            one[q] = 1.0f;
+        gateup_two<R, ST>(p, G, U, 0, ch, p.Is, one, xs, nullptr);
+        return;
+    }
+    const int e = blockIdx.x * (blockDim.x / kWave) + tid / kWave;
+    const bool live = e <= a.E;
+    const size_t rb = static_cast<size_t>(a.H) * (RT::kChunk == 4 ? 4 : 2);
+    const uint8_t *row = e < a.E ? a.router_w + e * rb : a.gate_w;
+    const int nch = static_cast<int>(rb / 16);
+    // the weight row does not depend on x: start its loads first
+    uint4 w[kLgPrefetch];
+#pragma unroll
+    for (int u = 0; u < kLgPrefetch; ++u) {
+        const int c = lane + u * kWave;
+        if (live && c < nch)
+            w[u] = *reinterpret_cast<const uint4 *>(row + c * 16);
+    }
+    for (int i = tid; i < R * a.H / 4; i += blockDim.x)
+        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(a.x)[i];
+    __syncthreads();
+    if (!live)
+        return;
+    double acc[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        acc[q] = 0.0;
+#pragma unroll
+    for (int u = 0; u < kLgPrefetch; ++u) {
+        const int c = lane + u * kWave;
+        if (c < nch)
+            router_chunk<R>(RT{}, w[u], c, xs, a.H, acc);
+    }
+    for (int c = lane + kLgPrefetch * kWave; c < nch; c += kWave) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(row + c * 16);
+        router_chunk<R>(RT{}, u, c, xs, a.H, acc);
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        acc[q] = lane_group_sum(acc[q], kWave);
+    if (lane == 0) {
 #pragma unroll
         for (int q = 0; q < R; ++q) {
-            const float v = lane_group_sum(acc[t][q], lpr);
-            const int row = t * rpi + lr;
-            if (lc == 0 && row < kDownRowsPerWave) {
-                if (add)
-                    ybuf[row * R + q] += v;
-                else
-                    ybuf[row * R + q] = v;
-            }
+            if (e < a.E)
+                a.logits[q * a.E + e] = acc[q] + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
+            else
+                a.zlogit[q] = acc[q];
         }
+    }
+}
+
+// ================================================================= down
+
+struct DownArgs {
+    float *y;                  // [R][H]
+    int H, I, Is, Imax;
+    const uint8_t *ed;         // routed down stack
+    size_t estride;            // bytes per routed [H][I] matrix
+    const uint8_t *sd;         // shared down
+    const SlotTable *slots;
+    const float *hbuf;         // [S][R][Imax]
+    int group;                 // slots staged in LDS at a time
+};
+
+constexpr int kDnWaves = 8;    // one output row per wave
+constexpr int kDnBatch = 12;   // slot rows whose loads are in flight together
+
+// Down rows are read in pieces of 8 elements (bf16: 16 bytes; 2-bit: 2 bytes
+// of codes plus the block's scale/min) or 4 elements (fp32: 16 bytes). Lane
+// c of a row takes piece c (then c+64, ...).
+template <typename W>
+struct DnPiece;
+template <>
+struct DnPiece<BF16> {
+    static constexpr int kElems = 8;
+    uint4 v;
+    __device__ __forceinline__ void load(const MatRef &M, int j, int c)
+    {
+        v = *reinterpret_cast<const uint4 *>(M.base + (static_cast<size_t>(j) * M.cols + c * 8) * 2);
+    }
+    template <int R>
+    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
+    {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float4 h0 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8);
+            const float4 h1 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8 + 4);
+            float s = acc[q];
+            s = fmaf(bf16_lo(v.x), h0.x, s);
+            s = fmaf(bf16_hi(v.x), h0.y, s);
+            s = fmaf(bf16_lo(v.y), h0.z, s);
+            s = fmaf(bf16_hi(v.y), h0.w, s);
+            s = fmaf(bf16_lo(v.z), h1.x, s);
+            s = fmaf(bf16_hi(v.z), h1.y, s);
+            s = fmaf(bf16_lo(v.w), h1.z, s);
+            s = fmaf(bf16_hi(v.w), h1.w, s);
+            acc[q] = s;
+        }
+    }
+};
+template <>
+struct DnPiece<F32> {
+    static constexpr int kElems = 4;
+    float4 v;
+    __device__ __forceinline__ void load(const MatRef &M, int j, int c)
+    {
+        v = *reinterpret_cast<const float4 *>(M.base + (static_cast<size_t>(j) * M.cols + c * 4) * 4);
+    }
+    template <int R>
+    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
+    {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float4 hv = *reinterpret_cast<const float4 *>(h + q * hs + c * 4);
+            acc[q] = fmaf(v.x, hv.x, fmaf(v.y, hv.y, fmaf(v.z, hv.z, fmaf(v.w, hv.w, acc[q]))));
+        }
+    }
+};
+template <>
+struct DnPiece<Q2> {
+    static constexpr int kElems = 8;
+    uint32_t codes;   // 16 bits used
+    uint32_t sm;
+    __device__ __forceinline__ void load(const MatRef &M, int j, int c)
+    {
+        const int nb = M.cols >> 5;
+        const int b = c >> 2;
+        codes = *reinterpret_cast<const uint16_t *>(M.base + static_cast<size_t>(j) * (M.cols >> 2) + c * 2);
+        sm = *reinterpret_cast<const uint32_t *>(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) +
+                                                 (static_cast<size_t>(j) * nb + b) * 4);
+    }
+    // h8: sums of each 8 consecutive h values (for the min term)
+    template <int R>
+    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *h8, int h8s, int c,
+                                             float (&acc)[R]) const
+    {
+        const float s = f16_to_f32(sm & 0xffffu);
+        const float m = f16_to_f32(sm >> 16);
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float4 h0 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8);
+            const float4 h1 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8 + 4);
+            float cx = 0.0f;
+            cx = fmaf(static_cast<float>(codes & 3u), h0.x, cx);
+            cx = fmaf(static_cast<float>((codes >> 2) & 3u), h0.y, cx);
+            cx = fmaf(static_cast<float>((codes >> 4) & 3u), h0.z, cx);
+            cx = fmaf(static_cast<float>((codes >> 6) & 3u), h0.w, cx);
+            cx = fmaf(static_cast<float>((codes >> 8) & 3u), h1.x, cx);
+            cx = fmaf(static_cast<float>((codes >> 10) & 3u), h1.y, cx);
+            cx = fmaf(static_cast<float>((codes >> 12) & 3u), h1.z, cx);
+            cx = fmaf(static_cast<float>((codes >> 14) & 3u), h1.w, cx);
+            acc[q] = fmaf(s, cx, fmaf(m, h8[q * h8s + c], acc[q]));
+        }
+    }
+};
+
+// Lane partials of row j of up to kDnBatch matrices of one format with their
+// staged h'; every load is issued before the math.
+template <int R, typename W>
+__device__ __forceinline__ void down_rows(const MatRef *mats, int ns, int j, const float *hl, const float *h8,
+                                          int Imax, int lane, float (&acc)[R])
+{
+    const int npc = mats[0].cols / DnPiece<W>::kElems;
+    for (int base = 0; base < npc; base += kWave) {
+        const int c = base + lane;
+        DnPiece<W> pc[kDnBatch];
+#pragma unroll
+        for (int s = 0; s < kDnBatch; ++s)
+            if (s < ns && c < npc)
+                pc[s].load(mats[s], j, c);
+#pragma unroll
+        for (int s = 0; s < kDnBatch; ++s)
+            if (s < ns && c < npc)
+                pc[s].template fma_into<R>(hl + s * R * Imax, Imax, h8 + s * R * (Imax >> 3), Imax >> 3, c, acc);
+    }
+}
+
+// h' of slots [s0, s0 + gs) into LDS; slot 0 (the shared expert) is scaled by
+// the gate of each row here. For 2-bit experts also the 8-element sums.
+template <int R, typename ET>
+__device__ __forceinline__ void stage_h(const DownArgs &p, int s0, int gs, float *hl, float *h8)
+{
+    const int n4 = gs * R * p.Imax / 4;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+        float4 v = reinterpret_cast<const float4 *>(p.hbuf + static_cast<size_t>(s0) * R * p.Imax)[i];
+        if (s0 == 0 && i < R * p.Imax / 4) {
+            const float g = p.slots->w[0][(i * 4) / p.Imax];
+            v.x *= g;
+            v.y *= g;
+            v.z *= g;
+            v.w *= g;
+        }
+        reinterpret_cast<float4 *>(hl)[i] = v;
+    }
+    __syncthreads();
+    if (ET::kChunk == 32) {
+        for (int i = threadIdx.x; i < gs * R * (p.Imax >> 3); i += blockDim.x) {
+            const float4 a = reinterpret_cast<const float4 *>(hl)[2 * i];
+            const float4 b = reinterpret_cast<const float4 *>(hl)[2 * i + 1];
+            h8[i] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+        }
+        __syncthreads();
     }
 }
 
 template <int R, typename ET, typename ST>
-__global__ void __launch_bounds__(256) k_down(DownArgs p)
+__global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) unsigned char lds_raw[];
     const int G = p.group;
-    float *hl = smem;                              // [G][R][Imax]
-    float *hs = smem + G * R * p.Imax;             // [G][R][Imax/32]
-    __shared__ float ybuf[4][kDownRowsPerWave * R];
+    float *hl = reinterpret_cast<float *>(lds_raw);        // [G][R][Imax]
+    float *h8 = hl + G * R * p.Imax;                         // [G][R][Imax/8]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int j0 = (blockIdx.x * (blockDim.x / kWave) + wave) * kDownRowsPerWave;
-    const SlotTable *st = p.ws.slots;
-    const int nslots = st->nslots;
+    const int j = blockIdx.x * kDnWaves + tid / kWave;
+    const bool live = j < p.H;
+    const int nslots = p.slots->nslots;
 
-    float acc_r[kDownRowsPerWave][R], acc_s[kDownRowsPerWave][R];
+    float acc[R];
 #pragma unroll
-    for (int t = 0; t < kDownRowsPerWave; ++t)
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            acc_r[t][q] = 0.0f;
-            acc_s[t][q] = 0.0f;
-        }
+    for (int q = 0; q < R; ++q)
+        acc[q] = 0.0f;
 
-    for (int s0 = 0; s0 < nslots; s0 += G) {
-        const int gs = min(G, nslots - s0);
-        __syncthreads();
-        const int n4 = gs * R * p.Imax / 4;
-        for (int i = tid; i < n4; i += blockDim.x)
-            reinterpret_cast<float4 *>(hl)[i] =
-                reinterpret_cast<const float4 *>(p.ws.hbuf + static_cast<size_t>(s0) * R * p.Imax)[i];
-        __syncthreads();
-        if (ET::kChunk == 32) {
-            const int nb = p.Imax >> 5;
-            for (int i = tid; i < gs * R * nb; i += blockDim.x) {
-                float s = 0.0f;
-                for (int j = 0; j < 32; ++j)
-                    s += hl[i * 32 + j];
-                hs[i] = s;
+    const int npr = p.I / DnPiece<ET>::kElems, nps = p.Is / DnPiece<ST>::kElems;
+    if (nslots <= G && nslots - 1 <= kDnBatch && npr <= kWave && nps <= kWave) {
+        // Every down-row piece of this wave is requested before h' is staged,
+        // so the weight stream overlaps the h' broadcast.
+        DnPiece<ST> ps;
+        DnPiece<ET> pr[kDnBatch];
+        if (live && lane < nps)
+            ps.load(MatRef{p.sd, p.H, p.Is}, j, lane);
+#pragma unroll
+        for (int s = 0; s < kDnBatch; ++s) {
+            if (live && s + 1 < nslots && lane < npr) {
+                const int e = p.slots->expert[s + 1];
+                pr[s].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
             }
-            __syncthreads();
         }
-        if (j0 < p.H) {
-            for (int g = 0; g < gs; ++g) {
-                const int slot = s0 + g;
-                const float *h = hl + g * R * p.Imax;
-                const float *hsum = hs + g * R * (p.Imax >> 5);
-                if (slot == 0) {
-                    const MatRef M{p.sd, p.H, p.Is};
-                    down_slot<R, ST>(M, j0, h, hsum, p.Imax, lane, acc_s);
-                } else {
-                    const int e = st->expert[slot];
-                    const MatRef M{p.ed + e * p.estride, p.H, p.I};
-                    down_slot<R, ET>(M, j0, h, hsum, p.Imax, lane, acc_r);
+        stage_h<R, ET>(p, 0, nslots, hl, h8);
+        if (live) {
+            if (lane < nps)
+                ps.template fma_into<R>(hl, p.Imax, h8, p.Imax >> 3, lane, acc);
+#pragma unroll
+            for (int s = 0; s < kDnBatch; ++s)
+                if (s + 1 < nslots && lane < npr)
+                    pr[s].template fma_into<R>(hl + (s + 1) * R * p.Imax, p.Imax,
+                                               h8 + (s + 1) * R * (p.Imax >> 3), p.Imax >> 3, lane, acc);
+        }
+    } else {
+        for (int s0 = 0; s0 < nslots; s0 += G) {
+            const int gs = min(G, nslots - s0);
+            if (s0 > 0)
+                __syncthreads();
+            stage_h<R, ET>(p, s0, gs, hl, h8);
+            if (!live)
+                continue;
+            int g = 0;
+            if (s0 == 0) {   // slot 0: the shared expert
+                const MatRef M{p.sd, p.H, p.Is};
+                down_rows<R, ST>(&M, 1, j, hl, h8, p.Imax, lane, acc);
+                g = 1;
+            }
+            for (; g < gs; g += kDnBatch) {
+                MatRef mats[kDnBatch];
+                const int nb = min(kDnBatch, gs - g);
+#pragma unroll
+                for (int s = 0; s < kDnBatch; ++s) {
+                    const int e = s < nb ? p.slots->expert[s0 + g + s] : 0;
+                    mats[s] = MatRef{p.ed + e * p.estride, p.H, p.I};
                 }
+                down_rows<R, ET>(mats, nb, j, hl + g * R * p.Imax, h8 + g * R * (p.Imax >> 3), p.Imax, lane,
+                                 acc);
             }
         }
     }
-    const bool live = j0 < p.H;
-    if (live)
-        down_reduce_store<R, ET>(p.I, lane, acc_r, ybuf[wave], false);
-    __syncthreads();
-    if (live)
-        down_reduce_store<R, ST>(p.Is, lane, acc_s, ybuf[wave], true);
-    __syncthreads();
-    if (live && lane < kDownRowsPerWave * R) {
-        const int row = lane / R, q = lane % R;
-        if (j0 + row < p.H)
-            p.y[q * p.H + j0 + row] = ybuf[wave][row * R + q];
+    if (live) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float v = lane_group_sum(acc[q], kWave);
+            if (lane == 0)
+                p.y[q * p.H + j] = v;
+        }
     }
 }
 
-// ============================================================ launch
+// ================================================================ launch
 
-template <typename RT>
-static int launch_route_t(const moe_layer_desc *d, const float *x, int R, int32_t *ids, float *wts, float *gate,
-                          const DecodeWs &ws, hipStream_t s)
+static inline int imax_of(const moe_layer_desc *d) { return d->inter > d->shared_inter ? d->inter : d->shared_inter; }
+
+size_t gateup_lds_bytes(int R, int H, int E)
 {
-    RouteArgs a;
+    const size_t a = sizeof(float) * (R * H + R * (H >> 5)), b = sizeof(double) * R * ((E + 1) & ~1);
+    return a > b ? a : b;
+}
+
+struct RoutingIO {
+    const int32_t *ids_in;
+    const float *wts_in, *gate_in;
+    int32_t *ids_out;
+    float *wts_out, *gate_out;
+};
+
+template <typename ET>
+static GateUpArgs gateup_args(const moe_layer_desc *d, const float *x, const DecodeWs &w)
+{
+    GateUpArgs g;
+    g.x = x;
+    g.H = d->hidden;
+    g.I = d->inter;
+    g.Is = d->shared_inter;
+    g.Imax = imax_of(d);
+    g.eg = static_cast<const uint8_t *>(d->exp_gate);
+    g.eu = static_cast<const uint8_t *>(d->exp_up);
+    g.estride = mat_bytes<ET>(g.I, g.H);
+    g.sg = static_cast<const uint8_t *>(d->sh_gate);
+    g.su = static_cast<const uint8_t *>(d->sh_up);
+    g.slots = w.slots;
+    g.hbuf = w.hbuf;
+    g.ch_per_wg = kGuWaves * 2;
+    g.wg_per_slot = (g.I + g.ch_per_wg - 1) / g.ch_per_wg;
+    return g;
+}
+
+// k_dense: logits (if `logits`) and the shared expert (if `shared`).
+template <typename RT, typename ST>
+static int launch_dense_t(const moe_layer_desc *d, const float *x, int R, const GateUpArgs &g, const DecodeWs &w,
+                          bool logits, bool shared, hipStream_t s)
+{
+    LogitArgs a;
     a.x = x;
     a.H = d->hidden;
     a.E = d->n_experts;
-    a.K = d->top_k;
-    a.renorm = d->renormalize;
     a.router_w = static_cast<const uint8_t *>(d->router_w);
     a.bias = d->router_bias;
     a.gate_w = static_cast<const uint8_t *>(d->shared_gate_w);
-    a.ids_out = ids;
-    a.wts_out = wts;
-    a.gate_out = gate;
-    a.ws = ws;
-    a.rows_per_wave = 1;
-    const int waves = (a.E + 1 + a.rows_per_wave - 1) / a.rows_per_wave;
-    const dim3 grid((waves + 3) / 4), block(256);
+    a.logits = w.logits;
+    a.zlogit = w.zlogit;
+    const int n_lg = logits ? (a.E + 1 + 3) / 4 : 0;
+    const int n_sh = shared ? (d->shared_inter + g.ch_per_wg - 1) / g.ch_per_wg : 0;
+    const dim3 grid(n_lg + n_sh), block(256);
     const size_t lds = sizeof(float) * R * a.H;
     switch (R) {
-    case 1: hipLaunchKernelGGL((k_route<1, RT>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_route<2, RT>), grid, block, lds, s, a); break;
-    case 3: hipLaunchKernelGGL((k_route<3, RT>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_route<4, RT>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_dense<1, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
+    case 2: hipLaunchKernelGGL((k_dense<2, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
+    case 3: hipLaunchKernelGGL((k_dense<3, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
+    default: hipLaunchKernelGGL((k_dense<4, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+static int launch_route(const moe_layer_desc *d, int R, const RoutingIO &io, const DecodeWs &w, bool slots,
+                        hipStream_t s)
+{
+    RouteArgs a;
+    a.logits = w.logits;
+    a.zlogit = w.zlogit;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.renorm = d->renormalize;
+    a.ids_in = io.ids_in;
+    a.wts_in = io.wts_in;
+    a.gate_in = io.gate_in;
+    a.ids_out = io.ids_out;
+    a.wts_out = io.wts_out;
+    a.gate_out = io.gate_out;
+    a.slots = slots ? w.slots : nullptr;
+    const size_t lds = io.ids_in ? 0 : sizeof(double) * R * ((a.E + 1) & ~1);
+    switch (R) {
+    case 1: hipLaunchKernelGGL((k_route<1>), dim3(1), dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_route<2>), dim3(1), dim3(256), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_route<3>), dim3(1), dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_route<4>), dim3(1), dim3(256), lds, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 template <typename ET, typename ST>
-static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, float *y, const DecodeWs &ws,
-                            hipStream_t s)
+static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, float *y, const RoutingIO &io,
+                            const DecodeWs &w, hipStream_t s)
 {
     const int H = d->hidden, I = d->inter, Is = d->shared_inter, K = d->top_k;
-    const int Imax = I > Is ? I : Is;
-    GateUpArgs g;
-    g.x = x;
-    g.H = H;
-    g.I = I;
-    g.Is = Is;
-    g.Imax = Imax;
-    g.eg = static_cast<const uint8_t *>(d->exp_gate);
-    g.eu = static_cast<const uint8_t *>(d->exp_up);
-    g.estride = mat_bytes<ET>(I, H);
-    g.sg = static_cast<const uint8_t *>(d->sh_gate);
-    g.su = static_cast<const uint8_t *>(d->sh_up);
-    g.ws = ws;
-    g.units = Is + R * K * I;
-    g.ch_per_wave = 2;
-    const int gw = (g.units + g.ch_per_wave - 1) / g.ch_per_wave;
-    const dim3 ggrid((gw + 3) / 4), block(256);
-    const size_t glds = sizeof(float) * R * H + (ET::kChunk == 32 ? sizeof(float) * R * (H / 32) : 0);
-    switch (R) {
-    case 1: hipLaunchKernelGGL((k_gateup<1, ET, ST>), ggrid, block, glds, s, g); break;
-    case 2: hipLaunchKernelGGL((k_gateup<2, ET, ST>), ggrid, block, glds, s, g); break;
-    case 3: hipLaunchKernelGGL((k_gateup<3, ET, ST>), ggrid, block, glds, s, g); break;
-    default: hipLaunchKernelGGL((k_gateup<4, ET, ST>), ggrid, block, glds, s, g); break;
+    const int Imax = imax_of(d);
+    const GateUpArgs g = gateup_args<ET>(d, x, w);
+    int rc = d->router_t == MOE_F32 ? launch_dense_t<F32, ST>(d, x, R, g, w, !io.ids_in, true, s)
+                                    : launch_dense_t<BF16, ST>(d, x, R, g, w, !io.ids_in, true, s);
+    if (rc != MOE_OK)
+        return rc;
+    rc = launch_route(d, R, io, w, true, s);
+    if (rc != MOE_OK)
+        return rc;
+    {
+        const dim3 block(kGuWaves * kWave);
+        const int grid = R * K * g.wg_per_slot;
+        const size_t lds = sizeof(float) * (R * H + R * (H >> 5));
+        switch (R) {
+        case 1: hipLaunchKernelGGL((k_gateup_routed<1, ET>), dim3(grid), block, lds, s, g); break;
+        case 2: hipLaunchKernelGGL((k_gateup_routed<2, ET>), dim3(grid), block, lds, s, g); break;
+        case 3: hipLaunchKernelGGL((k_gateup_routed<3, ET>), dim3(grid), block, lds, s, g); break;
+        default: hipLaunchKernelGGL((k_gateup_routed<4, ET>), dim3(grid), block, lds, s, g); break;
+        }
+        if (hipGetLastError() != hipSuccess)
+            return MOE_EHIP;
     }
-    if (hipGetLastError() != hipSuccess)
-        return MOE_EHIP;
-
     DownArgs dn;
     dn.y = y;
     dn.H = H;
@@ -586,73 +1009,62 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     dn.ed = static_cast<const uint8_t *>(d->exp_down);
     dn.estride = mat_bytes<ET>(H, I);
     dn.sd = static_cast<const uint8_t *>(d->sh_down);
-    dn.ws = ws;
-    // stage as many slots as fit in 48 KiB of LDS
-    const size_t per_slot = sizeof(float) * R * Imax + sizeof(float) * R * (Imax / 32);
+    dn.slots = w.slots;
+    dn.hbuf = w.hbuf;
+    const size_t per_slot = sizeof(float) * R * Imax + sizeof(float) * R * (Imax / 8);
     int group = static_cast<int>((48u * 1024u) / per_slot);
-    if (group < 1)
-        group = 1;
-    if (group > R * K + 1)
-        group = R * K + 1;
+    group = group < 1 ? 1 : (group > R * K + 1 ? R * K + 1 : group);
     dn.group = group;
-    const int rows_per_wg = 4 * kDownRowsPerWave;
-    const dim3 dgrid((H + rows_per_wg - 1) / rows_per_wg);
+    const dim3 dgrid((H + kDnWaves - 1) / kDnWaves), dblock(kDnWaves * kWave);
     const size_t dlds = per_slot * group;
     switch (R) {
-    case 1: hipLaunchKernelGGL((k_down<1, ET, ST>), dgrid, block, dlds, s, dn); break;
-    case 2: hipLaunchKernelGGL((k_down<2, ET, ST>), dgrid, block, dlds, s, dn); break;
-    case 3: hipLaunchKernelGGL((k_down<3, ET, ST>), dgrid, block, dlds, s, dn); break;
-    default: hipLaunchKernelGGL((k_down<4, ET, ST>), dgrid, block, dlds, s, dn); break;
+    case 1: hipLaunchKernelGGL((k_down<1, ET, ST>), dgrid, dblock, dlds, s, dn); break;
+    case 2: hipLaunchKernelGGL((k_down<2, ET, ST>), dgrid, dblock, dlds, s, dn); break;
+    case 3: hipLaunchKernelGGL((k_down<3, ET, ST>), dgrid, dblock, dlds, s, dn); break;
+    default: hipLaunchKernelGGL((k_down<4, ET, ST>), dgrid, dblock, dlds, s, dn); break;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 int decode_ws_size(const moe_layer_desc *d, int R)
 {
-    const int Imax = d->inter > d->shared_inter ? d->inter : d->shared_inter;
-    return static_cast<int>(decode_ws_bytes(R, d->n_experts, d->top_k, Imax));
-}
-
-int launch_decode_route(const moe_layer_desc *d, const float *x, int R, int32_t *ids, float *wts, float *gate,
-                        void *ws, hipStream_t s)
-{
-    const int Imax = d->inter > d->shared_inter ? d->inter : d->shared_inter;
-    const DecodeWs w = decode_ws_carve(ws, R, d->n_experts, d->top_k, Imax);
-    if (d->router_t == MOE_F32)
-        return launch_route_t<F32>(d, x, R, ids, wts, gate, w, s);
-    return launch_route_t<BF16>(d, x, R, ids, wts, gate, w, s);
+    return static_cast<int>(decode_ws_bytes(R, d->n_experts, d->top_k, imax_of(d)));
 }
 
 int launch_decode_forward(const moe_layer_desc *d, const float *x, int R, float *y, const int32_t *ids_in,
                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
                           float *gate_out, void *ws, hipStream_t s)
 {
-    const int Imax = d->inter > d->shared_inter ? d->inter : d->shared_inter;
-    const DecodeWs w = decode_ws_carve(ws, R, d->n_experts, d->top_k, Imax);
-    int rc;
-    if (ids_in) {
-        switch (R) {
-        case 1: hipLaunchKernelGGL((k_slots_from_routing<1>), dim3(1), dim3(64), 0, s, ids_in, wts_in, gate_in, d->top_k, d->n_experts, w.slots); break;
-        case 2: hipLaunchKernelGGL((k_slots_from_routing<2>), dim3(1), dim3(64), 0, s, ids_in, wts_in, gate_in, d->top_k, d->n_experts, w.slots); break;
-        case 3: hipLaunchKernelGGL((k_slots_from_routing<3>), dim3(1), dim3(64), 0, s, ids_in, wts_in, gate_in, d->top_k, d->n_experts, w.slots); break;
-        default: hipLaunchKernelGGL((k_slots_from_routing<4>), dim3(1), dim3(64), 0, s, ids_in, wts_in, gate_in, d->top_k, d->n_experts, w.slots); break;
-        }
-        rc = hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
-    } else {
-        rc = (d->router_t == MOE_F32) ? launch_route_t<F32>(d, x, R, ids_out, wts_out, gate_out, w, s)
-                                      : launch_route_t<BF16>(d, x, R, ids_out, wts_out, gate_out, w, s);
-    }
-    if (rc != MOE_OK)
-        return rc;
+    const DecodeWs w = decode_ws_carve(ws, R, d->n_experts, d->top_k, imax_of(d));
+    const RoutingIO io{ids_in, wts_in, gate_in, ids_out, wts_out, gate_out};
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32) {
-        if (et == MOE_F32) return launch_experts_t<F32, F32>(d, x, R, y, w, s);
-        if (et == MOE_BF16) return launch_experts_t<BF16, F32>(d, x, R, y, w, s);
-        return launch_experts_t<Q2, F32>(d, x, R, y, w, s);
+        if (et == MOE_F32) return launch_experts_t<F32, F32>(d, x, R, y, io, w, s);
+        if (et == MOE_BF16) return launch_experts_t<BF16, F32>(d, x, R, y, io, w, s);
+        return launch_experts_t<Q2, F32>(d, x, R, y, io, w, s);
     }
-    if (et == MOE_F32) return launch_experts_t<F32, BF16>(d, x, R, y, w, s);
-    if (et == MOE_BF16) return launch_experts_t<BF16, BF16>(d, x, R, y, w, s);
-    return launch_experts_t<Q2, BF16>(d, x, R, y, w, s);
+    if (et == MOE_F32) return launch_experts_t<F32, BF16>(d, x, R, y, io, w, s);
+    if (et == MOE_BF16) return launch_experts_t<BF16, BF16>(d, x, R, y, io, w, s);
+    return launch_experts_t<Q2, BF16>(d, x, R, y, io, w, s);
+}
+
+// Routing only: the logits, then the routing workgroup (no slot table).
+int launch_decode_route(const moe_layer_desc *d, const float *x, int R, int32_t *ids, float *wts, float *gate,
+                        void *ws, hipStream_t s)
+{
+    const DecodeWs w = decode_ws_carve(ws, R, d->n_experts, d->top_k, imax_of(d));
+    const GateUpArgs g = gateup_args<F32>(d, x, w);
+    int rc;
+    if (d->shared_t == MOE_F32)
+        rc = d->router_t == MOE_F32 ? launch_dense_t<F32, F32>(d, x, R, g, w, true, false, s)
+                                    : launch_dense_t<BF16, F32>(d, x, R, g, w, true, false, s);
+    else
+        rc = d->router_t == MOE_F32 ? launch_dense_t<F32, BF16>(d, x, R, g, w, true, false, s)
+                                    : launch_dense_t<BF16, BF16>(d, x, R, g, w, true, false, s);
+    if (rc != MOE_OK)
+        return rc;
+    const RoutingIO io{nullptr, nullptr, nullptr, ids, wts, gate};
+    return launch_route(d, R, io, w, false, s);
 }
 
 }  // namespace moe

@@ -10,6 +10,7 @@
 namespace moe {
 
 // decode / few-row path (R rows, 1 <= R <= 4)
+size_t gateup_lds_bytes(int R, int H, int E);
 int decode_ws_size(const moe_layer_desc *d, int R);
 int launch_decode_route(const moe_layer_desc *d, const float *x, int R, int32_t *ids, float *wts, float *gate,
                         void *ws, hipStream_t s);
