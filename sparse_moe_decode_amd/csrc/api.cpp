@@ -92,9 +92,9 @@ size_t ws_bytes_for(const moe_layer_desc *d, int T)
     if (T <= 0)
         return 256;
     const Path p = choose_path(T);
-    // the prefill path is served by few-row groups until its grouped kernels run
-    const int R = group_rows(d, p == kPrefill ? kFewRow : p, T);
-    return static_cast<size_t>(moe::decode_ws_size(d, R));
+    if (p == kPrefill)
+        return moe::prefill_ws_bytes(d, T);
+    return static_cast<size_t>(moe::decode_ws_size(d, group_rows(d, p, T)));
 }
 
 }  // namespace
@@ -143,8 +143,11 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T, int32_t *ids, 
         return MOE_EWORKSPACE;
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const Path path = choose_path(T);
+    if (path == kPrefill)
+        return moe::launch_prefill_route(d, x, T, ids, wts, gate, ws, s);
     const int H = d->hidden, K = d->top_k;
-    const int R = group_rows(d, kFewRow, T);
+    const int R = group_rows(d, path, T);
     for (int t = 0; t < T; t += R) {
         const int r = T - t < R ? T - t : R;
         rc = moe::launch_decode_route(d, x + static_cast<size_t>(t) * H, r, ids + static_cast<size_t>(t) * K,
@@ -181,8 +184,10 @@ int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y, co
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Path path = choose_path(T);
+    if (path == kPrefill)
+        return moe::launch_prefill_forward(d, x, T, y, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, ws, s);
     const int H = d->hidden, K = d->top_k;
-    const int R = group_rows(d, path == kPrefill ? kFewRow : path, T);
+    const int R = group_rows(d, path, T);
     for (int t = 0; t < T; t += R) {
         const int r = T - t < R ? T - t : R;
         const size_t ok = static_cast<size_t>(t) * K;
@@ -223,7 +228,8 @@ int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E, int3
     if (T == 0)
         return MOE_OK;
     (void)hipGetLastError();
-    return moe::launch_sort_by_expert(ids, T, K, E, counts, offsets, perm, ws, static_cast<hipStream_t>(stream));
+    return moe::launch_sort_by_expert(ids, T, K, E, counts, offsets, perm, ws, static_cast<hipStream_t>(stream),
+                                      nullptr);
 }
 
 int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream)

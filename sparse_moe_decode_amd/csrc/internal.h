@@ -24,6 +24,14 @@ int launch_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst,
 // stable counting sort of (row, slot) pairs by expert
 size_t sort_ws_bytes_tke(int64_t n, int E);
 int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                          int32_t *perm, void *ws, hipStream_t s);
+                          int32_t *perm, void *ws, hipStream_t s, int32_t *inv = nullptr);
+
+// prefill path (any number of rows; rows grouped by expert, MFMA GEMMs)
+size_t prefill_ws_bytes(const moe_layer_desc *d, int T);
+int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t *ids, float *wts, float *gate,
+                         void *ws, hipStream_t s);
+int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float *y, const int32_t *ids_in,
+                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
+                           float *gate_out, void *ws, hipStream_t s);
 
 }  // namespace moe

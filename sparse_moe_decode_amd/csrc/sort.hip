@@ -5,7 +5,8 @@
 //                   base positions.
 //   k_sort_scatter  each pair's rank among earlier pairs of its chunk with the
 //                   same expert gives its slot: perm[base + rank] = pair.
-// Integer-only and deterministic; the result is unique.
+// Integer-only and deterministic; the result is unique. Optionally also the
+// inverse permutation inv[pair] = sorted position.
 #include <hip/hip_runtime.h>
 
 #include "device_common.cuh"
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(1024) k_sort_hist(const int32_t *ids, int n, i
 }
 
 __global__ void __launch_bounds__(1024) k_sort_scatter(const int32_t *ids, int n, int E, const int *table,
-                                                      int32_t *perm)
+                                                      int32_t *perm, int32_t *inv)
 {
     __shared__ int le[kSortChunk];
     const int tid = threadIdx.x;
@@ -101,12 +102,15 @@ __global__ void __launch_bounds__(1024) k_sort_scatter(const int32_t *ids, int n
         int rank = 0;
         for (int j = 0; j < i; ++j)
             rank += (le[j] == e);
-        perm[table[static_cast<size_t>(blockIdx.x) * E + e] + rank] = base + i;
+        const int pos = table[static_cast<size_t>(blockIdx.x) * E + e] + rank;
+        perm[pos] = base + i;
+        if (inv)
+            inv[base + i] = pos;
     }
 }
 
 int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                          int32_t *perm, void *ws, hipStream_t s)
+                          int32_t *perm, void *ws, hipStream_t s, int32_t *inv)
 {
     const int n = T * K;
     const int chunks = (n + kSortChunk - 1) / kSortChunk;
@@ -116,7 +120,7 @@ int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *coun
     hipLaunchKernelGGL(k_sort_hist, dim3(chunks), dim3(1024), 0, s, ids, n, E, table, counts, offsets, ticket);
     if (hipGetLastError() != hipSuccess)
         return MOE_EHIP;
-    hipLaunchKernelGGL(k_sort_scatter, dim3(chunks), dim3(1024), 0, s, ids, n, E, table, perm);
+    hipLaunchKernelGGL(k_sort_scatter, dim3(chunks), dim3(1024), 0, s, ids, n, E, table, perm, inv);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -165,11 +165,11 @@ def run_calls(layer, x_host: np.ndarray, rows_per_call: int, force_path: str | N
     ids = torch.empty((T, layer.K), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, layer.K), dtype=torch.float32, device="cuda")
     gate = torch.empty((T,), dtype=torch.float32, device="cuda")
-    ws = layer.workspace(min(T, rows_per_call))
     old = os.environ.get("MOE_FORCE_PATH")
     if force_path:
         os.environ["MOE_FORCE_PATH"] = force_path
     try:
+        ws = layer.workspace(min(T, rows_per_call))
         for t in range(0, T, rows_per_call):
             r = min(rows_per_call, T - t)
             moe.forward(layer.desc, x[t:t + r], y[t:t + r], ws, ids_out=ids[t:t + r], wts_out=wts[t:t + r],

@@ -106,9 +106,11 @@ def test_duplicate_router_rows_tie_on_gpu():
     L = oracle_layer_from_arrays(a)
     ri, _, _, logits = L.route(x)
     G = gpu_layer_from_arrays(a)
-    got = run_calls(G, x, 1)
-    np.testing.assert_array_equal(got[0], ri)
-    assert_parity(got, _oracle_ref(L, x), "tie fixture")
+    ref = _oracle_ref(L, x)
+    for rows in (1, 200):   # decode and one prefill call
+        got = run_calls(G, x, rows)
+        np.testing.assert_array_equal(got[0], ri)
+        assert_parity(got, ref, f"tie fixture rows={rows}")
 
 
 @pytest.mark.parametrize("case", ["k_equals_e", "single_expert", "no_renorm", "bias", "zero_x", "wide"])
@@ -137,7 +139,7 @@ def test_edge_shapes(case):
     L = oracle_layer_from_arrays(a, renormalize=renorm)
     G = gpu_layer_from_arrays(a, renormalize=renorm)
     ref = _oracle_ref(L, x)
-    for rows in (1, 3, 4):
+    for rows in (1, 3, 4, T):   # decode, few-row, few-row, prefill (one call)
         assert_parity(run_calls(G, x, rows), ref, f"{case} rows={rows}")
 
 
@@ -153,7 +155,7 @@ def test_bf16_and_q2_small_shapes():
     L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
     G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
     ref = _oracle_ref(L, x)
-    for rows in (1, 2, 4):
+    for rows in (1, 2, 4, 11):
         assert_parity(run_calls(G, x, rows), ref, f"bf16 rows={rows}")
     _say("case: small 2-bit experts")
     import oracle
@@ -165,7 +167,7 @@ def test_bf16_and_q2_small_shapes():
     Gq = gpu_layer_from_arrays(dict(b, exp_gate=a["exp_gate"], exp_up=a["exp_up"], exp_down=a["exp_down"]),
                                router_t="bf16", expert_t="q2", shared_t="bf16")
     ref = _oracle_ref(Lq, x)
-    for rows in (1, 3):
+    for rows in (1, 3, 11):
         assert_parity(run_calls(Gq, x, rows), ref, f"q2 rows={rows}")
 
 
@@ -191,6 +193,70 @@ def test_given_routing_entry():
                         wts_in=wts[t:t + rows], gate_in=gate[t:t + rows])
         torch.cuda.synchronize()
         assert tolerance_ok(out.cpu().numpy(), y64).all()
+
+
+# ------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2"])
+@pytest.mark.parametrize("T", [5, 37, 300])
+def test_prefill_small(fmt, T):
+    """Grouped-GEMM path at small sizes: ragged expert groups (not multiples
+    of the 64-row tile), intermediate 96 (not a multiple of the 64-channel
+    block), all weight formats."""
+    _say(f"case: prefill {fmt} T={T}")
+    import oracle
+    rng = np.random.default_rng(1000 + T)
+    a = _random_arrays(rng, 256, 16, 4, 96, 64, rstd=0.05, estd=0.05)
+    a["router_bias"] = rng.standard_normal(16).astype(np.float32) * 0.5
+    x = rng.standard_normal((T, 256)).astype(np.float32)
+    rt = st = "f32" if fmt == "f32" else "bf16"
+    b = dict(a)
+    if fmt != "f32":
+        for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+            b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    if fmt == "q2":
+        src = {k: mi.bf16_bits_to_f32(b[k]).reshape(a[k].shape) for k in ("exp_gate", "exp_up", "exp_down")}
+        qo = dict(b)
+        for k in src:
+            qo[k] = [oracle.q2_quantize(m) for m in src[k]]
+        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t="q2", shared_t=st)
+        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t="q2", shared_t=st)
+    else:
+        L = oracle_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
+        G = gpu_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
+    ref = _oracle_ref(L, x)
+    assert_parity(run_calls(G, x, T), ref, f"prefill {fmt} T={T}")
+
+
+def test_prefill_forced_on_small_calls():
+    """MOE_FORCE_PATH=prefill runs the grouped path for 1..3 rows per call."""
+    _say("case: prefill forced for small calls")
+    cfg = mi.CONFIGS[0]
+    dense = mi.dense_weights(cfg)
+    stacks = mi.expert_stacks(cfg)
+    G = gpu_layer_from_config(cfg, dense, stacks)
+    L = oracle_layer_from_config(cfg, dense=dense, stacks=stacks)
+    x = mi.activations(cfg, T=7)
+    ref = _oracle_ref(L, x)
+    for rows in (1, 3):
+        assert_parity(run_calls(G, x, rows, force_path="prefill"), ref, f"forced prefill rows={rows}")
+
+
+def test_prefill_given_routing():
+    _say("case: prefill with caller-supplied routing")
+    rng = np.random.default_rng(52)
+    a = _random_arrays(rng, 128, 16, 3, 64, 64)
+    x = rng.standard_normal((40, 128)).astype(np.float32)
+    L = oracle_layer_from_arrays(a)
+    ri, rw, rg, y, y64 = L.forward(x)
+    G = gpu_layer_from_arrays(a)
+    import sparse_moe_decode_amd as moe
+    out = torch.empty((40, 128), dtype=torch.float32, device="cuda")
+    moe.forward(G.desc, torch.from_numpy(x).cuda(), out, G.workspace(40), ids_in=torch.from_numpy(ri).cuda(),
+                wts_in=torch.from_numpy(rw.astype(np.float32)).cuda(),
+                gate_in=torch.from_numpy(rg.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    assert tolerance_ok(out.cpu().numpy(), y64).all()
 
 
 # ------------------------------------------------------------ 2-bit format
