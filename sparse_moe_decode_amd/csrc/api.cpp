@@ -55,7 +55,7 @@ int validate_desc(const moe_layer_desc *d)
 int max_rows(const moe_layer_desc *d)
 {
     for (int r = moe::kMaxRows; r > 1; --r)
-        if (moe::gateup_lds_bytes(r, d->hidden, d->n_experts) + 4096 <= 60u * 1024u)
+        if (moe::gateup_lds_bytes(r, d->hidden, d->n_experts) + moe::kDecodeStaticLds <= 60u * 1024u)
             return r;
     return 1;
 }

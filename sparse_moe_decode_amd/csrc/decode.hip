@@ -1,23 +1,22 @@
 // Decode (1 row) and few-row (2..4 rows) path of the sparse MoE layer on gfx950.
 //
-// Four launches per call on the caller's stream; kernel boundaries are the
-// only synchronization (no cross-workgroup fences, counters or spin waits):
-//   k_dense          the routing-independent work: router logits in fp64
-//                    (products of bf16/fp32 weights with fp32 activations are
-//                    exact in double) plus the shared-gate logit, and the
-//                    shared expert's SwiGLU activations.
-//   k_route          one workgroup: exact top-K per row (one wave per row),
-//                    softmax weights over the selection, sigmoid gate, and the
-//                    slot table - the union of the rows' experts, slot 0 being
-//                    the shared expert weighted by the gate (router, top-k and
-//                    shared gate as one step, the shared expert as an extra
-//                    slot: Research notes page, section 1, "Metal").
-//   k_gateup_routed  two intermediate channels per wave of one selected
-//                    expert: gate and up rows streamed with 16-byte loads,
-//                    SwiGLU, scaled by the row's route weight.
-//   k_down           one output row per wave: D_s[j] . h'_s summed over all
-//                    slots, so the weighted combine happens inside the dot
-//                    product and each y element is written once.
+// Three launches per call on the caller's stream; kernel boundaries are the
+// only synchronization between workgroups (no fences, counters or spin waits):
+//   k_logits   router logits in fp64 (products of bf16/fp32 weights with fp32
+//              activations are exact in double) plus the shared-gate logit,
+//              one row per wave.
+//   k_gateup   the shared expert's gate/up channels, and - in every other
+//              workgroup - the exact top-K per row, softmax weights, sigmoid
+//              gate and slot table (the union of the rows' experts; slot 0 is
+//              the shared expert weighted by the gate: router, top-k and
+//              shared gate as one step, the shared expert as an extra slot,
+//              Research notes page, section 1, "Metal"), repeated per
+//              workgroup from the logits, followed by two intermediate
+//              channels per wave of one selected expert: gate and up rows
+//              streamed with 16-byte loads, SwiGLU, scaled by the route weight.
+//   k_down     one output row per wave: D_s[j] . h'_s summed over all slots,
+//              so the weighted combine happens inside the dot product and
+//              each y element is written once.
 // Each distinct selected expert is read once per call, however many rows
 // selected it (the few-row verify idea of the same page, section 1).
 #include <hip/hip_runtime.h>
@@ -98,20 +97,19 @@ struct RouteArgs {
     SlotTable *slots;          // published for the expert kernels (or null)
 };
 
-// One workgroup: routing of R rows (wave q selects row q), then the slot
-// table. With caller-supplied routing only the slot table is built (ids
-// outside [0, E) become expert 0 with weight 0).
+// Routing of the call's R rows inside one workgroup of at least R waves: wave
+// q selects row q from the logits (staged in `lg`, R rows of (E+1)&~1
+// doubles), or the caller's selection is taken as given (ids outside [0, E)
+// become expert 0 with weight 0); then wave 0 builds the slot table. Ends
+// with a workgroup barrier, after which `lg` may be reused.
 template <int R>
-__global__ void __launch_bounds__(256) k_route(RouteArgs a)
+__device__ inline void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
 {
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    double *lg = reinterpret_cast<double *>(lds_raw);   // [R][lgs]
-    __shared__ RouteLds rl;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     if (a.ids_in) {
         if (tid < R * a.K) {
-            const int q = tid / a.K, k = tid % a.K;
+            const int q = tid / a.K, k = tid - q * a.K;
             const int e = a.ids_in[tid];
             const bool ok = e >= 0 && e < a.E;
             rl.sel_e[q][k] = ok ? e : 0;
@@ -119,19 +117,33 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
         }
         if (tid < R)
             rl.g[tid] = a.gate_in[tid];
-        __syncthreads();
     } else {
         const int lgs = (a.E + 1) & ~1;
-        for (int i = tid; i < R * a.E; i += blockDim.x)
-            lg[(i / a.E) * lgs + i % a.E] = a.logits[i];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            for (int i = tid; i < a.E; i += blockDim.x)
+                lg[q * lgs + i] = a.logits[q * a.E + i];
         __syncthreads();
         if (wave < R) {
             wave_select(lg + wave * lgs, a.E, a.K, wave, rl, lane);
             wave_weights(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane);
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    if (wave == 0)
+        build_slots<R>(rl, a.K, lane);
+    __syncthreads();
+}
+
+// The routing of route_block to global memory: the selection, weights and
+// gate (when computed here and asked for) and the slot table (if a.slots).
+template <int R>
+__device__ inline void publish_route(const RouteArgs &a, const RouteLds &rl)
+{
+    const int tid = threadIdx.x;
+    if (!a.ids_in) {
         if (tid < R * a.K) {
-            const int q = tid / a.K, k = tid % a.K;
+            const int q = tid / a.K, k = tid - q * a.K;
             if (a.ids_out)
                 a.ids_out[tid] = rl.sel_e[q][k];
             if (a.wts_out)
@@ -140,19 +152,27 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
         if (tid < R && a.gate_out)
             a.gate_out[tid] = rl.g[tid];
     }
-    if (wave == 0 && a.slots) {
-        build_slots<R>(rl, a.K, lane);
-        __builtin_amdgcn_wave_barrier();
+    if (a.slots) {
         const int ns = rl.slots.nslots;
-        if (lane == 0)
+        if (tid == 0)
             a.slots->nslots = ns;
-        for (int i = lane; i < ns; i += kWave) {
+        for (int i = tid; i < ns; i += blockDim.x) {
             a.slots->expert[i] = rl.slots.expert[i];
 #pragma unroll
             for (int q = 0; q < R; ++q)
                 a.slots->w[i][q] = rl.slots.w[i][q];
         }
     }
+}
+
+// Routing on its own (the route-only entry point): one workgroup.
+template <int R>
+__global__ void __launch_bounds__(256) k_route(RouteArgs a)
+{
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    __shared__ RouteLds rl;
+    route_block<R>(a, reinterpret_cast<double *>(lds_raw), rl);
+    publish_route<R>(a, rl);
 }
 
 // ============================================================ gate / up
@@ -386,25 +406,44 @@ __device__ __forceinline__ void gateup_two(const GateUpArgs &p, const MatRef &G,
     }
 }
 
-// Routed experts: workgroup b covers channels of slot 1 + b / wg_per_slot.
-template <int R, typename ET>
-__global__ void __launch_bounds__(kGuWaves * kWave) k_gateup_routed(GateUpArgs p)
+// Gate/up of one call. Workgroups [0, n_sh) take channels of the shared
+// expert (unweighted; the gate multiplies them in the down pass) and start
+// streaming at once. Every later workgroup b first repeats the call's routing
+// from the logits (route_block: about a microsecond of one wave per row, hidden
+// behind the shared expert's stream), then takes channels of slot
+// 1 + b / wg_per_slot; workgroup b == 0 publishes the routing for the down pass
+// and the caller.
+template <int R, typename ET, typename ST>
+__global__ void __launch_bounds__(kGuWaves * kWave) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     float *xs = reinterpret_cast<float *>(lds_raw);   // [R][H]
     float *xsum = xs + R * p.H;                       // [R][H/32]
-    const int slot = 1 + blockIdx.x / p.wg_per_slot;
-    const int ch0 = (blockIdx.x % p.wg_per_slot) * p.ch_per_wg;
-    const int nslots = p.slots->nslots;
-    if (slot >= nslots)
+    __shared__ RouteLds rl;
+    const int wave = threadIdx.x / kWave;
+    if (static_cast<int>(blockIdx.x) < n_sh) {
+        const MatRef G{p.sg, p.Is, p.H}, U{p.su, p.Is, p.H};
+        float one[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            one[q] = 1.0f;
+        gateup_two<R, ST>(p, G, U, 0, blockIdx.x * p.ch_per_wg + wave * 2, p.Is, one, xs, xsum);
         return;
-    const int e = p.slots->expert[slot];
+    }
+    const int b = blockIdx.x - n_sh;
+    route_block<R>(ra, reinterpret_cast<double *>(lds_raw), rl);
+    if (b == 0)
+        publish_route<R>(ra, rl);
+    const int slot = 1 + b / p.wg_per_slot;
+    if (slot >= rl.slots.nslots)
+        return;
+    const int e = rl.slots.expert[slot];
     const MatRef G{p.eg + e * p.estride, p.I, p.H}, U{p.eu + e * p.estride, p.I, p.H};
     float w[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)
-        w[q] = p.slots->w[slot][q];
-    gateup_two<R, ET>(p, G, U, slot, ch0 + (threadIdx.x / kWave) * 2, p.I, w, xs, xsum);
+        w[q] = rl.slots.w[slot][q];
+    gateup_two<R, ET>(p, G, U, slot, (b % p.wg_per_slot) * p.ch_per_wg + wave * 2, p.I, w, xs, xsum);
 }
 
 // ================================================================= dense
@@ -451,26 +490,13 @@ __device__ __forceinline__ void router_chunk(BF16, const uint4 &u, int c, const 
 
 constexpr int kLgPrefetch = 4;   // 16-byte chunks per lane loaded before x is staged
 
-// Routing-independent work of a call: router logits (workgroups [0, n_lg_wg),
-// one row per wave, row E being the shared-gate vector) and the shared
-// expert's SwiGLU activations (workgroups n_lg_wg.., unweighted; the gate
-// multiplies them in the down pass).
-template <int R, typename RT, typename ST>
-__global__ void __launch_bounds__(256) k_dense(LogitArgs a, GateUpArgs p, int n_lg_wg)
+// Router logits of a call, one row per wave; row E is the shared-gate vector.
+template <int R, typename RT>
+__global__ void __launch_bounds__(256) k_logits(LogitArgs a)
 {
     extern __shared__ float xs[];   // [R][H]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    if (static_cast<int>(blockIdx.x) >= n_lg_wg) {
-        const MatRef G{p.sg, p.Is, p.H}, U{p.su, p.Is, p.H};
-        const int ch = (blockIdx.x - n_lg_wg) * p.ch_per_wg + (tid / kWave) * 2;
-        float one[R];
-#pragma unroll
-        for (int q = 0; q < R; ++q)
-            one[q] = 1.0f;
-        gateup_two<R, ST>(p, G, U, 0, ch, p.Is, one, xs, nullptr);
-        return;
-    }
     const int e = blockIdx.x * (blockDim.x / kWave) + tid / kWave;
     const bool live = e <= a.E;
     const size_t rb = static_cast<size_t>(a.H) * (RT::kChunk == 4 ? 4 : 2);
@@ -755,6 +781,8 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 
 static inline int imax_of(const moe_layer_desc *d) { return d->inter > d->shared_inter ? d->inter : d->shared_inter; }
 
+static_assert(sizeof(RouteLds) <= kDecodeStaticLds, "routing state exceeds its LDS bound");
+
 size_t gateup_lds_bytes(int R, int H, int E)
 {
     const size_t a = sizeof(float) * (R * H + R * (H >> 5)), b = sizeof(double) * R * ((E + 1) & ~1);
@@ -789,10 +817,9 @@ static GateUpArgs gateup_args(const moe_layer_desc *d, const float *x, const Dec
     return g;
 }
 
-// k_dense: logits (if `logits`) and the shared expert (if `shared`).
-template <typename RT, typename ST>
-static int launch_dense_t(const moe_layer_desc *d, const float *x, int R, const GateUpArgs &g, const DecodeWs &w,
-                          bool logits, bool shared, hipStream_t s)
+// k_logits: the router logits and the shared-gate logit of R rows.
+template <typename RT>
+static int launch_logits_t(const moe_layer_desc *d, const float *x, int R, const DecodeWs &w, hipStream_t s)
 {
     LogitArgs a;
     a.x = x;
@@ -803,21 +830,23 @@ static int launch_dense_t(const moe_layer_desc *d, const float *x, int R, const 
     a.gate_w = static_cast<const uint8_t *>(d->shared_gate_w);
     a.logits = w.logits;
     a.zlogit = w.zlogit;
-    const int n_lg = logits ? (a.E + 1 + 3) / 4 : 0;
-    const int n_sh = shared ? (d->shared_inter + g.ch_per_wg - 1) / g.ch_per_wg : 0;
-    const dim3 grid(n_lg + n_sh), block(256);
+    const dim3 grid((a.E + 1 + 3) / 4), block(256);
     const size_t lds = sizeof(float) * R * a.H;
     switch (R) {
-    case 1: hipLaunchKernelGGL((k_dense<1, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
-    case 2: hipLaunchKernelGGL((k_dense<2, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
-    case 3: hipLaunchKernelGGL((k_dense<3, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
-    default: hipLaunchKernelGGL((k_dense<4, RT, ST>), grid, block, lds, s, a, g, n_lg); break;
+    case 1: hipLaunchKernelGGL((k_logits<1, RT>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_logits<2, RT>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_logits<3, RT>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((k_logits<4, RT>), grid, block, lds, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-static int launch_route(const moe_layer_desc *d, int R, const RoutingIO &io, const DecodeWs &w, bool slots,
-                        hipStream_t s)
+static int launch_logits(const moe_layer_desc *d, const float *x, int R, const DecodeWs &w, hipStream_t s)
+{
+    return d->router_t == MOE_F32 ? launch_logits_t<F32>(d, x, R, w, s) : launch_logits_t<BF16>(d, x, R, w, s);
+}
+
+static RouteArgs route_args(const moe_layer_desc *d, const RoutingIO &io, const DecodeWs &w, bool slots)
 {
     RouteArgs a;
     a.logits = w.logits;
@@ -832,7 +861,13 @@ static int launch_route(const moe_layer_desc *d, int R, const RoutingIO &io, con
     a.wts_out = io.wts_out;
     a.gate_out = io.gate_out;
     a.slots = slots ? w.slots : nullptr;
-    const size_t lds = io.ids_in ? 0 : sizeof(double) * R * ((a.E + 1) & ~1);
+    return a;
+}
+
+static int launch_route(const moe_layer_desc *d, int R, const RoutingIO &io, const DecodeWs &w, hipStream_t s)
+{
+    const RouteArgs a = route_args(d, io, w, false);
+    const size_t lds = sizeof(double) * R * ((a.E + 1) & ~1);
     switch (R) {
     case 1: hipLaunchKernelGGL((k_route<1>), dim3(1), dim3(256), lds, s, a); break;
     case 2: hipLaunchKernelGGL((k_route<2>), dim3(1), dim3(256), lds, s, a); break;
@@ -848,23 +883,22 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
 {
     const int H = d->hidden, I = d->inter, Is = d->shared_inter, K = d->top_k;
     const int Imax = imax_of(d);
-    const GateUpArgs g = gateup_args<ET>(d, x, w);
-    int rc = d->router_t == MOE_F32 ? launch_dense_t<F32, ST>(d, x, R, g, w, !io.ids_in, true, s)
-                                    : launch_dense_t<BF16, ST>(d, x, R, g, w, !io.ids_in, true, s);
-    if (rc != MOE_OK)
-        return rc;
-    rc = launch_route(d, R, io, w, true, s);
-    if (rc != MOE_OK)
-        return rc;
+    if (!io.ids_in) {
+        const int rc = launch_logits(d, x, R, w, s);
+        if (rc != MOE_OK)
+            return rc;
+    }
     {
-        const dim3 block(kGuWaves * kWave);
-        const int grid = R * K * g.wg_per_slot;
-        const size_t lds = sizeof(float) * (R * H + R * (H >> 5));
+        const GateUpArgs g = gateup_args<ET>(d, x, w);
+        const RouteArgs ra = route_args(d, io, w, true);
+        const int n_sh = (Is + g.ch_per_wg - 1) / g.ch_per_wg;
+        const dim3 grid(n_sh + R * K * g.wg_per_slot), block(kGuWaves * kWave);
+        const size_t lds = gateup_lds_bytes(R, H, d->n_experts);
         switch (R) {
-        case 1: hipLaunchKernelGGL((k_gateup_routed<1, ET>), dim3(grid), block, lds, s, g); break;
-        case 2: hipLaunchKernelGGL((k_gateup_routed<2, ET>), dim3(grid), block, lds, s, g); break;
-        case 3: hipLaunchKernelGGL((k_gateup_routed<3, ET>), dim3(grid), block, lds, s, g); break;
-        default: hipLaunchKernelGGL((k_gateup_routed<4, ET>), dim3(grid), block, lds, s, g); break;
+        case 1: hipLaunchKernelGGL((k_gateup<1, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
+        case 2: hipLaunchKernelGGL((k_gateup<2, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
+        case 3: hipLaunchKernelGGL((k_gateup<3, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
+        default: hipLaunchKernelGGL((k_gateup<4, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
         }
         if (hipGetLastError() != hipSuccess)
             return MOE_EHIP;
@@ -922,18 +956,11 @@ int launch_decode_route(const moe_layer_desc *d, const float *x, int R, int32_t 
                         void *ws, hipStream_t s)
 {
     const DecodeWs w = decode_ws_carve(ws, R, d->n_experts, d->top_k, imax_of(d));
-    const GateUpArgs g = gateup_args<F32>(d, x, w);
-    int rc;
-    if (d->shared_t == MOE_F32)
-        rc = d->router_t == MOE_F32 ? launch_dense_t<F32, F32>(d, x, R, g, w, true, false, s)
-                                    : launch_dense_t<BF16, F32>(d, x, R, g, w, true, false, s);
-    else
-        rc = d->router_t == MOE_F32 ? launch_dense_t<F32, BF16>(d, x, R, g, w, true, false, s)
-                                    : launch_dense_t<BF16, BF16>(d, x, R, g, w, true, false, s);
+    const int rc = launch_logits(d, x, R, w, s);
     if (rc != MOE_OK)
         return rc;
     const RoutingIO io{nullptr, nullptr, nullptr, ids, wts, gate};
-    return launch_route(d, R, io, w, false, s);
+    return launch_route(d, R, io, w, s);
 }
 
 }  // namespace moe

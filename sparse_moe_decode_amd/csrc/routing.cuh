@@ -18,6 +18,7 @@ struct RouteLds {
     float sel_w[kMaxRows][kMaxK];
     double ex[kMaxRows][kMaxK];
     int cand[kMaxRows][kWave];
+    double cand_v[kMaxRows][kWave];
     float g[kMaxRows];
     SlotTable slots;
 };
@@ -39,21 +40,22 @@ __device__ __forceinline__ uint32_t f32_key(float v)
 //     non-candidate is below M, hence below the K-th largest.
 //  3. The candidates are ranked exactly (fp64 compare, then id).
 // The threshold is found by a bitwise binary search whose counts are
-// wave-wide ballots; broadcasts use readlane.
+// wave-wide ballots; the candidates are compacted into LDS and ranked there.
 __device__ inline void wave_select(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
 {
     constexpr int PL = kMaxE / kWave;
     const int npl = (E + kWave - 1) / kWave;
+    // Every slot is written on every path (no divergent writes into the
+    // array), so the keys stay plain registers.
     uint32_t key[PL];
     uint32_t mk = 0;   // 0 is below every real key
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
         const int e = lane + m * kWave;
-        key[m] = 0;
-        if (m < npl && e < E) {
-            key[m] = f32_key(static_cast<float>(lg[e]));
-            mk = key[m] > mk ? key[m] : mk;
-        }
+        const bool in = e < E;
+        const uint32_t k = f32_key(static_cast<float>(lg[in ? e : 0]));
+        key[m] = in ? k : 0u;
+        mk = key[m] > mk ? key[m] : mk;
     }
     uint32_t t = 0;
     for (int b = 31; b >= 0; --b) {
@@ -65,38 +67,41 @@ __device__ inline void wave_select(const double *lg, int E, int K, int q, RouteL
     int C = 0;
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
-        if (m >= npl)
-            break;
-        const bool cand = key[m] >= t && key[m] != 0;
-        const unsigned long long mask = __ballot(cand);
-        const int pos = C + __popcll(mask & lt);
-        if (cand && pos < kWave)
-            rl.cand[q][pos] = lane + m * kWave;
-        C += __popcll(mask);
+        if (m < npl) {
+            const bool cand = key[m] >= t && key[m] != 0;
+            const unsigned long long mask = __ballot(cand);
+            const int pos = C + __popcll(mask & lt);
+            if (cand && pos < kWave) {
+                const int e = lane + m * kWave;
+                rl.cand[q][pos] = e;
+                rl.cand_v[q][pos] = lg[e];
+            }
+            C += __popcll(mask);
+        }
     }
     __builtin_amdgcn_wave_barrier();
     if (C <= kWave) {
+        // rank of each candidate among the candidates; the table is read
+        // with same-address (broadcast) LDS loads
         const int e = lane < C ? rl.cand[q][lane] : 0;
-        const double v = lane < C ? lg[e] : 0.0;
-        const long long vb = __double_as_longlong(v);
-        const int vlo = static_cast<int>(vb & 0xffffffff), vhi = static_cast<int>(vb >> 32);
+        const double v = lane < C ? rl.cand_v[q][lane] : 0.0;
         int rank = 0;
+#pragma unroll 4
         for (int j = 0; j < C; ++j) {
-            const unsigned long long bj =
-                (static_cast<unsigned long long>(static_cast<uint32_t>(__builtin_amdgcn_readlane(vhi, j))) << 32) |
-                static_cast<uint32_t>(__builtin_amdgcn_readlane(vlo, j));
-            const double vj = __longlong_as_double(static_cast<long long>(bj));
-            const int ej = __builtin_amdgcn_readlane(e, j);
+            const double vj = rl.cand_v[q][j];
+            const int ej = rl.cand[q][j];
             rank += (vj > v) | ((vj == v) & (ej < e));
         }
         if (lane < C && rank < K) {
             rl.sel_e[q][rank] = e;
             rl.sel_l[q][rank] = v;
         }
+        __builtin_amdgcn_wave_barrier();
         return;
     }
     // many candidates (massive exact ties): rank each against all logits
-    for (int m = 0; m < npl; ++m) {
+#pragma unroll
+    for (int m = 0; m < PL; ++m) {
         const int e = lane + m * kWave;
         if (e >= E || key[m] < t)
             continue;
@@ -111,6 +116,7 @@ __device__ inline void wave_select(const double *lg, int E, int K, int q, RouteL
             rl.sel_l[q][rank] = v;
         }
     }
+    __builtin_amdgcn_wave_barrier();
 }
 
 // Route weights of row q by the wave that selected it, in selection order:
@@ -129,8 +135,10 @@ __device__ inline void wave_weights(const double *lg, int E, int K, int renorm, 
     __builtin_amdgcn_wave_barrier();
     double denom = 0.0;
     if (renorm) {
-        for (int j = 0; j < K; ++j)
-            denom += rl.ex[q][j];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < K)
+                denom += rl.ex[q][j];
     } else {
         double s = 0.0;
         for (int e = lane; e < E; e += kWave)
