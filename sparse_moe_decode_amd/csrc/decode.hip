@@ -11,9 +11,10 @@
 //              the shared expert weighted by the gate: router, top-k and
 //              shared gate as one step, the shared expert as an extra slot,
 //              Research notes page, section 1, "Metal"), repeated per
-//              workgroup from the logits, followed by two intermediate
-//              channels per wave of one selected expert: gate and up rows
-//              streamed with 16-byte loads, SwiGLU, scaled by the route weight.
+//              workgroup from the logits, followed by one intermediate
+//              channel per wave of one selected expert: gate and up rows
+//              streamed with 16-byte non-temporal loads, SwiGLU, scaled by the
+//              route weight.
 //   k_down     one output row per wave: D_s[j] . h'_s summed over all slots,
 //              so the weighted combine happens inside the dot product and
 //              each y element is written once.
@@ -37,7 +38,7 @@ namespace moe {
 // (row-major over [R][K]); the weight of a slot for row q is that row's route
 // weight of the expert (0 if the row did not select it). Run by one wave.
 template <int R>
-__device__ inline void build_slots(RouteLds &rl, int K, int lane)
+__device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
 {
     if (R == 1) {
         if (lane < K) {
@@ -97,13 +98,15 @@ struct RouteArgs {
     SlotTable *slots;          // published for the expert kernels (or null)
 };
 
-// Routing of the call's R rows inside one workgroup of at least R waves: wave
+constexpr int kRouteThreads = 256;   // threads of every workgroup that routes
+
+// Routing of the call's R rows inside one workgroup of kRouteThreads: wave
 // q selects row q from the logits (staged in `lg`, R rows of (E+1)&~1
 // doubles), or the caller's selection is taken as given (ids outside [0, E)
 // become expert 0 with weight 0); then wave 0 builds the slot table. Ends
 // with a workgroup barrier, after which `lg` may be reused.
 template <int R>
-__device__ inline void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
+__device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
 {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -118,11 +121,25 @@ __device__ inline void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
         if (tid < R)
             rl.g[tid] = a.gate_in[tid];
     } else {
+        // every load is issued before the first LDS store
+        constexpr int PT = kMaxE / kRouteThreads;
         const int lgs = (a.E + 1) & ~1;
+        double v[R][PT];
 #pragma unroll
         for (int q = 0; q < R; ++q)
-            for (int i = tid; i < a.E; i += blockDim.x)
-                lg[q * lgs + i] = a.logits[q * a.E + i];
+#pragma unroll
+            for (int u = 0; u < PT; ++u) {
+                const int i = tid + u * kRouteThreads;
+                v[q][u] = i < a.E ? a.logits[q * a.E + i] : 0.0;
+            }
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+            for (int u = 0; u < PT; ++u) {
+                const int i = tid + u * kRouteThreads;
+                if (i < a.E)
+                    lg[q * lgs + i] = v[q][u];
+            }
         __syncthreads();
         if (wave < R) {
             wave_select(lg + wave * lgs, a.E, a.K, wave, rl, lane);
@@ -138,7 +155,7 @@ __device__ inline void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
 // The routing of route_block to global memory: the selection, weights and
 // gate (when computed here and asked for) and the slot table (if a.slots).
 template <int R>
-__device__ inline void publish_route(const RouteArgs &a, const RouteLds &rl)
+__device__ __forceinline__ void publish_route(const RouteArgs &a, const RouteLds &rl)
 {
     const int tid = threadIdx.x;
     if (!a.ids_in) {
@@ -167,7 +184,7 @@ __device__ inline void publish_route(const RouteArgs &a, const RouteLds &rl)
 
 // Routing on its own (the route-only entry point): one workgroup.
 template <int R>
-__global__ void __launch_bounds__(256) k_route(RouteArgs a)
+__global__ void __launch_bounds__(kRouteThreads) k_route(RouteArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     __shared__ RouteLds rl;
@@ -185,11 +202,12 @@ struct GateUpArgs {
     const uint8_t *sg, *su;    // shared gate/up
     const SlotTable *slots;
     float *hbuf;               // [S][R][Imax]
-    int ch_per_wg;             // channels per workgroup (two per wave)
+    int ch_per_wg;             // channels per workgroup (one per wave)
     int wg_per_slot;           // workgroups per routed slot
 };
 
 constexpr int kGuWaves = 4;
+static_assert(kGuWaves * kWave == kRouteThreads, "gate/up workgroups route");
 constexpr int kGuMaxChunks = 4;   // chunks per lane in flight per row
 
 // Raw row chunks of one channel (gate and up), kGuMaxChunks per lane.
@@ -212,8 +230,8 @@ __device__ __forceinline__ void load_rows(W, const MatRef &G, const MatRef &U, i
     for (int u = 0; u < kGuMaxChunks; ++u) {
         const int k = base + u * kWave + lane;
         if (k < nch) {
-            r.g[u] = *reinterpret_cast<const uint4 *>(G.base + (static_cast<size_t>(ch) * G.cols + k * W::kChunk) * esz);
-            r.u[u] = *reinterpret_cast<const uint4 *>(U.base + (static_cast<size_t>(ch) * U.cols + k * W::kChunk) * esz);
+            r.g[u] = ld_nt16(G.base + (static_cast<size_t>(ch) * G.cols + k * W::kChunk) * esz);
+            r.u[u] = ld_nt16(U.base + (static_cast<size_t>(ch) * U.cols + k * W::kChunk) * esz);
         }
     }
 }
@@ -225,11 +243,11 @@ __device__ __forceinline__ void load_rows(Q2, const MatRef &G, const MatRef &U, 
     for (int u = 0; u < kGuMaxChunks; ++u) {
         const int b = base + u * kWave + lane;
         if (b < nch) {
-            r.gc[u] = *reinterpret_cast<const uint2 *>(G.base + static_cast<size_t>(ch) * (G.cols >> 2) + b * 8);
-            r.uc[u] = *reinterpret_cast<const uint2 *>(U.base + static_cast<size_t>(ch) * (U.cols >> 2) + b * 8);
-            r.gs[u] = *reinterpret_cast<const uint32_t *>(G.base + static_cast<size_t>(G.rows) * (G.cols >> 2) +
+            r.gc[u] = ld_nt8(G.base + static_cast<size_t>(ch) * (G.cols >> 2) + b * 8);
+            r.uc[u] = ld_nt8(U.base + static_cast<size_t>(ch) * (U.cols >> 2) + b * 8);
+            r.gs[u] = ld_nt4(G.base + static_cast<size_t>(G.rows) * (G.cols >> 2) +
                                                           (static_cast<size_t>(ch) * nb + b) * 4);
-            r.us[u] = *reinterpret_cast<const uint32_t *>(U.base + static_cast<size_t>(U.rows) * (U.cols >> 2) +
+            r.us[u] = ld_nt4(U.base + static_cast<size_t>(U.rows) * (U.cols >> 2) +
                                                           (static_cast<size_t>(ch) * nb + b) * 4);
         }
     }
@@ -346,8 +364,8 @@ __device__ __forceinline__ void finish_channel(const GateUpArgs &p, int slot, in
 {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-        a[q] = lane_group_sum(a[q], kWave);
-        c[q] = lane_group_sum(c[q], kWave);
+        a[q] = wave_sum(a[q]);
+        c[q] = wave_sum(c[q]);
     }
     if (lane < R) {
         float hv = 0.0f;
@@ -359,51 +377,41 @@ __device__ __forceinline__ void finish_channel(const GateUpArgs &p, int slot, in
     }
 }
 
-// The two channels ch, ch+1 of this wave. When a row fits one chunk set
-// (H <= 256 * chunk), both channels' rows are requested before x is staged,
-// so the weight stream overlaps the staging; wider rows stream in steps.
+// Channel ch of this wave (nothing when ch >= n, but x is still staged: every
+// wave takes part in the workgroup barrier). When a row fits one chunk set
+// (H <= 256 * chunk), the gate and up rows are requested before x is
+// staged, so the weight stream overlaps the staging; wider rows stream in
+// steps.
 template <int R, typename W>
-__device__ __forceinline__ void gateup_two(const GateUpArgs &p, const MatRef &G, const MatRef &U, int slot, int ch,
+__device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G, const MatRef &U, int slot, int ch,
                                            int n, const float (&wq)[R], float *xs, float *xsum)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int nck = p.H / W::kChunk;
-    float a[R], c[R], a2[R], c2[R];
+    float a[R], c[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)
-        a[q] = c[q] = a2[q] = c2[q] = 0.0f;
+        a[q] = c[q] = 0.0f;
     if (nck <= kWave * kGuMaxChunks) {
-        RowChunks<W> r0, r1;
+        RowChunks<W> r;
         if (ch < n)
-            load_rows(W{}, G, U, ch, 0, lane, nck, r0);
-        if (ch + 1 < n)
-            load_rows(W{}, G, U, ch + 1, 0, lane, nck, r1);
+            load_rows(W{}, G, U, ch, 0, lane, nck, r);
         stage_x<R, W>(p.x, p.H, xs, xsum);
         if (ch < n) {
-            dot_rows<R>(W{}, r0, 0, lane, nck, xs, p.H, xsum, a, c);
+            dot_rows<R>(W{}, r, 0, lane, nck, xs, p.H, xsum, a, c);
             finish_channel<R>(p, slot, ch, a, c, wq, lane);
-        }
-        if (ch + 1 < n) {
-            dot_rows<R>(W{}, r1, 0, lane, nck, xs, p.H, xsum, a2, c2);
-            finish_channel<R>(p, slot, ch + 1, a2, c2, wq, lane);
         }
         return;
     }
     stage_x<R, W>(p.x, p.H, xs, xsum);
-    for (int i = 0; i < 2; ++i) {
-        const int cc = ch + i;
-        if (cc >= n)
-            break;
-#pragma unroll
-        for (int q = 0; q < R; ++q)
-            a[q] = c[q] = 0.0f;
-        for (int base = 0; base < nck; base += kWave * kGuMaxChunks) {
-            RowChunks<W> part;
-            load_rows(W{}, G, U, cc, base, lane, nck, part);
-            dot_rows<R>(W{}, part, base, lane, nck, xs, p.H, xsum, a, c);
-        }
-        finish_channel<R>(p, slot, cc, a, c, wq, lane);
+    if (ch >= n)
+        return;
+    for (int base = 0; base < nck; base += kWave * kGuMaxChunks) {
+        RowChunks<W> part;
+        load_rows(W{}, G, U, ch, base, lane, nck, part);
+        dot_rows<R>(W{}, part, base, lane, nck, xs, p.H, xsum, a, c);
     }
+    finish_channel<R>(p, slot, ch, a, c, wq, lane);
 }
 
 // Gate/up of one call. Workgroups [0, n_sh) take channels of the shared
@@ -427,7 +435,7 @@ __global__ void __launch_bounds__(kGuWaves * kWave) k_gateup(GateUpArgs p, Route
 #pragma unroll
         for (int q = 0; q < R; ++q)
             one[q] = 1.0f;
-        gateup_two<R, ST>(p, G, U, 0, blockIdx.x * p.ch_per_wg + wave * 2, p.Is, one, xs, xsum);
+        gateup_one<R, ST>(p, G, U, 0, blockIdx.x * p.ch_per_wg + wave, p.Is, one, xs, xsum);
         return;
     }
     const int b = blockIdx.x - n_sh;
@@ -443,7 +451,7 @@ __global__ void __launch_bounds__(kGuWaves * kWave) k_gateup(GateUpArgs p, Route
 #pragma unroll
     for (int q = 0; q < R; ++q)
         w[q] = rl.slots.w[slot][q];
-    gateup_two<R, ET>(p, G, U, slot, (b % p.wg_per_slot) * p.ch_per_wg + wave * 2, p.I, w, xs, xsum);
+    gateup_one<R, ET>(p, G, U, slot, (b % p.wg_per_slot) * p.ch_per_wg + wave, p.I, w, xs, xsum);
 }
 
 // ================================================================= dense
@@ -508,7 +516,7 @@ __global__ void __launch_bounds__(256) k_logits(LogitArgs a)
     for (int u = 0; u < kLgPrefetch; ++u) {
         const int c = lane + u * kWave;
         if (live && c < nch)
-            w[u] = *reinterpret_cast<const uint4 *>(row + c * 16);
+            w[u] = ld_nt16(row + c * 16);
     }
     for (int i = tid; i < R * a.H / 4; i += blockDim.x)
         reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(a.x)[i];
@@ -526,12 +534,12 @@ __global__ void __launch_bounds__(256) k_logits(LogitArgs a)
             router_chunk<R>(RT{}, w[u], c, xs, a.H, acc);
     }
     for (int c = lane + kLgPrefetch * kWave; c < nch; c += kWave) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(row + c * 16);
+        const uint4 u = ld_nt16(row + c * 16);
         router_chunk<R>(RT{}, u, c, xs, a.H, acc);
     }
 #pragma unroll
     for (int q = 0; q < R; ++q)
-        acc[q] = lane_group_sum(acc[q], kWave);
+        acc[q] = wave_sum(acc[q]);
     if (lane == 0) {
 #pragma unroll
         for (int q = 0; q < R; ++q) {
@@ -570,7 +578,7 @@ struct DnPiece<BF16> {
     uint4 v;
     __device__ __forceinline__ void load(const MatRef &M, int j, int c)
     {
-        v = *reinterpret_cast<const uint4 *>(M.base + (static_cast<size_t>(j) * M.cols + c * 8) * 2);
+        v = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 8) * 2);
     }
     template <int R>
     __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
@@ -598,7 +606,8 @@ struct DnPiece<F32> {
     float4 v;
     __device__ __forceinline__ void load(const MatRef &M, int j, int c)
     {
-        v = *reinterpret_cast<const float4 *>(M.base + (static_cast<size_t>(j) * M.cols + c * 4) * 4);
+        const uint4 u = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 4) * 4);
+        v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
     template <int R>
     __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
@@ -619,8 +628,8 @@ struct DnPiece<Q2> {
     {
         const int nb = M.cols >> 5;
         const int b = c >> 2;
-        codes = *reinterpret_cast<const uint16_t *>(M.base + static_cast<size_t>(j) * (M.cols >> 2) + c * 2);
-        sm = *reinterpret_cast<const uint32_t *>(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) +
+        codes = ld_nt2(M.base + static_cast<size_t>(j) * (M.cols >> 2) + c * 2);
+        sm = ld_nt4(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) +
                                                  (static_cast<size_t>(j) * nb + b) * 4);
     }
     // h8: sums of each 8 consecutive h values (for the min term)
@@ -770,7 +779,7 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     if (live) {
 #pragma unroll
         for (int q = 0; q < R; ++q) {
-            const float v = lane_group_sum(acc[q], kWave);
+            const float v = wave_sum(acc[q]);
             if (lane == 0)
                 p.y[q * p.H + j] = v;
         }
@@ -812,7 +821,7 @@ static GateUpArgs gateup_args(const moe_layer_desc *d, const float *x, const Dec
     g.su = static_cast<const uint8_t *>(d->sh_up);
     g.slots = w.slots;
     g.hbuf = w.hbuf;
-    g.ch_per_wg = kGuWaves * 2;
+    g.ch_per_wg = kGuWaves;
     g.wg_per_slot = (g.I + g.ch_per_wg - 1) / g.ch_per_wg;
     return g;
 }
@@ -869,10 +878,10 @@ static int launch_route(const moe_layer_desc *d, int R, const RoutingIO &io, con
     const RouteArgs a = route_args(d, io, w, false);
     const size_t lds = sizeof(double) * R * ((a.E + 1) & ~1);
     switch (R) {
-    case 1: hipLaunchKernelGGL((k_route<1>), dim3(1), dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_route<2>), dim3(1), dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((k_route<3>), dim3(1), dim3(256), lds, s, a); break;
-    default: hipLaunchKernelGGL((k_route<4>), dim3(1), dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_route<1>), dim3(1), dim3(kRouteThreads), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_route<2>), dim3(1), dim3(kRouteThreads), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_route<3>), dim3(1), dim3(kRouteThreads), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_route<4>), dim3(1), dim3(kRouteThreads), lds, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

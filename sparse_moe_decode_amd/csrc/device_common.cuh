@@ -151,6 +151,75 @@ __device__ __forceinline__ T lane_group_sum(T v, int width)
     return v;
 }
 
+// Loads of weight data, which each call reads once: non-temporal, so the
+// stream does not displace the small hot data (activations, routing state)
+// from the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void *p)
+{
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void *p)
+{
+    const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+__device__ __forceinline__ uint32_t ld_nt2(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+}
+
+// Sum over the 64 lanes of a wave, returned in every lane: DPP adds within
+// each row of 16 lanes (quad permutations [1,0,3,2] and [2,3,0,1], then row
+// rotations by 4 and 8), then the four row sums read from lanes 0/16/32/48.
+__device__ __forceinline__ float dpp_row_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = dpp_row_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ double wave_sum(double v)
+{
+#define MOE_DPP_ADD_F64(ctrl)                                                                                    \
+    {                                                                                                            \
+        const long long b = __double_as_longlong(v);                                                             \
+        const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffff), ctrl, 0xF, 0xF, false);  \
+        const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), ctrl, 0xF, 0xF, false);         \
+        v += __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));              \
+    }
+    MOE_DPP_ADD_F64(0xB1)
+    MOE_DPP_ADD_F64(0x4E)
+    MOE_DPP_ADD_F64(0x124)
+    MOE_DPP_ADD_F64(0x128)
+#undef MOE_DPP_ADD_F64
+    double r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const long long b = __double_as_longlong(v);
+        const int lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffff), 16 * i);
+        const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 16 * i);
+        r[i] = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
 __device__ __forceinline__ float silu_mul(float a, float c)
 {
     return a / (1.0f + __expf(-a)) * c;

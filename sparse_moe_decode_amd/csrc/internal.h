@@ -12,7 +12,7 @@ namespace moe {
 // decode / few-row path (R rows, 1 <= R <= 4)
 size_t gateup_lds_bytes(int R, int H, int E);
 // Bound on the static LDS of the decode kernels (the routing state).
-constexpr size_t kDecodeStaticLds = 8192;
+constexpr size_t kDecodeStaticLds = 12288;
 int decode_ws_size(const moe_layer_desc *d, int R);
 int launch_decode_route(const moe_layer_desc *d, const float *x, int R, int32_t *ids, float *wts, float *gate,
                         void *ws, hipStream_t s);

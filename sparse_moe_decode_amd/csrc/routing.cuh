@@ -17,8 +17,12 @@ struct RouteLds {
     double sel_l[kMaxRows][kMaxK];
     float sel_w[kMaxRows][kMaxK];
     double ex[kMaxRows][kMaxK];
-    int cand[kMaxRows][kWave];
-    double cand_v[kMaxRows][kWave];
+    alignas(16) int cand[kMaxRows][kWave];
+    alignas(16) double cand_v[kMaxRows][kWave];
+    alignas(16) uint64_t cand_p[kMaxRows][kWave];
+    alignas(16) uint32_t pmax[kMaxRows][kWave / 2];
+    uint32_t srt_k[kMaxRows][kMaxK + 1];
+    double srt_v[kMaxRows][kMaxK + 1];
     float g[kMaxRows];
     SlotTable slots;
 };
@@ -30,72 +34,158 @@ __device__ __forceinline__ uint32_t f32_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exact rank of candidate `lane` among the C <= 64 candidates of row q
+// (rl.cand / rl.cand_v, padded with NaN to a multiple of 8), fp64 compare then
+// id; lanes with rank < K write the selection.
+__device__ __forceinline__ void rank_exact(int C, int K, int q, RouteLds &rl, int lane)
+{
+    const int C8 = (C + 7) & ~7;
+    if (lane >= C && lane < C8)
+        rl.cand_v[q][lane] = __builtin_nan("");
+    __builtin_amdgcn_wave_barrier();
+    const int e = lane < C ? rl.cand[q][lane] : 0;
+    const double v = lane < C ? rl.cand_v[q][lane] : 0.0;
+    int rank = 0;
+    for (int j = 0; j < C; j += 8) {
+        double2 pv[4];
+        int4 pe[2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            pv[u] = *reinterpret_cast<const double2 *>(&rl.cand_v[q][j + 2 * u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            pe[u] = *reinterpret_cast<const int4 *>(&rl.cand[q][j + 4 * u]);
+        const double vj[8] = {pv[0].x, pv[0].y, pv[1].x, pv[1].y, pv[2].x, pv[2].y, pv[3].x, pv[3].y};
+        const int ej[8] = {pe[0].x, pe[0].y, pe[0].z, pe[0].w, pe[1].x, pe[1].y, pe[1].z, pe[1].w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            rank += (vj[u] > v) | ((vj[u] == v) & (ej[u] < e));
+    }
+    if (lane < C && rank < K) {
+        rl.sel_e[q][rank] = e;
+        rl.sel_l[q][rank] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Top-K of one row of E logits (double, in LDS) by one wave, under the order
 // "logit desc, then id asc". Writes rl.sel_e[q][0..K) and rl.sel_l[q][0..K)
-// in that order. Expert e = lane + 64*m is element m of lane `lane`.
-//  1. Each lane's maximum; the K-th largest lane maximum M is at most the
-//     K-th largest logit (the K lanes above it hold K distinct logits >= M).
-//  2. Candidates: logits whose fp32 rounding is >= fp32(M). Rounding to fp32
-//     is monotone, so every logit of the true top K is a candidate and every
-//     non-candidate is below M, hence below the K-th largest.
-//  3. The candidates are ranked exactly (fp64 compare, then id).
-// The threshold is found by a bitwise binary search whose counts are
-// wave-wide ballots; the candidates are compacted into LDS and ranked there.
-__device__ inline void wave_select(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
+// in that order. Expert e = lane + 64*m is element m of lane `lane`; PL is
+// the number of elements per lane (E <= 64*PL).
+//  1. Keys: order-preserving integers of the fp32 roundings (rounding to
+//     fp32 is monotone). M = the K-th largest of the 32 maxima of lane pairs;
+//     the K pairs at or above it hold K distinct logits whose keys are >= M,
+//     so the K-th largest logit has key >= M.
+//  2. Candidates: logits with key >= M; every logit of the true top K is one.
+//     They are compacted into LDS.
+//  3. Ranking by (key desc, id asc) packed in 64 bits. This is the exact
+//     order unless two of the first K+1 share a key but not a value; that is
+//     checked, and then the candidates are ranked in fp64 (rank_exact).
+// More than 64 candidates (massive ties) take a slower exact path.
+template <int PL>
+__device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
 {
-    constexpr int PL = kMaxE / kWave;
-    const int npl = (E + kWave - 1) / kWave;
-    // Every slot is written on every path (no divergent writes into the
-    // array), so the keys stay plain registers.
+    double d[PL];
     uint32_t key[PL];
-    uint32_t mk = 0;   // 0 is below every real key
+    uint32_t mk = 0;   // 0 is below every key of a non-NaN value
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
         const int e = lane + m * kWave;
         const bool in = e < E;
-        const uint32_t k = f32_key(static_cast<float>(lg[in ? e : 0]));
+        d[m] = lg[in ? e : 0];
+        const uint32_t k = f32_key(static_cast<float>(d[m]));
         key[m] = in ? k : 0u;
         mk = key[m] > mk ? key[m] : mk;
     }
-    uint32_t t = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t c = t | (1u << b);
-        if (__popcll(__ballot(mk >= c)) >= K)
-            t = c;
+    // 1. maximum over the lane pair (2i, 2i+1): DPP quad permutation [1,0,3,2]
+    const uint32_t other =
+        static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mk), 0xB1, 0xF, 0xF, false));
+    const uint32_t pm = other > mk ? other : mk;
+    if ((lane & 1) == 0)
+        rl.pmax[q][lane >> 1] = pm;
+    __builtin_amdgcn_wave_barrier();
+    // lane l counts the pair maxima above pair maximum l%32 in half l/32
+    const uint32_t v = rl.pmax[q][lane & 31];
+    const uint32_t *half = &rl.pmax[q][16 * (lane >> 5)];
+    uint4 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = *reinterpret_cast<const uint4 *>(half + 4 * j);
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        gt += (o[j].x > v) + (o[j].y > v) + (o[j].z > v) + (o[j].w > v);
+    gt += __shfl_xor(gt, 32);
+    // exactly K-1 above: the K-th largest; with ties at that value no lane
+    // may see K-1, then: fewer than K above and at least K at or above
+    unsigned long long hit = __ballot(lane < 32 && gt == K - 1);
+    if (hit == 0) {
+        int ge = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ge += (o[j].x >= v) + (o[j].y >= v) + (o[j].z >= v) + (o[j].w >= v);
+        ge += __shfl_xor(ge, 32);
+        hit = __ballot(lane < 32 && gt < K && ge >= K);
     }
+    const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), __builtin_ctzll(hit)));
+
+    // 2. compaction: exclusive prefix of the per-lane counts from ballots of
+    // their bits
+    int cnt = 0;
+#pragma unroll
+    for (int m = 0; m < PL; ++m)
+        cnt += (key[m] >= t) & (key[m] != 0);
     const unsigned long long lt = (1ull << lane) - 1ull;
-    int C = 0;
+    int pos = 0, C = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= PL; ++b) {
+        const unsigned long long mb = __ballot((cnt >> b) & 1);
+        pos += __popcll(mb & lt) << b;
+        C += __popcll(mb) << b;
+    }
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
-        if (m < npl) {
-            const bool cand = key[m] >= t && key[m] != 0;
-            const unsigned long long mask = __ballot(cand);
-            const int pos = C + __popcll(mask & lt);
-            if (cand && pos < kWave) {
-                const int e = lane + m * kWave;
-                rl.cand[q][pos] = e;
-                rl.cand_v[q][pos] = lg[e];
-            }
-            C += __popcll(mask);
+        const bool c = (key[m] >= t) & (key[m] != 0);
+        if (c && pos < kWave) {
+            const int e = lane + m * kWave;
+            rl.cand[q][pos] = e;
+            rl.cand_v[q][pos] = d[m];
+            rl.cand_p[q][pos] = (static_cast<uint64_t>(key[m]) << 32) | static_cast<uint32_t>(~e);
         }
+        pos += c;
     }
-    __builtin_amdgcn_wave_barrier();
     if (C <= kWave) {
-        // rank of each candidate among the candidates; the table is read
-        // with same-address (broadcast) LDS loads
-        const int e = lane < C ? rl.cand[q][lane] : 0;
-        const double v = lane < C ? rl.cand_v[q][lane] : 0.0;
+        // 3. rank by packed key (padding 0 is below every candidate)
+        const int C4 = (C + 3) & ~3;
+        if (lane >= C && lane < C4)
+            rl.cand_p[q][lane] = 0;
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t p = rl.cand_p[q][lane];
         int rank = 0;
-#pragma unroll 4
-        for (int j = 0; j < C; ++j) {
-            const double vj = rl.cand_v[q][j];
-            const int ej = rl.cand[q][j];
-            rank += (vj > v) | ((vj == v) & (ej < e));
+        for (int j = 0; j < C; j += 4) {
+            const ulonglong2 a = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]);
+            const ulonglong2 b = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]);
+            rank += (a.x > p) + (a.y > p) + (b.x > p) + (b.y > p);
         }
-        if (lane < C && rank < K) {
+        const bool live = lane < C;
+        const int e = static_cast<int>(~static_cast<uint32_t>(p));
+        const double val = rl.cand_v[q][lane];
+        if (live && rank < K) {
             rl.sel_e[q][rank] = e;
-            rl.sel_l[q][rank] = v;
+            rl.sel_l[q][rank] = val;
         }
+        if (live && rank <= K) {
+            rl.srt_k[q][rank] = static_cast<uint32_t>(p >> 32);
+            rl.srt_v[q][rank] = val;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // neighbours r, r+1 (r < K) with one key but two values are the only
+        // way the packed order can differ from the exact one
+        const int nchk = K < C - 1 ? K : C - 1;
+        const bool bad = lane < nchk && rl.srt_k[q][lane] == rl.srt_k[q][lane + 1] &&
+                         rl.srt_v[q][lane] != rl.srt_v[q][lane + 1];
+        if (__ballot(bad) != 0)
+            rank_exact(C, K, q, rl, lane);
         __builtin_amdgcn_wave_barrier();
         return;
     }
@@ -105,11 +195,11 @@ __device__ inline void wave_select(const double *lg, int E, int K, int q, RouteL
         const int e = lane + m * kWave;
         if (e >= E || key[m] < t)
             continue;
-        const double v = lg[e];
+        const double v = d[m];
         int rank = 0;
         for (int e2 = 0; e2 < E; ++e2) {
-            const double o = lg[e2];
-            rank += (o > v) | ((o == v) & (e2 < e));
+            const double o2 = lg[e2];
+            rank += (o2 > v) | ((o2 == v) & (e2 < e));
         }
         if (rank < K) {
             rl.sel_e[q][rank] = e;
@@ -119,19 +209,31 @@ __device__ inline void wave_select(const double *lg, int E, int K, int q, RouteL
     __builtin_amdgcn_wave_barrier();
 }
 
+__device__ __forceinline__ void wave_select(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
+{
+    if (E <= 8 * kWave)
+        wave_select_pl<8>(lg, E, K, q, rl, lane);
+    else
+        wave_select_pl<kMaxE / kWave>(lg, E, K, q, rl, lane);
+}
+
 // Route weights of row q by the wave that selected it, in selection order:
 // w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the selection
-// (renormalized) or over all E logits; the gate sigmoid(z_q).
-__device__ inline void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
-                                    int lane)
+// (renormalized) or over all E logits; the gate sigmoid(z_q) = 1/(1+exp(-z_q)).
+// Lane k < K evaluates exp(l_k - l_0), lane K evaluates exp(-z), in one pass.
+__device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
+                                             int lane)
 {
     __builtin_amdgcn_wave_barrier();
     const double l0 = rl.sel_l[q][0];
-    double v = 0.0;
-    if (lane < K) {
-        v = exp(rl.sel_l[q][lane] - l0);
+    double arg = 0.0;
+    if (lane < K)
+        arg = rl.sel_l[q][lane] - l0;
+    else if (lane == K)
+        arg = -z;
+    const double v = exp(arg);
+    if (lane < K)
         rl.ex[q][lane] = v;
-    }
     __builtin_amdgcn_wave_barrier();
     double denom = 0.0;
     if (renorm) {
@@ -145,10 +247,12 @@ __device__ inline void wave_weights(const double *lg, int E, int K, int renorm, 
             s += exp(lg[e] - l0);
         denom = lane_group_sum(s, kWave);
     }
+    const double r = (lane < K ? v : 1.0) / (lane < K ? denom : 1.0 + v);
     if (lane < K)
-        rl.sel_w[q][lane] = static_cast<float>(v / denom);
-    if (lane == 0)
-        rl.g[q] = static_cast<float>(1.0 / (1.0 + exp(-z)));
+        rl.sel_w[q][lane] = static_cast<float>(r);
+    if (lane == K)
+        rl.g[q] = static_cast<float>(r);
+    __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace moe
