@@ -208,6 +208,11 @@ struct GateUpArgs {
 
 constexpr int kGuWaves = 4;
 static_assert(kGuWaves * kWave == kRouteThreads, "gate/up workgroups route");
+// Waves per SIMD the one-row gate/up kernel is compiled for (a register
+// budget of 512/6 per lane): six 4-wave workgroups per CU keep a decode
+// call's 1,400-odd workgroups resident at once, so none waits for a free slot
+// and then repeats the routing late.
+constexpr int kGuMinWaves = 6;
 constexpr int kGuMaxChunks = 4;   // chunks per lane in flight per row
 
 // Raw row chunks of one channel (gate and up), kGuMaxChunks per lane.
@@ -422,7 +427,7 @@ __device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G,
 // 1 + b / wg_per_slot; workgroup b == 0 publishes the routing for the down pass
 // and the caller.
 template <int R, typename ET, typename ST>
-__global__ void __launch_bounds__(kGuWaves * kWave) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
+__global__ void __launch_bounds__(kGuWaves * kWave, R == 1 ? kGuMinWaves : 1) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     float *xs = reinterpret_cast<float *>(lds_raw);   // [R][H]

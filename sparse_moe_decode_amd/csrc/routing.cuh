@@ -85,15 +85,13 @@ __device__ __forceinline__ void rank_exact(int C, int K, int q, RouteLds &rl, in
 template <int PL>
 __device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
 {
-    double d[PL];
     uint32_t key[PL];
     uint32_t mk = 0;   // 0 is below every key of a non-NaN value
 #pragma unroll
     for (int m = 0; m < PL; ++m) {
         const int e = lane + m * kWave;
         const bool in = e < E;
-        d[m] = lg[in ? e : 0];
-        const uint32_t k = f32_key(static_cast<float>(d[m]));
+        const uint32_t k = f32_key(static_cast<float>(lg[in ? e : 0]));
         key[m] = in ? k : 0u;
         mk = key[m] > mk ? key[m] : mk;
     }
@@ -149,7 +147,7 @@ __device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, i
         if (c && pos < kWave) {
             const int e = lane + m * kWave;
             rl.cand[q][pos] = e;
-            rl.cand_v[q][pos] = d[m];
+            rl.cand_v[q][pos] = lg[e];
             rl.cand_p[q][pos] = (static_cast<uint64_t>(key[m]) << 32) | static_cast<uint32_t>(~e);
         }
         pos += c;
@@ -195,7 +193,7 @@ __device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, i
         const int e = lane + m * kWave;
         if (e >= E || key[m] < t)
             continue;
-        const double v = d[m];
+        const double v = lg[e];
         int rank = 0;
         for (int e2 = 0; e2 < E; ++e2) {
             const double o2 = lg[e2];
