@@ -19,7 +19,6 @@ the plain double-precision CPU oracle on a bounded sample of the same tokens.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -151,13 +150,8 @@ def traffic_for(kernel_key: str, cfg_name: str):
 
 
 def source_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_moe_decode_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from sparse_moe_decode_amd.profiling import source_sha as sha
+    return sha()
 
 
 # ---------------------------------------------------------- CPU baseline
