@@ -24,6 +24,8 @@
 
 #include <cfloat>
 #include <climits>
+#include <mutex>
+#include <vector>
 
 #include "device_common.cuh"
 #include "internal.h"
@@ -45,8 +47,13 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
             rl.slots.expert[lane + 1] = rl.sel_e[0][lane];
             rl.slots.w[lane + 1][0] = rl.sel_w[0][lane];
         }
+        if (lane <= K) {
+            rl.slots.rmask[lane] = 1u;
+            rl.slots.pstart[lane] = lane;
+        }
         if (lane == 0) {
             rl.slots.nslots = K + 1;
+            rl.slots.pstart[K + 1] = K + 1;
             rl.slots.expert[0] = -1;
             rl.slots.w[0][0] = rl.g[0];
         }
@@ -67,24 +74,54 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
     }
     const unsigned long long mask = __ballot(first);
     const int slot = 1 + __popcll(mask & ((1ull << lane) - 1ull));
+    const int ns = 1 + __popcll(mask);
+    uint32_t rm = 0;
     if (first) {
         rl.slots.expert[slot] = e;
 #pragma unroll
         for (int q = 0; q < R; ++q) {
             float w = 0.0f;
+            bool used = false;
             for (int k = 0; k < K; ++k)
-                if (rl.sel_e[q][k] == e)
+                if (rl.sel_e[q][k] == e) {
                     w += rl.sel_w[q][k];
+                    used = true;
+                }
             rl.slots.w[slot][q] = w;
+            rm |= used ? 1u << q : 0u;
         }
+        rl.slots.rmask[slot] = rm;
     }
+    // pair numbering: slot 0 (all rows) first, then the slots in order;
+    // lane l holds the first-appearance flag of slot 1 + (its rank)
+    const int cnt = first ? __popc(rm) : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += t;
+    }
+    if (first)
+        rl.slots.pstart[slot] = R + incl - cnt;
     if (lane == 0) {
-        rl.slots.nslots = 1 + __popcll(mask);
+        rl.slots.nslots = ns;
         rl.slots.expert[0] = -1;
+        rl.slots.rmask[0] = (1u << R) - 1u;
+        rl.slots.pstart[0] = 0;
 #pragma unroll
         for (int q = 0; q < R; ++q)
             rl.slots.w[0][q] = rl.g[q];
     }
+    if (lane == kWave - 1)
+        rl.slots.pstart[ns] = R + incl;
+}
+
+// Pair (row i of hbuf) of row q in `slot`, or -1 if the row does not use it.
+__device__ __forceinline__ int pair_of(const SlotTable &t, int slot, int q)
+{
+    const uint32_t m = t.rmask[slot];
+    return ((m >> q) & 1u) ? t.pstart[slot] + __popc(m & ((1u << q) - 1u)) : -1;
 }
 
 struct RouteArgs {
@@ -175,10 +212,14 @@ __device__ __forceinline__ void publish_route(const RouteArgs &a, const RouteLds
             a.slots->nslots = ns;
         for (int i = tid; i < ns; i += blockDim.x) {
             a.slots->expert[i] = rl.slots.expert[i];
+            a.slots->rmask[i] = rl.slots.rmask[i];
+            a.slots->pstart[i] = rl.slots.pstart[i];
 #pragma unroll
             for (int q = 0; q < R; ++q)
                 a.slots->w[i][q] = rl.slots.w[i][q];
         }
+        if (tid == 0)
+            a.slots->pstart[ns] = rl.slots.pstart[ns];
     }
 }
 
@@ -213,17 +254,30 @@ static_assert(kGuWaves * kWave == kRouteThreads, "gate/up workgroups route");
 // call's 1,400-odd workgroups resident at once, so none waits for a free slot
 // and then repeats the routing late.
 constexpr int kGuMinWaves = 6;
-constexpr int kGuMaxChunks = 4;   // chunks per lane in flight per row
+// Few-row calls: four waves per SIMD (128 registers), enough for the two
+// sets of rows in flight.
+constexpr int kGuMinWavesRows = 4;
+// Chunks per lane in flight per row: four 16-byte chunks (a 2048-wide bf16
+// row per wave), or one 2-bit block (a 2048-wide row per wave; wider rows
+// stream in steps).
+template <typename W>
+struct GuChunks {
+    static constexpr int value = 4;
+};
+template <>
+struct GuChunks<Q2> {
+    static constexpr int value = 1;
+};
 
-// Raw row chunks of one channel (gate and up), kGuMaxChunks per lane.
+// Raw row chunks of one channel (gate and up), GuChunks<W> per lane.
 template <typename W>
 struct RowChunks {
-    uint4 g[kGuMaxChunks], u[kGuMaxChunks];
+    uint4 g[GuChunks<W>::value], u[GuChunks<W>::value];
 };
 template <>
 struct RowChunks<Q2> {
-    uint2 gc[kGuMaxChunks], uc[kGuMaxChunks];
-    uint32_t gs[kGuMaxChunks], us[kGuMaxChunks];
+    uint2 gc[GuChunks<Q2>::value], uc[GuChunks<Q2>::value];
+    uint32_t gs[GuChunks<Q2>::value], us[GuChunks<Q2>::value];
 };
 
 template <typename W>
@@ -232,7 +286,7 @@ __device__ __forceinline__ void load_rows(W, const MatRef &G, const MatRef &U, i
 {
     constexpr int esz = W::kChunk == 4 ? 4 : 2;   // f32 / bf16 element bytes
 #pragma unroll
-    for (int u = 0; u < kGuMaxChunks; ++u) {
+    for (int u = 0; u < GuChunks<W>::value; ++u) {
         const int k = base + u * kWave + lane;
         if (k < nch) {
             r.g[u] = ld_nt16(G.base + (static_cast<size_t>(ch) * G.cols + k * W::kChunk) * esz);
@@ -245,7 +299,7 @@ __device__ __forceinline__ void load_rows(Q2, const MatRef &G, const MatRef &U, 
 {
     const int nb = G.cols >> 5;
 #pragma unroll
-    for (int u = 0; u < kGuMaxChunks; ++u) {
+    for (int u = 0; u < GuChunks<Q2>::value; ++u) {
         const int b = base + u * kWave + lane;
         if (b < nch) {
             r.gc[u] = ld_nt8(G.base + static_cast<size_t>(ch) * (G.cols >> 2) + b * 8);
@@ -317,12 +371,47 @@ __device__ __forceinline__ void dot_block(const uint2 &cw, uint32_t sm, int b, c
     }
 }
 
+// The gate and up blocks at the same position share their x values: each
+// float4 of x is used for both as soon as it is read.
+template <int R>
+__device__ __forceinline__ void dot_block2(const uint2 &gc, uint32_t gsm, const uint2 &uc, uint32_t usm, int b,
+                                           const float *xs, int H, const float *xsum, float (&a)[R], float (&c)[R])
+{
+    const float gsc = f16_to_f32(gsm & 0xffffu), gmn = f16_to_f32(gsm >> 16);
+    const float usc = f16_to_f32(usm & 0xffffu), umn = f16_to_f32(usm >> 16);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float *x = xs + q * H + b * 32;
+        float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t dg = half ? gc.y : gc.x, du = half ? uc.y : uc.x;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const float4 xv = *reinterpret_cast<const float4 *>(x + half * 16 + j4 * 4);
+                const uint32_t bg = dg >> (8 * j4), bu = du >> (8 * j4);
+                ga = fmaf(static_cast<float>(bg & 3u), xv.x, ga);
+                ga = fmaf(static_cast<float>((bg >> 2) & 3u), xv.y, ga);
+                ga = fmaf(static_cast<float>((bg >> 4) & 3u), xv.z, ga);
+                ga = fmaf(static_cast<float>((bg >> 6) & 3u), xv.w, ga);
+                ua = fmaf(static_cast<float>(bu & 3u), xv.x, ua);
+                ua = fmaf(static_cast<float>((bu >> 2) & 3u), xv.y, ua);
+                ua = fmaf(static_cast<float>((bu >> 4) & 3u), xv.z, ua);
+                ua = fmaf(static_cast<float>((bu >> 6) & 3u), xv.w, ua);
+            }
+        }
+        const float sx = xsum[q * (H >> 5) + b];
+        a[q] = fmaf(gsc, ga, fmaf(gmn, sx, a[q]));
+        c[q] = fmaf(usc, ua, fmaf(umn, sx, c[q]));
+    }
+}
+
 template <int R, typename W>
 __device__ __forceinline__ void dot_rows(W, const RowChunks<W> &r, int base, int lane, int nch, const float *xs,
                                          int H, const float *, float (&a)[R], float (&c)[R])
 {
 #pragma unroll
-    for (int u = 0; u < kGuMaxChunks; ++u) {
+    for (int u = 0; u < GuChunks<W>::value; ++u) {
         const int k = base + u * kWave + lane;
         if (k < nch) {
             dot_chunk<R>(W{}, r.g[u], k, xs, H, a);
@@ -335,12 +424,10 @@ __device__ __forceinline__ void dot_rows(Q2, const RowChunks<Q2> &r, int base, i
                                          int H, const float *xsum, float (&a)[R], float (&c)[R])
 {
 #pragma unroll
-    for (int u = 0; u < kGuMaxChunks; ++u) {
+    for (int u = 0; u < GuChunks<Q2>::value; ++u) {
         const int b = base + u * kWave + lane;
-        if (b < nch) {
-            dot_block<R>(r.gc[u], r.gs[u], b, xs, H, xsum, a);
-            dot_block<R>(r.uc[u], r.us[u], b, xs, H, xsum, c);
-        }
+        if (b < nch)
+            dot_block2<R>(r.gc[u], r.gs[u], r.uc[u], r.us[u], b, xs, H, xsum, a, c);
     }
 }
 
@@ -362,10 +449,11 @@ __device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float 
     }
 }
 
-// h'[slot][q][ch] = w_q * silu(a) * c for one channel, from lane partials.
+// h'(pair of row q)[ch] = w_q * silu(a_q) * c_q for one channel, from lane
+// partials; rows with pair < 0 are not written.
 template <int R>
-__device__ __forceinline__ void finish_channel(const GateUpArgs &p, int slot, int ch, float (&a)[R], float (&c)[R],
-                                               const float (&wq)[R], int lane)
+__device__ __forceinline__ void finish_channel(const GateUpArgs &p, const int (&pair)[R], int ch, float (&a)[R],
+                                               float (&c)[R], const float (&wq)[R], int lane)
 {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -374,22 +462,43 @@ __device__ __forceinline__ void finish_channel(const GateUpArgs &p, int slot, in
     }
     if (lane < R) {
         float hv = 0.0f;
+        int pr = -1;
 #pragma unroll
         for (int q = 0; q < R; ++q)
-            if (q == lane)
+            if (q == lane) {
                 hv = silu_mul(a[q], c[q]) * wq[q];
-        p.hbuf[(static_cast<size_t>(slot) * R + lane) * p.Imax + ch] = hv;
+                pr = pair[q];
+            }
+        if (pr >= 0)
+            p.hbuf[static_cast<size_t>(pr) * p.Imax + ch] = hv;
     }
 }
 
-// Channel ch of this wave (nothing when ch >= n, but x is still staged: every
-// wave takes part in the workgroup barrier). When a row fits one chunk set
-// (H <= 256 * chunk), the gate and up rows are requested before x is
-// staged, so the weight stream overlaps the staging; wider rows stream in
-// steps.
+// One routed channel for the rows that use its slot: the rows' dot products
+// one at a time from the loaded gate/up rows, h' written to the row's pair.
 template <int R, typename W>
-__device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G, const MatRef &U, int slot, int ch,
-                                           int n, const float (&wq)[R], float *xs, float *xsum)
+__device__ __forceinline__ void routed_channel(const GateUpArgs &p, const RowChunks<W> &r, const SlotTable &t,
+                                               int slot, int ch, const float *xs, const float *xsum, int lane)
+{
+    const int nck = p.H / W::kChunk;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int pr = pair_of(t, slot, q);
+        if (pr >= 0) {
+            float a[1] = {0.0f}, c[1] = {0.0f};
+            dot_rows<1>(W{}, r, 0, lane, nck, xs + q * p.H, p.H, xsum + q * (p.H >> 5), a, c);
+            const float hv = silu_mul(wave_sum(a[0]), wave_sum(c[0])) * t.w[slot][q];
+            if (lane == 0)
+                p.hbuf[static_cast<size_t>(pr) * p.Imax + ch] = hv;
+        }
+    }
+}
+
+// One channel of rows wider than one chunk set (H > 256 * chunk): the gate
+// and up rows stream in steps; x is already staged.
+template <int R, typename W>
+__device__ __forceinline__ void gateup_wide(const GateUpArgs &p, const MatRef &G, const MatRef &U, const int (&pair)[R],
+                                            int ch, const float (&wq)[R], const float *xs, const float *xsum)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int nck = p.H / W::kChunk;
@@ -397,26 +506,46 @@ __device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G,
 #pragma unroll
     for (int q = 0; q < R; ++q)
         a[q] = c[q] = 0.0f;
-    if (nck <= kWave * kGuMaxChunks) {
+    for (int base = 0; base < nck; base += kWave * GuChunks<W>::value) {
+        RowChunks<W> part;
+        load_rows(W{}, G, U, ch, base, lane, nck, part);
+        dot_rows<R>(W{}, part, base, lane, nck, xs, p.H, xsum, a, c);
+    }
+    finish_channel<R>(p, pair, ch, a, c, wq, lane);
+}
+
+// Channel ch (< n, or nothing) of the shared expert by this wave, all rows
+// with weight 1. x is staged here (every wave takes part in the barrier).
+// When a row fits one chunk set (H <= 256 * chunk), the gate and up rows
+// are requested before x is staged, so the weight stream overlaps the staging.
+template <int R, typename W>
+__device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G, const MatRef &U, int ch, int n,
+                                           const float (&wq)[R], float *xs, float *xsum)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nck = p.H / W::kChunk;
+    int pair[R];   // the shared expert's pairs are rows 0..R-1
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        pair[q] = q;
+    if (nck <= kWave * GuChunks<W>::value) {
+        float a[R], c[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            a[q] = c[q] = 0.0f;
         RowChunks<W> r;
         if (ch < n)
             load_rows(W{}, G, U, ch, 0, lane, nck, r);
         stage_x<R, W>(p.x, p.H, xs, xsum);
         if (ch < n) {
             dot_rows<R>(W{}, r, 0, lane, nck, xs, p.H, xsum, a, c);
-            finish_channel<R>(p, slot, ch, a, c, wq, lane);
+            finish_channel<R>(p, pair, ch, a, c, wq, lane);
         }
         return;
     }
     stage_x<R, W>(p.x, p.H, xs, xsum);
-    if (ch >= n)
-        return;
-    for (int base = 0; base < nck; base += kWave * kGuMaxChunks) {
-        RowChunks<W> part;
-        load_rows(W{}, G, U, ch, base, lane, nck, part);
-        dot_rows<R>(W{}, part, base, lane, nck, xs, p.H, xsum, a, c);
-    }
-    finish_channel<R>(p, slot, ch, a, c, wq, lane);
+    if (ch < n)
+        gateup_wide<R, W>(p, G, U, pair, ch, wq, xs, xsum);
 }
 
 // Gate/up of one call. Workgroups [0, n_sh) take channels of the shared
@@ -427,7 +556,7 @@ __device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G,
 // 1 + b / wg_per_slot; workgroup b == 0 publishes the routing for the down pass
 // and the caller.
 template <int R, typename ET, typename ST>
-__global__ void __launch_bounds__(kGuWaves * kWave, R == 1 ? kGuMinWaves : 1) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
+__global__ void __launch_bounds__(kGuWaves * kWave, R == 1 ? kGuMinWaves : kGuMinWavesRows) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     float *xs = reinterpret_cast<float *>(lds_raw);   // [R][H]
@@ -440,23 +569,93 @@ __global__ void __launch_bounds__(kGuWaves * kWave, R == 1 ? kGuMinWaves : 1) k_
 #pragma unroll
         for (int q = 0; q < R; ++q)
             one[q] = 1.0f;
-        gateup_one<R, ST>(p, G, U, 0, blockIdx.x * p.ch_per_wg + wave, p.Is, one, xs, xsum);
+        gateup_one<R, ST>(p, G, U, blockIdx.x * p.ch_per_wg + wave, p.Is, one, xs, xsum);
         return;
     }
     const int b = blockIdx.x - n_sh;
     route_block<R>(ra, reinterpret_cast<double *>(lds_raw), rl);
     if (b == 0)
         publish_route<R>(ra, rl);
-    const int slot = 1 + b / p.wg_per_slot;
-    if (slot >= rl.slots.nslots)
+    // work items: ch_per_wg channels of one routed slot; item i is slot
+    // 1 + i / wg_per_slot; the routed workgroups stride over the items
+    const int nitems = (rl.slots.nslots - 1) * p.wg_per_slot;
+    if (b >= nitems)
         return;
-    const int e = rl.slots.expert[slot];
-    const MatRef G{p.eg + e * p.estride, p.I, p.H}, U{p.eu + e * p.estride, p.I, p.H};
-    float w[R];
+    const int stride = gridDim.x - n_sh;
+    const int lane = threadIdx.x & (kWave - 1);
+    auto item_mats = [&](int it, int &slot, int &ch, MatRef &G, MatRef &U) {
+        slot = 1 + it / p.wg_per_slot;
+        ch = (it % p.wg_per_slot) * p.ch_per_wg + wave;
+        const int e = rl.slots.expert[slot];
+        G = MatRef{p.eg + e * p.estride, p.I, p.H};
+        U = MatRef{p.eu + e * p.estride, p.I, p.H};
+    };
+    const int nck = p.H / ET::kChunk;
+    if (nck > kWave * GuChunks<ET>::value) {
+        // wide rows: each item streams its rows in steps
+        stage_x<R, ET>(p.x, p.H, xs, xsum);
+        for (int it = b; it < nitems; it += stride) {
+            int slot, ch;
+            MatRef G, U;
+            item_mats(it, slot, ch, G, U);
+            float w[R];
+            int pair[R];
 #pragma unroll
-    for (int q = 0; q < R; ++q)
-        w[q] = rl.slots.w[slot][q];
-    gateup_one<R, ET>(p, G, U, slot, (b % p.wg_per_slot) * p.ch_per_wg + wave, p.I, w, xs, xsum);
+            for (int q = 0; q < R; ++q) {
+                w[q] = rl.slots.w[slot][q];
+                pair[q] = pair_of(rl.slots, slot, q);
+            }
+            if (ch < p.I)
+                gateup_wide<R, ET>(p, G, U, pair, ch, w, xs, xsum);
+        }
+        return;
+    }
+    if constexpr (R == 1) {
+        // decode: normally one item per routed workgroup
+        auto one_item = [&](int it, bool first) {
+            int slot, ch;
+            MatRef G, U;
+            item_mats(it, slot, ch, G, U);
+            RowChunks<ET> r;
+            if (ch < p.I)
+                load_rows(ET{}, G, U, ch, 0, lane, nck, r);
+            if (first)
+                stage_x<R, ET>(p.x, p.H, xs, xsum);
+            if (ch < p.I)
+                routed_channel<R, ET>(p, r, rl.slots, slot, ch, xs, xsum, lane);
+        };
+        one_item(b, true);
+        for (int it = b + stride; it < nitems; it += stride)
+            one_item(it, false);
+    } else {
+        // few-row: the next item's rows are requested before the current
+        // one is reduced
+        int it = b, slot, ch;
+        MatRef G, U;
+        item_mats(it, slot, ch, G, U);
+        RowChunks<ET> cur, nxt;
+        if (ch < p.I)
+            load_rows(ET{}, G, U, ch, 0, lane, nck, cur);
+        stage_x<R, ET>(p.x, p.H, xs, xsum);
+        while (true) {
+            const int nx = it + stride;
+            int nslot = 0, nch = 0;
+            if (nx < nitems) {
+                MatRef G2, U2;
+                item_mats(nx, nslot, nch, G2, U2);
+                if (nch < p.I)
+                    load_rows(ET{}, G2, U2, nch, 0, lane, nck, nxt);
+            }
+            if (ch < p.I)
+                routed_channel<R, ET>(p, cur, rl.slots, slot, ch, xs, xsum, lane);
+            if (nx >= nitems)
+                break;
+            cur = nxt;
+            it = nx;
+            slot = nslot;
+            ch = nch;
+        }
+    }
 }
 
 // ================================================================= dense
@@ -565,16 +764,18 @@ struct DownArgs {
     size_t estride;            // bytes per routed [H][I] matrix
     const uint8_t *sd;         // shared down
     const SlotTable *slots;
-    const float *hbuf;         // [S][R][Imax]
-    int group;                 // slots staged in LDS at a time
+    const float *hbuf;         // [pairs][Imax]
+    int max_pairs;             // R * (K + 1): bound on the (slot, row) pairs
 };
 
 constexpr int kDnWaves = 8;    // one output row per wave
-constexpr int kDnBatch = 12;   // slot rows whose loads are in flight together
+// LDS for the staged h' rows of the down pass; beyond it h' is read from L2
+constexpr size_t kDnStageLds = 144 * 1024;
 
 // Down rows are read in pieces of 8 elements (bf16: 16 bytes; 2-bit: 2 bytes
 // of codes plus the block's scale/min) or 4 elements (fp32: 16 bytes). Lane
-// c of a row takes piece c (then c+64, ...).
+// c of a row takes piece c (then c+64, ...). fma1 adds piece . h[piece] of
+// one h' row.
 template <typename W>
 struct DnPiece;
 template <>
@@ -585,24 +786,20 @@ struct DnPiece<BF16> {
     {
         v = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 8) * 2);
     }
-    template <int R>
-    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
+    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
     {
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 h0 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8);
-            const float4 h1 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8 + 4);
-            float s = acc[q];
-            s = fmaf(bf16_lo(v.x), h0.x, s);
-            s = fmaf(bf16_hi(v.x), h0.y, s);
-            s = fmaf(bf16_lo(v.y), h0.z, s);
-            s = fmaf(bf16_hi(v.y), h0.w, s);
-            s = fmaf(bf16_lo(v.z), h1.x, s);
-            s = fmaf(bf16_hi(v.z), h1.y, s);
-            s = fmaf(bf16_lo(v.w), h1.z, s);
-            s = fmaf(bf16_hi(v.w), h1.w, s);
-            acc[q] = s;
-        }
+        const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
+        const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
+        float s = acc;
+        s = fmaf(bf16_lo(v.x), h0.x, s);
+        s = fmaf(bf16_hi(v.x), h0.y, s);
+        s = fmaf(bf16_lo(v.y), h0.z, s);
+        s = fmaf(bf16_hi(v.y), h0.w, s);
+        s = fmaf(bf16_lo(v.z), h1.x, s);
+        s = fmaf(bf16_hi(v.z), h1.y, s);
+        s = fmaf(bf16_lo(v.w), h1.z, s);
+        s = fmaf(bf16_hi(v.w), h1.w, s);
+        acc = s;
     }
 };
 template <>
@@ -614,14 +811,10 @@ struct DnPiece<F32> {
         const uint4 u = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 4) * 4);
         v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
-    template <int R>
-    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *, int, int c, float (&acc)[R]) const
+    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
     {
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 hv = *reinterpret_cast<const float4 *>(h + q * hs + c * 4);
-            acc[q] = fmaf(v.x, hv.x, fmaf(v.y, hv.y, fmaf(v.z, hv.z, fmaf(v.w, hv.w, acc[q]))));
-        }
+        const float4 hv = *reinterpret_cast<const float4 *>(h + c * 4);
+        acc = fmaf(v.x, hv.x, fmaf(v.y, hv.y, fmaf(v.z, hv.z, fmaf(v.w, hv.w, acc))));
     }
 };
 template <>
@@ -634,160 +827,136 @@ struct DnPiece<Q2> {
         const int nb = M.cols >> 5;
         const int b = c >> 2;
         codes = ld_nt2(M.base + static_cast<size_t>(j) * (M.cols >> 2) + c * 2);
-        sm = ld_nt4(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) +
-                                                 (static_cast<size_t>(j) * nb + b) * 4);
+        sm = ld_nt4(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) + (static_cast<size_t>(j) * nb + b) * 4);
     }
-    // h8: sums of each 8 consecutive h values (for the min term)
-    template <int R>
-    __device__ __forceinline__ void fma_into(const float *h, int hs, const float *h8, int h8s, int c,
-                                             float (&acc)[R]) const
+    // sum_i (code_i * s + m) h_i = s * sum_i code_i h_i + m * sum_i h_i
+    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
     {
         const float s = f16_to_f32(sm & 0xffffu);
         const float m = f16_to_f32(sm >> 16);
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 h0 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8);
-            const float4 h1 = *reinterpret_cast<const float4 *>(h + q * hs + c * 8 + 4);
-            float cx = 0.0f;
-            cx = fmaf(static_cast<float>(codes & 3u), h0.x, cx);
-            cx = fmaf(static_cast<float>((codes >> 2) & 3u), h0.y, cx);
-            cx = fmaf(static_cast<float>((codes >> 4) & 3u), h0.z, cx);
-            cx = fmaf(static_cast<float>((codes >> 6) & 3u), h0.w, cx);
-            cx = fmaf(static_cast<float>((codes >> 8) & 3u), h1.x, cx);
-            cx = fmaf(static_cast<float>((codes >> 10) & 3u), h1.y, cx);
-            cx = fmaf(static_cast<float>((codes >> 12) & 3u), h1.z, cx);
-            cx = fmaf(static_cast<float>((codes >> 14) & 3u), h1.w, cx);
-            acc[q] = fmaf(s, cx, fmaf(m, h8[q * h8s + c], acc[q]));
-        }
+        const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
+        const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
+        float cx = 0.0f;
+        cx = fmaf(static_cast<float>(codes & 3u), h0.x, cx);
+        cx = fmaf(static_cast<float>((codes >> 2) & 3u), h0.y, cx);
+        cx = fmaf(static_cast<float>((codes >> 4) & 3u), h0.z, cx);
+        cx = fmaf(static_cast<float>((codes >> 6) & 3u), h0.w, cx);
+        cx = fmaf(static_cast<float>((codes >> 8) & 3u), h1.x, cx);
+        cx = fmaf(static_cast<float>((codes >> 10) & 3u), h1.y, cx);
+        cx = fmaf(static_cast<float>((codes >> 12) & 3u), h1.z, cx);
+        cx = fmaf(static_cast<float>((codes >> 14) & 3u), h1.w, cx);
+        const float hs = ((h0.x + h0.y) + (h0.z + h0.w)) + ((h1.x + h1.y) + (h1.z + h1.w));
+        acc = fmaf(s, cx, fmaf(m, hs, acc));
     }
 };
 
-// Lane partials of row j of up to kDnBatch matrices of one format with their
-// staged h'; every load is issued before the math.
-template <int R, typename W>
-__device__ __forceinline__ void down_rows(const MatRef *mats, int ns, int j, const float *hl, const float *h8,
-                                          int Imax, int lane, float (&acc)[R])
-{
-    const int npc = mats[0].cols / DnPiece<W>::kElems;
-    for (int base = 0; base < npc; base += kWave) {
-        const int c = base + lane;
-        DnPiece<W> pc[kDnBatch];
-#pragma unroll
-        for (int s = 0; s < kDnBatch; ++s)
-            if (s < ns && c < npc)
-                pc[s].load(mats[s], j, c);
-#pragma unroll
-        for (int s = 0; s < kDnBatch; ++s)
-            if (s < ns && c < npc)
-                pc[s].template fma_into<R>(hl + s * R * Imax, Imax, h8 + s * R * (Imax >> 3), Imax >> 3, c, acc);
-    }
-}
+template <typename W>
+struct DnBatch {
+    static constexpr int value = 12;   // 16-byte pieces in flight per lane
+};
+template <>
+struct DnBatch<Q2> {
+    static constexpr int value = 32;   // 2 + 4 bytes per piece
+};
 
-// h' of slots [s0, s0 + gs) into LDS; slot 0 (the shared expert) is scaled by
-// the gate of each row here. For 2-bit experts also the 8-element sums.
-template <int R, typename ET>
-__device__ __forceinline__ void stage_h(const DownArgs &p, int s0, int gs, float *hl, float *h8)
-{
-    const int n4 = gs * R * p.Imax / 4;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-        float4 v = reinterpret_cast<const float4 *>(p.hbuf + static_cast<size_t>(s0) * R * p.Imax)[i];
-        if (s0 == 0 && i < R * p.Imax / 4) {
-            const float g = p.slots->w[0][(i * 4) / p.Imax];
-            v.x *= g;
-            v.y *= g;
-            v.z *= g;
-            v.w *= g;
-        }
-        reinterpret_cast<float4 *>(hl)[i] = v;
-    }
-    __syncthreads();
-    if (ET::kChunk == 32) {
-        for (int i = threadIdx.x; i < gs * R * (p.Imax >> 3); i += blockDim.x) {
-            const float4 a = reinterpret_cast<const float4 *>(hl)[2 * i];
-            const float4 b = reinterpret_cast<const float4 *>(hl)[2 * i + 1];
-            h8[i] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-        }
-        __syncthreads();
-    }
-}
-
-template <int R, typename ET, typename ST>
+// Down projection and combine, one output row j per wave:
+//   y[q][j] = sum over routed slots s used by row q of D_s[j] . h'(s, q)
+//             + gate_q * D_shared[j] . h'(0, q)
+// (h' carries the route weight). Only the (slot, row) pairs that carry
+// weight exist, so a few-row call costs one row's arithmetic per slot. The
+// shared piece and the first batch of routed pieces are requested before
+// h' is staged in LDS (STAGED; otherwise h' is read from L2).
+template <int R, typename ET, typename ST, bool STAGED>
 __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    const int G = p.group;
-    float *hl = reinterpret_cast<float *>(lds_raw);        // [G][R][Imax]
-    float *h8 = hl + G * R * p.Imax;                         // [G][R][Imax/8]
+    constexpr int B = DnBatch<ET>::value;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int j = blockIdx.x * kDnWaves + tid / kWave;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int j = blockIdx.x * kDnWaves + wave;
     const bool live = j < p.H;
     const int nslots = p.slots->nslots;
+    const int npr = p.I / DnPiece<ET>::kElems, nps = p.Is / DnPiece<ST>::kElems;
+    const MatRef SD{p.sd, p.H, p.Is};
 
-    float acc[R];
+    DnPiece<ST> ps;
+    DnPiece<ET> pc[B];
+    if (live && lane < nps)
+        ps.load(SD, j, lane);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        if (live && 1 + u < nslots && lane < npr) {
+            const int e = p.slots->expert[1 + u];
+            pc[u].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
+        }
+    }
+    // the slot table's pair layout and gates into LDS, beside the h' staging
+    __shared__ uint32_t rmask[kMaxRows * kMaxK + 1];
+    __shared__ int pstart[kMaxRows * kMaxK + 1];
+    __shared__ float gate[kMaxRows];
+    __shared__ int expert[kMaxRows * kMaxK + 1];
+    if (tid < nslots) {
+        expert[tid] = p.slots->expert[tid];
+        rmask[tid] = p.slots->rmask[tid];
+        pstart[tid] = p.slots->pstart[tid];
+    }
+    if (tid < R)
+        gate[tid] = p.slots->w[0][tid];
+    const float *hl = p.hbuf;
+    if (STAGED) {
+        float *dst = reinterpret_cast<float *>(lds_raw);
+        const int n4 = p.max_pairs * p.Imax / 4;
+        for (int i = tid; i < n4; i += blockDim.x)
+            reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(p.hbuf)[i];
+        hl = dst;
+    }
+    __syncthreads();
+    if (!live)
+        return;
+
+    float acc[R], sh[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)
-        acc[q] = 0.0f;
-
-    const int npr = p.I / DnPiece<ET>::kElems, nps = p.Is / DnPiece<ST>::kElems;
-    if (nslots <= G && nslots - 1 <= kDnBatch && npr <= kWave && nps <= kWave) {
-        // Every down-row piece of this wave is requested before h' is staged,
-        // so the weight stream overlaps the h' broadcast.
-        DnPiece<ST> ps;
-        DnPiece<ET> pr[kDnBatch];
-        if (live && lane < nps)
-            ps.load(MatRef{p.sd, p.H, p.Is}, j, lane);
+        acc[q] = sh[q] = 0.0f;
+    // shared expert: pairs 0..R-1
+    for (int base = 0; base < nps; base += kWave) {
+        const int c = base + lane;
+        if (base > 0 && c < nps)
+            ps.load(SD, j, c);
+        if (c < nps) {
 #pragma unroll
-        for (int s = 0; s < kDnBatch; ++s) {
-            if (live && s + 1 < nslots && lane < npr) {
-                const int e = p.slots->expert[s + 1];
-                pr[s].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
-            }
+            for (int q = 0; q < R; ++q)
+                ps.fma1(hl + q * p.Imax, c, sh[q]);
         }
-        stage_h<R, ET>(p, 0, nslots, hl, h8);
-        if (live) {
-            if (lane < nps)
-                ps.template fma_into<R>(hl, p.Imax, h8, p.Imax >> 3, lane, acc);
+    }
+    // routed slots in batches of B
+    for (int s0 = 1; s0 < nslots; s0 += B) {
+        for (int base = 0; base < npr; base += kWave) {
+            const int c = base + lane;
+            if (s0 > 1 || base > 0) {
 #pragma unroll
-            for (int s = 0; s < kDnBatch; ++s)
-                if (s + 1 < nslots && lane < npr)
-                    pr[s].template fma_into<R>(hl + (s + 1) * R * p.Imax, p.Imax,
-                                               h8 + (s + 1) * R * (p.Imax >> 3), p.Imax >> 3, lane, acc);
-        }
-    } else {
-        for (int s0 = 0; s0 < nslots; s0 += G) {
-            const int gs = min(G, nslots - s0);
-            if (s0 > 0)
-                __syncthreads();
-            stage_h<R, ET>(p, s0, gs, hl, h8);
-            if (!live)
-                continue;
-            int g = 0;
-            if (s0 == 0) {   // slot 0: the shared expert
-                const MatRef M{p.sd, p.H, p.Is};
-                down_rows<R, ST>(&M, 1, j, hl, h8, p.Imax, lane, acc);
-                g = 1;
+                for (int u = 0; u < B; ++u)
+                    if (s0 + u < nslots && c < npr)
+                        pc[u].load(MatRef{p.ed + expert[s0 + u] * p.estride, p.H, p.I}, j, c);
             }
-            for (; g < gs; g += kDnBatch) {
-                MatRef mats[kDnBatch];
-                const int nb = min(kDnBatch, gs - g);
 #pragma unroll
-                for (int s = 0; s < kDnBatch; ++s) {
-                    const int e = s < nb ? p.slots->expert[s0 + g + s] : 0;
-                    mats[s] = MatRef{p.ed + e * p.estride, p.H, p.I};
+            for (int u = 0; u < B; ++u) {
+                if (s0 + u < nslots && c < npr) {
+                    const uint32_t m = rmask[s0 + u];
+                    int pp = pstart[s0 + u];
+#pragma unroll
+                    for (int q = 0; q < R; ++q)
+                        if ((m >> q) & 1u)
+                            pc[u].fma1(hl + static_cast<size_t>(pp++) * p.Imax, c, acc[q]);
                 }
-                down_rows<R, ET>(mats, nb, j, hl + g * R * p.Imax, h8 + g * R * (p.Imax >> 3), p.Imax, lane,
-                                 acc);
             }
         }
     }
-    if (live) {
 #pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float v = wave_sum(acc[q]);
-            if (lane == 0)
-                p.y[q * p.H + j] = v;
-        }
+    for (int q = 0; q < R; ++q) {
+        const float v = wave_sum(acc[q]) + gate[q] * wave_sum(sh[q]);
+        if (lane == 0)
+            p.y[q * p.H + j] = v;
     }
 }
 
@@ -829,6 +998,39 @@ static GateUpArgs gateup_args(const moe_layer_desc *d, const float *x, const Dec
     g.ch_per_wg = kGuWaves;
     g.wg_per_slot = (g.I + g.ch_per_wg - 1) / g.ch_per_wg;
     return g;
+}
+
+// Workgroups of kernel `fn` (block threads, dynamic LDS bytes) that the
+// current device holds at once: occupancy per CU times the CU count, cached
+// per (kernel, LDS size, device). 0 if the runtime cannot tell.
+static int resident_blocks(const void *fn, int block, size_t lds)
+{
+    struct Entry {
+        const void *fn;
+        size_t lds;
+        int dev, n;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (e.fn == fn && e.lds == lds && e.dev == dev)
+                return e.n;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int n = per_cu * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(Entry{fn, lds, dev, n});
+    return n;
 }
 
 // k_logits: the router logits and the shared-gate logit of R rows.
@@ -906,8 +1108,18 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
         const GateUpArgs g = gateup_args<ET>(d, x, w);
         const RouteArgs ra = route_args(d, io, w, true);
         const int n_sh = (Is + g.ch_per_wg - 1) / g.ch_per_wg;
-        const dim3 grid(n_sh + R * K * g.wg_per_slot), block(kGuWaves * kWave);
         const size_t lds = gateup_lds_bytes(R, H, d->n_experts);
+        const void *fn = R == 1   ? reinterpret_cast<const void *>(&k_gateup<1, ET, ST>)
+                         : R == 2 ? reinterpret_cast<const void *>(&k_gateup<2, ET, ST>)
+                         : R == 3 ? reinterpret_cast<const void *>(&k_gateup<3, ET, ST>)
+                                  : reinterpret_cast<const void *>(&k_gateup<4, ET, ST>);
+        // routed workgroups: one per work item up to what stays resident
+        // beside the shared ones (each routes once, then strides over items)
+        int n_rt = R * K * g.wg_per_slot;
+        const int resident = resident_blocks(fn, kGuWaves * kWave, lds) - n_sh;
+        if (resident > 0 && n_rt > resident)
+            n_rt = resident;
+        const dim3 grid(n_sh + n_rt), block(kGuWaves * kWave);
         switch (R) {
         case 1: hipLaunchKernelGGL((k_gateup<1, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
         case 2: hipLaunchKernelGGL((k_gateup<2, ET, ST>), grid, block, lds, s, g, ra, n_sh); break;
@@ -928,17 +1140,23 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     dn.sd = static_cast<const uint8_t *>(d->sh_down);
     dn.slots = w.slots;
     dn.hbuf = w.hbuf;
-    const size_t per_slot = sizeof(float) * R * Imax + sizeof(float) * R * (Imax / 8);
-    int group = static_cast<int>((48u * 1024u) / per_slot);
-    group = group < 1 ? 1 : (group > R * K + 1 ? R * K + 1 : group);
-    dn.group = group;
+    dn.max_pairs = max_pairs(R, K);
     const dim3 dgrid((H + kDnWaves - 1) / kDnWaves), dblock(kDnWaves * kWave);
-    const size_t dlds = per_slot * group;
-    switch (R) {
-    case 1: hipLaunchKernelGGL((k_down<1, ET, ST>), dgrid, dblock, dlds, s, dn); break;
-    case 2: hipLaunchKernelGGL((k_down<2, ET, ST>), dgrid, dblock, dlds, s, dn); break;
-    case 3: hipLaunchKernelGGL((k_down<3, ET, ST>), dgrid, dblock, dlds, s, dn); break;
-    default: hipLaunchKernelGGL((k_down<4, ET, ST>), dgrid, dblock, dlds, s, dn); break;
+    const size_t stage = static_cast<size_t>(dn.max_pairs) * Imax * sizeof(float);
+    if (stage <= kDnStageLds) {
+        switch (R) {
+        case 1: hipLaunchKernelGGL((k_down<1, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
+        case 2: hipLaunchKernelGGL((k_down<2, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
+        case 3: hipLaunchKernelGGL((k_down<3, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
+        default: hipLaunchKernelGGL((k_down<4, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
+        }
+    } else {
+        switch (R) {
+        case 1: hipLaunchKernelGGL((k_down<1, ET, ST, false>), dgrid, dblock, 0, s, dn); break;
+        case 2: hipLaunchKernelGGL((k_down<2, ET, ST, false>), dgrid, dblock, 0, s, dn); break;
+        case 3: hipLaunchKernelGGL((k_down<3, ET, ST, false>), dgrid, dblock, 0, s, dn); break;
+        default: hipLaunchKernelGGL((k_down<4, ET, ST, false>), dgrid, dblock, 0, s, dn); break;
+        }
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -240,18 +240,29 @@ __device__ __forceinline__ int next_pow2(int v)
 //   logits      : [R][E] double
 //   zlogit      : [R] double
 //   slot table  : nslots, slot_expert[S], slot_w[S][R] (S = R*K + 1)
-//   hbuf        : [S][R][Imax] fp32   (weighted SwiGLU activations)
+//   hbuf        : [S][R][Imax] fp32   (weighted SwiGLU activations, one row
+//                 per (slot, row) pair; at most R*(K+1) rows are used)
 struct Control {
     unsigned int route_done;   // last-block ticket of the route kernel
     unsigned int pad[63];
 };
 
+// Slots of a decode / few-row call: slot 0 is the shared expert, slots
+// 1.. the distinct routed experts. The (slot, row) pairs of the rows that use
+// a slot are numbered slot-major: pair pstart[s] + (rank of row q among the
+// rows of rmask[s]); the gate/up pass writes h' of pair i to row i of hbuf.
 struct SlotTable {
     int nslots;
     int pad[3];
     int expert[kMaxRows * kMaxK + 1];          // slot 0 = shared expert (-1)
     float w[kMaxRows * kMaxK + 1][kMaxRows];   // per-row weight (0: row does not use the slot)
+    uint32_t rmask[kMaxRows * kMaxK + 1];      // rows that use the slot
+    int pstart[kMaxRows * kMaxK + 2];          // first pair of each slot; [nslots] = pair count
 };
+
+// Bound on the pairs of a call of R rows: each row uses K routed slots and
+// the shared one.
+__host__ __device__ inline int max_pairs(int R, int K) { return R * (K + 1); }
 
 struct DecodeWs {
     Control *ctl;

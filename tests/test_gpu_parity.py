@@ -171,6 +171,35 @@ def test_bf16_and_q2_small_shapes():
         assert_parity(run_calls(Gq, x, rows), ref, f"q2 rows={rows}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "q2"])
+def test_wide_rows_and_large_pair_sets(fmt):
+    """Rows wider than one chunk set per wave (H = 2112: the streamed gate/up
+    path) and, at four rows with K = 16, more (slot, row) pairs than the
+    down pass stages in LDS (h' read from L2)."""
+    _say(f"case: wide rows {fmt} H=2112 E=16 K=16 I=544 Is=96")
+    rng = np.random.default_rng(77)
+    a = _random_arrays(rng, 2112, 16, 16, 544, 96, rstd=0.05, estd=0.03)
+    b = dict(a)
+    for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+        b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    x = rng.standard_normal((4, 2112)).astype(np.float32)
+    if fmt == "bf16":
+        L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+        G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    else:
+        import oracle
+        ef = {k: [mi.bf16_bits_to_f32(m) for m in b[k]] for k in ("exp_gate", "exp_up", "exp_down")}
+        q = dict(b)
+        for k in ef:
+            q[k] = [oracle.q2_quantize(m) for m in ef[k]]
+        L = oracle_layer_from_arrays(q, router_t="bf16", expert_t="q2", shared_t="bf16")
+        G = gpu_layer_from_arrays(dict(b, **{k: np.stack(v) for k, v in ef.items()}),
+                                  router_t="bf16", expert_t="q2", shared_t="bf16")
+    ref = _oracle_ref(L, x)
+    for rows in (1, 4):
+        assert_parity(run_calls(G, x, rows), ref, f"wide {fmt} rows={rows}")
+
+
 def test_given_routing_entry():
     """moe_forward with ids_in/wts_in/gate_in uses the routing as given."""
     _say("case: caller-supplied routing")
