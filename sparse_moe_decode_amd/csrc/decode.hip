@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <cstddef>
 #include <climits>
 #include <mutex>
 #include <vector>
@@ -483,7 +484,7 @@ __device__ __forceinline__ void routed_channel(const GateUpArgs &p, const RowChu
     const int nck = p.H / W::kChunk;
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-        const int pr = pair_of(t, slot, q);
+        const int pr = R == 1 ? slot : pair_of(t, slot, q);   // one row: every slot is the row's, pair = slot
         if (pr >= 0) {
             float a[1] = {0.0f}, c[1] = {0.0f};
             dot_rows<1>(W{}, r, 0, lane, nck, xs + q * p.H, p.H, xsum + q * (p.H >> 5), a, c);
@@ -883,11 +884,20 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     DnPiece<ET> pc[B];
     if (live && lane < nps)
         ps.load(SD, j, lane);
+    {
+        // the first batch's expert ids in one go (16-byte reads of the table)
+        constexpr int NV = (B + 4) / 4;
+        int4 ev[NV];
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-        if (live && 1 + u < nslots && lane < npr) {
-            const int e = p.slots->expert[1 + u];
-            pc[u].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
+        for (int k = 0; k < NV; ++k)
+            ev[k] = reinterpret_cast<const int4 *>(p.slots->expert)[k];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int4 &v = ev[(1 + u) >> 2];
+            const int r = (1 + u) & 3;
+            const int e = r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
+            if (live && 1 + u < nslots && lane < npr)
+                pc[u].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
         }
     }
     // the slot table's pair layout and gates into LDS, beside the h' staging
@@ -895,11 +905,13 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     __shared__ int pstart[kMaxRows * kMaxK + 1];
     __shared__ float gate[kMaxRows];
     __shared__ int expert[kMaxRows * kMaxK + 1];
-    if (tid < nslots) {
+    if (R > 1 && tid < nslots) {
         expert[tid] = p.slots->expert[tid];
         rmask[tid] = p.slots->rmask[tid];
         pstart[tid] = p.slots->pstart[tid];
     }
+    if (R == 1 && tid < nslots)
+        expert[tid] = p.slots->expert[tid];
     if (tid < R)
         gate[tid] = p.slots->w[0][tid];
     const float *hl = p.hbuf;
@@ -942,12 +954,16 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 #pragma unroll
             for (int u = 0; u < B; ++u) {
                 if (s0 + u < nslots && c < npr) {
-                    const uint32_t m = rmask[s0 + u];
-                    int pp = pstart[s0 + u];
+                    if constexpr (R == 1) {
+                        pc[u].fma1(hl + static_cast<size_t>(s0 + u) * p.Imax, c, acc[0]);   // pair = slot
+                    } else {
+                        const uint32_t m = rmask[s0 + u];
+                        int pp = pstart[s0 + u];
 #pragma unroll
-                    for (int q = 0; q < R; ++q)
-                        if ((m >> q) & 1u)
-                            pc[u].fma1(hl + static_cast<size_t>(pp++) * p.Imax, c, acc[q]);
+                        for (int q = 0; q < R; ++q)
+                            if ((m >> q) & 1u)
+                                pc[u].fma1(hl + static_cast<size_t>(pp++) * p.Imax, c, acc[q]);
+                    }
                 }
             }
         }
@@ -965,6 +981,8 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 static inline int imax_of(const moe_layer_desc *d) { return d->inter > d->shared_inter ? d->inter : d->shared_inter; }
 
 static_assert(sizeof(RouteLds) <= kDecodeStaticLds, "routing state exceeds its LDS bound");
+static_assert(offsetof(SlotTable, expert) % 16 == 0 && sizeof(SlotTable) % 16 == 0,
+              "the down pass reads expert ids 16 bytes at a time");
 
 size_t gateup_lds_bytes(int R, int H, int E)
 {
