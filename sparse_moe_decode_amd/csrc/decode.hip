@@ -180,8 +180,7 @@ __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, Rout
             }
         __syncthreads();
         if (wave < R) {
-            wave_select(lg + wave * lgs, a.E, a.K, wave, rl, lane);
-            wave_weights(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane);
+            wave_route(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane);
         }
     }
     __syncthreads();

@@ -176,8 +176,7 @@ __global__ void __launch_bounds__(256) k_select_rows(const double *logits, const
     if (t >= T)
         return;
     const double *lg = logits + static_cast<size_t>(t) * E;
-    wave_select(lg, E, K, wave, rl, lane);
-    wave_weights(lg, E, K, renorm, z[t], wave, rl, lane);
+    wave_route(lg, E, K, renorm, z[t], wave, rl, lane);
     __builtin_amdgcn_wave_barrier();
     if (lane < K) {
         const int e = rl.sel_e[wave][lane];

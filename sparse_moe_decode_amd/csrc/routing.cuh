@@ -16,13 +16,10 @@ struct RouteLds {
     int sel_e[kMaxRows][kMaxK];
     double sel_l[kMaxRows][kMaxK];
     float sel_w[kMaxRows][kMaxK];
-    double ex[kMaxRows][kMaxK];
     alignas(16) int cand[kMaxRows][kWave];
     alignas(16) double cand_v[kMaxRows][kWave];
     alignas(16) uint64_t cand_p[kMaxRows][kWave];
     alignas(16) uint32_t pmax[kMaxRows][kWave / 2];
-    uint32_t srt_k[kMaxRows][kMaxK + 1];
-    double srt_v[kMaxRows][kMaxK + 1];
     float g[kMaxRows];
     SlotTable slots;
 };
@@ -68,22 +65,61 @@ __device__ __forceinline__ void rank_exact(int C, int K, int q, RouteLds &rl, in
     __builtin_amdgcn_wave_barrier();
 }
 
-// Top-K of one row of E logits (double, in LDS) by one wave, under the order
-// "logit desc, then id asc". Writes rl.sel_e[q][0..K) and rl.sel_l[q][0..K)
-// in that order. Expert e = lane + 64*m is element m of lane `lane`; PL is
-// the number of elements per lane (E <= 64*PL).
+// Route weights of row q by the wave that selected it, in selection order:
+// w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the selection
+// (renormalized) or over all E logits; the gate sigmoid(z_q) = 1/(1+exp(-z_q)).
+// The differences l_k - l_0 (<= 0) are taken in fp64 and rounded once; the
+// exponentials, sums and quotients are fp32 (the outputs are fp32). Lane k < K
+// evaluates exp(l_k - l_0), lane K evaluates exp(-z), in one pass; sums are
+// wave reductions in a fixed order.
+__device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
+                                             int lane)
+{
+    __builtin_amdgcn_wave_barrier();
+    const double l0 = rl.sel_l[q][0];
+    float arg = 0.0f;
+    if (lane < K)
+        arg = static_cast<float>(rl.sel_l[q][lane] - l0);
+    else if (lane == K)
+        arg = static_cast<float>(-z);
+    const float v = expf(arg);
+    float denom;
+    if (renorm) {
+        denom = wave_sum(lane < K ? v : 0.0f);
+    } else {
+        float s = 0.0f;
+        for (int e = lane; e < E; e += kWave)
+            s += expf(static_cast<float>(lg[e] - l0));
+        denom = wave_sum(s);
+    }
+    const float r = (lane < K ? v : 1.0f) / (lane < K ? denom : 1.0f + v);
+    if (lane < K)
+        rl.sel_w[q][lane] = r;
+    if (lane == K)
+        rl.g[q] = r;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Routing of one row of E logits (double, in LDS) by one wave: the top K
+// under the order "logit desc, then id asc" into rl.sel_e[q][0..K) and
+// rl.sel_l[q][0..K), the route weights into rl.sel_w[q] and the gate into
+// rl.g[q] (weights as in wave_weights). Expert e = lane + 64*m is element m of
+// lane `lane`; PL is the number of elements per lane (E <= 64*PL).
 //  1. Keys: order-preserving integers of the fp32 roundings (rounding to
 //     fp32 is monotone). M = the K-th largest of the 32 maxima of lane pairs;
 //     the K pairs at or above it hold K distinct logits whose keys are >= M,
 //     so the K-th largest logit has key >= M.
-//  2. Candidates: logits with key >= M; every logit of the true top K is one.
-//     They are compacted into LDS.
-//  3. Ranking by (key desc, id asc) packed in 64 bits. This is the exact
-//     order unless two of the first K+1 share a key but not a value; that is
-//     checked, and then the candidates are ranked in fp64 (rank_exact).
-// More than 64 candidates (massive ties) take a slower exact path.
+//  2. Candidates: logits with key >= M (every logit of the true top K is
+//     one), compacted into LDS by a ballot prefix of the per-lane counts.
+//  3. Ranking by (key desc, id asc) packed in 64 bits. Distinct keys order
+//     their values exactly; if any of the first K+1 shares its key with
+//     another candidate, the candidates are ranked in fp64 instead
+//     (rank_exact). The weights are then computed by the ranked lanes
+//     themselves. More than 64 candidates (massive ties) take a slower exact
+//     path.
 template <int PL>
-__device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
+__device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, int renorm, double z, int q,
+                                              RouteLds &rl, int lane)
 {
     uint32_t key[PL];
     uint32_t mk = 0;   // 0 is below every key of a non-NaN value
@@ -147,110 +183,93 @@ __device__ __forceinline__ void wave_select_pl(const double *lg, int E, int K, i
         if (c && pos < kWave) {
             const int e = lane + m * kWave;
             rl.cand[q][pos] = e;
-            rl.cand_v[q][pos] = lg[e];
             rl.cand_p[q][pos] = (static_cast<uint64_t>(key[m]) << 32) | static_cast<uint32_t>(~e);
         }
         pos += c;
     }
     if (C <= kWave) {
-        // 3. rank by packed key (padding 0 is below every candidate)
+        // 3. rank by packed key (padding 0 is below every candidate and
+        // shares no key with one)
         const int C4 = (C + 3) & ~3;
         if (lane >= C && lane < C4)
             rl.cand_p[q][lane] = 0;
         __builtin_amdgcn_wave_barrier();
         const uint64_t p = rl.cand_p[q][lane];
-        int rank = 0;
+        const uint32_t pk = static_cast<uint32_t>(p >> 32);
+        int rank = 0, tie = 0;
         for (int j = 0; j < C; j += 4) {
             const ulonglong2 a = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]);
             const ulonglong2 b = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]);
             rank += (a.x > p) + (a.y > p) + (b.x > p) + (b.y > p);
+            tie += (static_cast<uint32_t>(a.x >> 32) == pk) + (static_cast<uint32_t>(a.y >> 32) == pk) +
+                   (static_cast<uint32_t>(b.x >> 32) == pk) + (static_cast<uint32_t>(b.y >> 32) == pk);
         }
         const bool live = lane < C;
-        const int e = static_cast<int>(~static_cast<uint32_t>(p));
-        const double val = rl.cand_v[q][lane];
-        if (live && rank < K) {
-            rl.sel_e[q][rank] = e;
-            rl.sel_l[q][rank] = val;
+        if (__ballot(live && rank <= K && tie > 1) == 0) {
+            const int e = static_cast<int>(~static_cast<uint32_t>(p));
+            const double val = live ? lg[e] : 0.0;
+            // l_0: the value of the candidate ranked first
+            const int r0 = __builtin_ctzll(__ballot(live && rank == 0));
+            const long long vb = __double_as_longlong(val);
+            const int lo = __builtin_amdgcn_readlane(static_cast<int>(vb & 0xffffffff), r0);
+            const int hi = __builtin_amdgcn_readlane(static_cast<int>(vb >> 32), r0);
+            const double l0 = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+            const bool sel = live && rank < K;
+            const float ex = sel ? expf(static_cast<float>(val - l0)) : 0.0f;
+            float denom;
+            if (renorm) {
+                denom = wave_sum(ex);
+            } else {
+                float sum = 0.0f;
+                for (int e2 = lane; e2 < E; e2 += kWave)
+                    sum += expf(static_cast<float>(lg[e2] - l0));
+                denom = wave_sum(sum);
+            }
+            if (sel) {
+                rl.sel_e[q][rank] = e;
+                rl.sel_l[q][rank] = val;
+                rl.sel_w[q][rank] = ex / denom;
+            }
+            if (lane == 0)
+                rl.g[q] = 1.0f / (1.0f + expf(static_cast<float>(-z)));
+            __builtin_amdgcn_wave_barrier();
+            return;
         }
-        if (live && rank <= K) {
-            rl.srt_k[q][rank] = static_cast<uint32_t>(p >> 32);
-            rl.srt_v[q][rank] = val;
-        }
-        __builtin_amdgcn_wave_barrier();
-        // neighbours r, r+1 (r < K) with one key but two values are the only
-        // way the packed order can differ from the exact one
-        const int nchk = K < C - 1 ? K : C - 1;
-        const bool bad = lane < nchk && rl.srt_k[q][lane] == rl.srt_k[q][lane + 1] &&
-                         rl.srt_v[q][lane] != rl.srt_v[q][lane + 1];
-        if (__ballot(bad) != 0)
-            rank_exact(C, K, q, rl, lane);
-        __builtin_amdgcn_wave_barrier();
-        return;
-    }
-    // many candidates (massive exact ties): rank each against all logits
+        // a key shared near the boundary: exact fp64 ranking
+        if (live)
+            rl.cand_v[q][lane] = lg[rl.cand[q][lane]];
+        rank_exact(C, K, q, rl, lane);
+    } else {
+        // many candidates (massive exact ties): rank each against all logits
 #pragma unroll
-    for (int m = 0; m < PL; ++m) {
-        const int e = lane + m * kWave;
-        if (e >= E || key[m] < t)
-            continue;
-        const double v = lg[e];
-        int rank = 0;
-        for (int e2 = 0; e2 < E; ++e2) {
-            const double o2 = lg[e2];
-            rank += (o2 > v) | ((o2 == v) & (e2 < e));
+        for (int m = 0; m < PL; ++m) {
+            const int e = lane + m * kWave;
+            if (e >= E || key[m] < t)
+                continue;
+            const double val = lg[e];
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) {
+                const double o2 = lg[e2];
+                rank += (o2 > val) | ((o2 == val) & (e2 < e));
+            }
+            if (rank < K) {
+                rl.sel_e[q][rank] = e;
+                rl.sel_l[q][rank] = val;
+            }
         }
-        if (rank < K) {
-            rl.sel_e[q][rank] = e;
-            rl.sel_l[q][rank] = v;
-        }
+        __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_weights(lg, E, K, renorm, z, q, rl, lane);
 }
 
-__device__ __forceinline__ void wave_select(const double *lg, int E, int K, int q, RouteLds &rl, int lane)
+// Routing of row q by one wave (see wave_route_pl).
+__device__ __forceinline__ void wave_route(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
+                                           int lane)
 {
     if (E <= 8 * kWave)
-        wave_select_pl<8>(lg, E, K, q, rl, lane);
+        wave_route_pl<8>(lg, E, K, renorm, z, q, rl, lane);
     else
-        wave_select_pl<kMaxE / kWave>(lg, E, K, q, rl, lane);
-}
-
-// Route weights of row q by the wave that selected it, in selection order:
-// w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the selection
-// (renormalized) or over all E logits; the gate sigmoid(z_q) = 1/(1+exp(-z_q)).
-// Lane k < K evaluates exp(l_k - l_0), lane K evaluates exp(-z), in one pass.
-__device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
-                                             int lane)
-{
-    __builtin_amdgcn_wave_barrier();
-    const double l0 = rl.sel_l[q][0];
-    double arg = 0.0;
-    if (lane < K)
-        arg = rl.sel_l[q][lane] - l0;
-    else if (lane == K)
-        arg = -z;
-    const double v = exp(arg);
-    if (lane < K)
-        rl.ex[q][lane] = v;
-    __builtin_amdgcn_wave_barrier();
-    double denom = 0.0;
-    if (renorm) {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < K)
-                denom += rl.ex[q][j];
-    } else {
-        double s = 0.0;
-        for (int e = lane; e < E; e += kWave)
-            s += exp(lg[e] - l0);
-        denom = lane_group_sum(s, kWave);
-    }
-    const double r = (lane < K ? v : 1.0) / (lane < K ? denom : 1.0 + v);
-    if (lane < K)
-        rl.sel_w[q][lane] = static_cast<float>(r);
-    if (lane == K)
-        rl.g[q] = static_cast<float>(r);
-    __builtin_amdgcn_wave_barrier();
+        wave_route_pl<kMaxE / kWave>(lg, E, K, renorm, z, q, rl, lane);
 }
 
 }  // namespace moe
