@@ -10,20 +10,20 @@
 //                     sigmoid gate
 //   sort (sort.hip)   stable counting sort of the T*K (row, slot) pairs by
 //                     expert, with the inverse permutation
-//   k_tiles           per-expert 64-row tile offsets
-//   k_gemm_gateup     per (expert, 64-row tile, 64-channel block): gathered
-//                     x rows times the gate and up rows of the expert, SwiGLU,
-//                     times the route weight -> h (fp32, sorted row order)
-//   k_gemm_down       per (expert, 64-row tile, 128-column block): h times the
+//   k_tiles           per-expert row-tile offsets (32- or 64-row tiles)
+//   k_ggemm (dual)    per (expert row tile, 128-channel block): gathered x
+//                     rows times the gate and up rows of the expert, SwiGLU,
+//                     times the route weight -> h (bf16 hi/lo, sorted rows)
+//   k_ggemm           per (expert row tile, 256-column block): h times the
 //                     expert's down rows -> one output row per (row, slot)
 //   k_combine         y[t] = sum_k out[(t, k)] + g_t * shared(t)
 // The shared expert uses the same GEMM kernels over all rows.
 //
-// MFMA precision: weights enter as an exact bf16 (bf16 weights) or as a
-// bf16 hi+lo pair of their fp32 value (2-bit weights are first decoded
-// exactly, w = code*scale + min); activations enter as hi+lo pairs. The
-// products hi*hi + hi*lo + lo*hi are accumulated in fp32 by
-// v_mfma_f32_16x16x32_bf16, giving ~2^-16 relative error per term.
+// MFMA precision: activations enter as bf16 hi+lo pairs; 2-bit weights as
+// their exact codes with the block scale applied to each 32-deep partial sum
+// and the block minima as a separate small GEMM; bf16 weights exactly; fp32
+// weights as hi+lo pairs. v_mfma_f32_16x16x32_bf16 accumulates in fp32; the
+// dropped lo*lo terms are below 2^-16 of each product.
 #include <hip/hip_runtime.h>
 
 #include "device_common.cuh"
@@ -56,10 +56,10 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4 &hi, uint4 &lo
 
 // ============================================================== split x
 
-__global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uint4 *xh, uint4 *xl)
+__global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uint4 *xh, uint4 *xl, float *xsum)
 {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n8)
+    if (i >= n8)   // n8 is a multiple of 4: a lane quad is all in or all out
         return;
     const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
     const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
@@ -68,6 +68,12 @@ __global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uin
     split8(v, hi, lo);
     xh[i] = hi;
     xl[i] = lo;
+    // sums of the 32-element blocks (4 lanes of a quad), for 2-bit weights
+    float s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+    if ((i & 3) == 0)
+        xsum[i >> 2] = s;
 }
 
 // =========================================================== fp64 logits
@@ -210,12 +216,12 @@ __global__ void __launch_bounds__(256) k_take_routing(const int32_t *ids_in, con
         gate[i] = gate_in[i];
 }
 
-// Per-expert tile offsets: tile_off[e] = sum_{e' < e} ceil(count[e'] / 64).
-__global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, int32_t *tile_off)
+// Per-expert tile offsets: tile_off[e] = sum_{e' < e} ceil(count[e'] / bm).
+__global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, int bm, int32_t *tile_off)
 {
     __shared__ int s[kMaxE];
     const int t = threadIdx.x;
-    const int v = t < E ? (counts[t] + 63) / 64 : 0;
+    const int v = t < E ? (counts[t] + bm - 1) / bm : 0;
     if (t < E)
         s[t] = v;
     __syncthreads();
@@ -235,85 +241,75 @@ __global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, in
 }
 
 // ================================================================= GEMMs
+//
+// Grouped GEMM  C[r][n] = sum_k A[r][k] B[n][k]  over the rows r of one row
+// tile (rows of one expert group, or of the chunk for the shared expert) and
+// the B rows n of one column block, K = Kd, on v_mfma_f32_16x16x32_bf16.
+//   A: bf16 hi/lo pairs of fp32 values (x - hi - lo below 2^-17 |x|); rows
+//      gathered by token (gate/up) or taken in sorted order (down).
+//   B: 2-bit blocks, bf16 (exact) or fp32 (as hi/lo pairs).
+// 2-bit weights enter as their codes, exact in bf16: each 32-deep step is one
+// block, t = A_hi.c + A_lo.c, acc += s * t with the block's scale s (per B
+// row); the minimum terms sum_b m[n][b] * asum[r][b] (asum: block sums of A,
+// m: block minima) are a second small GEMM with K = blocks (3 passes over
+// hi/lo pairs). bf16 weights: two passes (A_hi.w + A_lo.w); fp32 weights:
+// three (A_hi.w_hi + A_hi.w_lo + A_lo.w_hi).
+// Workgroup: 4 waves, BM rows x kGN B rows. Gate/up (DUAL) puts the gate and
+// up rows of the same channels in the same wave (the LDS B rows alternate
+// gate / up chunks) and ends with SwiGLU times the route weight, written as
+// bf16 hi/lo (the A operand of the down pass) with its 32-channel block sums.
 
-constexpr int kBM = 64;          // rows per tile
-constexpr int kLDK = 40;         // LDS row stride in bf16 (32 + 8 padding)
+constexpr int kGN = 256;         // B rows per workgroup
+constexpr int kLD = 40;          // LDS row stride in bf16 (32 + 8 padding)
 
-// 8 consecutive weights (k0 .. k0+7) of row n of a [rows][cols] matrix as
-// bf16 hi/lo. Rows past the end give zeros.
-__device__ __forceinline__ void b_piece(Q2, const uint8_t *base, int rows, int cols, int n, int k0, uint4 &hi,
-                                        uint4 &lo)
-{
-    if (n >= rows) {
-        hi = lo = make_uint4(0, 0, 0, 0);
-        return;
-    }
-    const int nb = cols >> 5, b = k0 >> 5, part = (k0 & 31) >> 3;
-    const uint32_t codes =
-        *reinterpret_cast<const uint16_t *>(base + static_cast<size_t>(n) * (cols >> 2) + b * 8 + part * 2);
-    const uint32_t sm = *reinterpret_cast<const uint32_t *>(base + static_cast<size_t>(rows) * (cols >> 2) +
-                                                            (static_cast<size_t>(n) * nb + b) * 4);
-    const float s = f16_to_f32(sm & 0xffffu), m = f16_to_f32(sm >> 16);
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        v[j] = __fmaf_rn(static_cast<float>((codes >> (2 * j)) & 3u), s, m);
-    split8(v, hi, lo);
-}
-__device__ __forceinline__ void b_piece(BF16, const uint8_t *base, int rows, int cols, int n, int k0, uint4 &hi,
-                                        uint4 &lo)
-{
-    lo = make_uint4(0, 0, 0, 0);
-    hi = n < rows ? *reinterpret_cast<const uint4 *>(base + (static_cast<size_t>(n) * cols + k0) * 2) : lo;
-}
-__device__ __forceinline__ void b_piece(F32, const uint8_t *base, int rows, int cols, int n, int k0, uint4 &hi,
-                                        uint4 &lo)
-{
-    if (n >= rows) {
-        hi = lo = make_uint4(0, 0, 0, 0);
-        return;
-    }
-    const float *p = reinterpret_cast<const float *>(base) + static_cast<size_t>(n) * cols + k0;
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    split8(v, hi, lo);
-}
+template <int BM>
+struct GemmShape {
+    static constexpr int WR = BM == 64 ? 2 : 1;   // waves along rows
+    static constexpr int WC = 4 / WR;             // waves along B rows
+    static constexpr int TR = BM / WR;            // rows per wave (32)
+    static constexpr int TC = kGN / WC;           // B rows per wave
+    static constexpr int RT = TR / 16, CT = TC / 16;
+};
 
 struct GemmArgs {
-    // rows: routed (sorted pair rows of expert groups) or shared (all T rows)
-    int routed;
-    int T, K, E;
+    int routed, T, K, E;
     const int32_t *tile_off;   // [E+1] (routed)
     const int32_t *offsets;    // [E+1] (routed)
     const int32_t *perm;       // [T*K] sorted row -> pair index (routed)
     const float *wts;          // [T*K] route weights by pair index (routed)
-    // A operand
-    const uint4 *xh, *xl;      // gate/up: x as bf16 hi/lo [T][H]
-    const float *a32;          // down: h rows (fp32) [rows][Kd]
-    // B operand: matrices [N][Kd]; routed expert e at base + e * stride
-    const uint8_t *b0, *b1;    // gate/up: gate, up; down: down (b1 unused)
+    const uint16_t *ah, *al;   // A rows, bf16 hi/lo [rows][Kd]
+    int a_bytes;               // bytes of each of ah, al
+    int a_lo_off;              // bytes from ah to al (al follows ah)
+    const float *asum;         // 2-bit B: block sums of the A rows [rows][Kd/32]
+    int a_gather;              // A row of a tile row: token of the pair (1) or the row itself (0)
+    const uint8_t *b0, *b1;    // B: gate, up (dual) or one matrix; routed expert e at base + e * bstride
     size_t bstride;
     int N, Kd;
-    float *out;                // gate/up: h [rows][N]; down: [rows][N]
+    uint16_t *hh, *hl;         // dual: h hi/lo [rows][N]
+    float *hsum;               // dual, optional: block sums of h [rows][N/32]
+    float *out;                // single: [rows][N]
 };
 
-// Rows of this workgroup: (first row index, row count), the row -> source
-// row map (token for gate/up A rows, sorted row for h) and route weights.
-struct TileRows {
-    int e, r0, nrows;
-};
-
-__device__ inline bool tile_rows(const GemmArgs &p, TileRows &tr)
+// 8 fp32 -> bf16 hi and lo = bf16(v - hi), packed as the MFMA operand.
+__device__ __forceinline__ void split_frag(const float (&v)[8], bf16x8 &hi, bf16x8 &lo)
 {
-    __shared__ int sh[3];
-    const int tix = blockIdx.y;
+    uint4 h, l;
+    split8(v, h, l);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// The tile of this workgroup (blockIdx.y): expert, first sorted row, rows;
+// the A source row and route weight of each tile row. Every thread calls it.
+template <int BM>
+__device__ __forceinline__ bool gemm_tile(const GemmArgs &p, int *tile, int *tok, float *rw)
+{
     if (threadIdx.x == 0) {
+        const int tix = blockIdx.y;
+        int e = -1, r0 = 0, nr = 0;
         if (p.routed) {
-            int lo = 0, hi = p.E;   // largest e with tile_off[e] <= tix
-            if (tix >= p.tile_off[p.E]) {
-                sh[0] = -1;
-            } else {
+            if (tix < p.tile_off[p.E]) {
+                int lo = 0, hi = p.E;   // largest e with tile_off[e] <= tix
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) >> 1;
                     if (p.tile_off[mid] <= tix)
@@ -321,215 +317,454 @@ __device__ inline bool tile_rows(const GemmArgs &p, TileRows &tr)
                     else
                         hi = mid;
                 }
-                const int mt = tix - p.tile_off[lo];
-                const int r0 = p.offsets[lo] + mt * kBM;
-                sh[0] = lo;
-                sh[1] = r0;
-                sh[2] = min(kBM, p.offsets[lo + 1] - r0);
+                e = lo;
+                r0 = p.offsets[lo] + (tix - p.tile_off[lo]) * BM;
+                nr = min(BM, p.offsets[lo + 1] - r0);
             }
-        } else {
-            const int r0 = tix * kBM;
-            sh[0] = r0 < p.T ? 0 : -1;
-            sh[1] = r0;
-            sh[2] = min(kBM, p.T - r0);
+        } else if (tix * BM < p.T) {
+            e = 0;
+            r0 = tix * BM;
+            nr = min(BM, p.T - r0);
         }
+        tile[0] = e;
+        tile[1] = r0;
+        tile[2] = nr;
     }
     __syncthreads();
-    tr.e = sh[0];
-    tr.r0 = sh[1];
-    tr.nrows = sh[2];
-    return tr.e >= 0 && tr.nrows > 0;
-}
-
-// acc[rt][ct] += A(rows wr*32 + rt*16 ..) x B(cols bcol[ct] ..) over one
-// 32-deep step, with hi/lo passes (B lo skipped for exact bf16 weights).
-template <bool BLO>
-__device__ __forceinline__ void mfma_step(const uint16_t *Ah, const uint16_t *Al, const uint16_t *Bh,
-                                          const uint16_t *Bl, int arow0, const int (&bcol)[4], int lane,
-                                          f32x4 (&acc)[2][4])
-{
-    const int li = lane & 15, kq = lane >> 4;
-    bf16x8 ah[2], al[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = arow0 + rt * 16 + li;
-        ah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Ah + r * kLDK + kq * 8));
-        al[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Al + r * kLDK + kq * 8));
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int c = bcol[ct] + li;
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Bh + c * kLDK + kq * 8));
-        bf16x8 bl;
-        if (BLO)
-            bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Bl + c * kLDK + kq * 8));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt], bh, acc[rt][ct], 0, 0, 0);
-            if (BLO)
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rt], bl, acc[rt][ct], 0, 0, 0);
-            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rt], bh, acc[rt][ct], 0, 0, 0);
-        }
-    }
-}
-
-template <typename W>
-struct HasLo {
-    static constexpr bool value = true;
-};
-template <>
-struct HasLo<BF16> {
-    static constexpr bool value = false;
-};
-
-// Gate/up: tile of 64 rows x 64 channels (both gate and up), 4 waves in 2x2,
-// each wave 32 rows x 32 channels of gate and of up. h = silu(g) * u * w.
-template <typename W>
-__global__ void __launch_bounds__(256) k_gemm_gateup(GemmArgs p)
-{
-    __shared__ __align__(16) uint16_t Ah[kBM * kLDK], Al[kBM * kLDK];
-    __shared__ __align__(16) uint16_t Bh[128 * kLDK], Bl[128 * kLDK];
-    __shared__ int tok[kBM];
-    __shared__ float rw[kBM];
-    TileRows tr;
-    if (!tile_rows(p, tr))
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 64;
-    if (tid < kBM) {
-        int t = -1;
+    const int e = tile[0], r0 = tile[1], nrows = tile[2];
+    if (e < 0 || nrows <= 0)
+        return false;
+    if (threadIdx.x < BM) {
+        const int t = threadIdx.x;
+        int src = -1;
         float w = 0.0f;
-        if (tid < tr.nrows) {
+        if (t < nrows) {
             if (p.routed) {
-                const int pi = p.perm[tr.r0 + tid];
-                t = pi / p.K;
+                const int pi = p.perm[r0 + t];
+                src = p.a_gather ? pi / p.K : r0 + t;
                 w = p.wts[pi];
             } else {
-                t = tr.r0 + tid;
+                src = r0 + t;
                 w = 1.0f;
             }
         }
-        tok[tid] = t;
-        rw[tid] = w;
+        tok[t] = src;
+        rw[t] = w;
     }
     __syncthreads();
-    const uint8_t *G = p.b0 + (p.routed ? tr.e * p.bstride : 0);
-    const uint8_t *U = p.b1 + (p.routed ? tr.e * p.bstride : 0);
-    const int wr = wave >> 1, wc = wave & 1;
-    const int bcol[4] = {wc * 32, wc * 32 + 16, 64 + wc * 32, 64 + wc * 32 + 16};
-    f32x4 acc[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-            acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int lr = tid >> 2, lp = tid & 3;
-    const int Hd = p.Kd;
-    for (int k0 = 0; k0 < Hd; k0 += 32) {
-        // A: 64 gathered x rows, 32 columns, hi and lo
-        {
-            const int t = tok[lr];
-            uint4 h = make_uint4(0, 0, 0, 0), l = h;
-            if (t >= 0) {
-                const size_t idx = (static_cast<size_t>(t) * Hd + k0 + lp * 8) / 8;
-                h = p.xh[idx];
-                l = p.xl[idx];
-            }
-            *reinterpret_cast<uint4 *>(Ah + lr * kLDK + lp * 8) = h;
-            *reinterpret_cast<uint4 *>(Al + lr * kLDK + lp * 8) = l;
-        }
-        // B: 64 gate rows then 64 up rows, 32 columns
-        {
-            uint4 h, l;
-            b_piece(W{}, G, p.N, Hd, n0 + lr, k0 + lp * 8, h, l);
-            *reinterpret_cast<uint4 *>(Bh + lr * kLDK + lp * 8) = h;
-            *reinterpret_cast<uint4 *>(Bl + lr * kLDK + lp * 8) = l;
-            b_piece(W{}, U, p.N, Hd, n0 + lr, k0 + lp * 8, h, l);
-            *reinterpret_cast<uint4 *>(Bh + (64 + lr) * kLDK + lp * 8) = h;
-            *reinterpret_cast<uint4 *>(Bl + (64 + lr) * kLDK + lp * 8) = l;
-        }
-        __syncthreads();
-        mfma_step<HasLo<W>::value>(Ah, Al, Bh, Bl, wr * 32, bcol, lane, acc);
-        __syncthreads();
+    return true;
+}
+
+// B row (channel or output column) and matrix of LDS B row t. DUAL: chunks
+// of kGN / (2 WC) rows alternate gate / up.
+template <bool DUAL, int BM>
+__device__ __forceinline__ int gemm_brow(const GemmArgs &p, int e, int n0, int t, const uint8_t *&mat)
+{
+    const size_t eoff = p.routed ? static_cast<size_t>(e) * p.bstride : 0;
+    if (DUAL) {
+        constexpr int chunk = kGN / (2 * GemmShape<BM>::WC);
+        const int blk = t / chunk;
+        mat = ((blk & 1) ? p.b1 : p.b0) + eoff;
+        return n0 + (blk >> 1) * chunk + t % chunk;
     }
-    // epilogue: lane holds rows 4*(lane/16)+i of each 16x16 tile, column lane%16
+    mat = p.b0 + eoff;
+    return n0 + t;
+}
+
+// lane holds rows 4*(lane/16)+i of each 16x16 tile, column lane%16
+template <bool DUAL, int BM>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
+                                              f32x4 (&acc)[GemmShape<BM>::RT][GemmShape<BM>::CT], int n0, int r0,
+                                              int nrows, const float *rw, int wr, int wc, int lane)
+{
+    using S = GemmShape<BM>;
+    const int li = lane & 15, kq = lane >> 4;
+    if (DUAL) {
+        constexpr int chunk = kGN / (2 * S::WC);
+        const int nb32 = p.N >> 5;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int ch = n0 + wc * 32 + ct * 16 + (lane & 15);
+        for (int rt = 0; rt < S::RT; ++rt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = wr * 32 + rt * 16 + 4 * (lane >> 4) + i;
-                if (r < tr.nrows && ch < p.N) {
-                    const float h = silu_mul(acc[rt][ct][i], acc[rt][ct + 2][i]) * rw[r];
-                    p.out[static_cast<size_t>(tr.r0 + r) * p.N + ch] = h;
+                const int r = wr * S::TR + rt * 16 + 4 * kq + i;
+                float bs = 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < S::CT / 2; ++ct) {
+                    const int ch = n0 + wc * chunk + ct * 16 + li;
+                    const float h = silu_mul(acc[rt][ct][i], acc[rt][ct + S::CT / 2][i]) * (r < nrows ? rw[r] : 0.0f);
+                    if (r < nrows && ch < p.N) {
+                        const uint32_t hb = bf16_rne_bits(h);
+                        const uint32_t lb = bf16_rne_bits(h - __uint_as_float(hb << 16));
+                        const size_t o = static_cast<size_t>(r0 + r) * p.N + ch;
+                        p.hh[o] = static_cast<uint16_t>(hb);
+                        p.hl[o] = static_cast<uint16_t>(lb);
+                    }
+                    // 32-channel block sums: two tiles of 16 channels, summed over the 16 lanes
+                    bs += h;
+                    if (ct & 1) {
+                        const float tot = dpp_row_sum(bs);
+                        const int blk = (n0 + wc * chunk + (ct - 1) * 16) >> 5;
+                        if (p.hsum && li == 0 && r < nrows && blk < nb32)
+                            p.hsum[static_cast<size_t>(r0 + r) * nb32 + blk] = tot;
+                        bs = 0.0f;
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < S::RT; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < S::CT; ++ct) {
+                const int col = n0 + wc * S::TC + ct * 16 + li;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wr * S::TR + rt * 16 + 4 * kq + i;
+                    if (r < nrows && col < p.N)
+                        p.out[static_cast<size_t>(r0 + r) * p.N + col] = acc[rt][ct][i];
                 }
             }
         }
     }
 }
 
-// Down: tile of 64 rows x 128 output columns; 4 waves in 2x2, each wave 32
-// rows x 64 columns. A = h rows (fp32, split to hi/lo as they are staged).
+// Next step's B rows in registers (one B row per thread: kGN = 256 threads).
 template <typename W>
-__global__ void __launch_bounds__(256) k_gemm_down(GemmArgs p)
-{
-    __shared__ __align__(16) uint16_t Ah[kBM * kLDK], Al[kBM * kLDK];
-    __shared__ __align__(16) uint16_t Bh[128 * kLDK], Bl[128 * kLDK];
-    TileRows tr;
-    if (!tile_rows(p, tr))
-        return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 128;
-    const uint8_t *D = p.b0 + (p.routed ? tr.e * p.bstride : 0);
-    const int wr = wave >> 1, wc = wave & 1;
-    const int bcol[4] = {wc * 64, wc * 64 + 16, wc * 64 + 32, wc * 64 + 48};
-    f32x4 acc[2][4];
+struct BStage;
+template <>
+struct BStage<BF16> {
+    uint4 v[4];
+    __device__ __forceinline__ void load(const uint8_t *M, int rows, int cols, int n, int blk)
+    {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+        for (int q = 0; q < 4; ++q)
+            v[q] = n < rows ? ld_nt16(M + (static_cast<size_t>(n) * cols + blk * 32 + q * 8) * 2) : make_uint4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ void store(uint16_t *Bh, uint16_t *, int row) const
+    {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-            acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int lr = tid >> 2, lp = tid & 3;
-    const int Kd = p.Kd;
-    for (int k0 = 0; k0 < Kd; k0 += 32) {
-        {
-            uint4 h = make_uint4(0, 0, 0, 0), l = h;
-            if (lr < tr.nrows) {
-                const float *src = p.a32 + static_cast<size_t>(tr.r0 + lr) * Kd + k0 + lp * 8;
-                const float4 a = *reinterpret_cast<const float4 *>(src);
-                const float4 b = *reinterpret_cast<const float4 *>(src + 4);
-                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                split8(v, h, l);
-            }
-            *reinterpret_cast<uint4 *>(Ah + lr * kLDK + lp * 8) = h;
-            *reinterpret_cast<uint4 *>(Al + lr * kLDK + lp * 8) = l;
-        }
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint4 *>(Bh + row * kLD + q * 8) = v[q];
+    }
+};
+template <>
+struct BStage<F32> {
+    uint4 v[8];
+    __device__ __forceinline__ void load(const uint8_t *M, int rows, int cols, int n, int blk)
+    {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int q = 0; q < 8; ++q)
+            v[q] = n < rows ? ld_nt16(M + (static_cast<size_t>(n) * cols + blk * 32 + q * 4) * 4) : make_uint4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ void store(uint16_t *Bh, uint16_t *Bl, int row) const
+    {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float f[8] = {__uint_as_float(v[2 * q].x), __uint_as_float(v[2 * q].y), __uint_as_float(v[2 * q].z),
+                                __uint_as_float(v[2 * q].w), __uint_as_float(v[2 * q + 1].x),
+                                __uint_as_float(v[2 * q + 1].y), __uint_as_float(v[2 * q + 1].z),
+                                __uint_as_float(v[2 * q + 1].w)};
             uint4 h, l;
-            b_piece(W{}, D, p.N, Kd, n0 + half * 64 + lr, k0 + lp * 8, h, l);
-            *reinterpret_cast<uint4 *>(Bh + (half * 64 + lr) * kLDK + lp * 8) = h;
-            *reinterpret_cast<uint4 *>(Bl + (half * 64 + lr) * kLDK + lp * 8) = l;
+            split8(f, h, l);
+            *reinterpret_cast<uint4 *>(Bh + row * kLD + q * 8) = h;
+            *reinterpret_cast<uint4 *>(Bl + row * kLD + q * 8) = l;
+        }
+    }
+};
+
+// bf16 / fp32 weights: one 32-deep step in LDS, the next one's global loads
+// in registers while the current one is multiplied.
+template <typename W, bool DUAL, int BM>
+__global__ void __launch_bounds__(256) k_ggemm(GemmArgs p)
+{
+    using S = GemmShape<BM>;
+    constexpr bool kBLo = W::kChunk == 4;
+    __shared__ __align__(16) uint16_t Lah[BM * kLD], Lal[BM * kLD], Lbh[kGN * kLD];
+    __shared__ __align__(16) uint16_t Lbl[kBLo ? kGN * kLD : 8];
+    __shared__ int Ltok[BM];
+    __shared__ float Lrw[BM];
+    __shared__ int Ltile[3];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, kq = lane >> 4;
+    const int wr = wave / S::WC, wc = wave % S::WC;
+    if (!gemm_tile<BM>(p, Ltile, Ltok, Lrw))
+        return;
+    const int e = Ltile[0], r0 = Ltile[1], nrows = Ltile[2];
+    const int n0 = blockIdx.x * (DUAL ? kGN / 2 : kGN);
+    const uint8_t *bmat;
+    const int bn = gemm_brow<DUAL, BM>(p, e, n0, tid, bmat);
+    const bool a_loader = tid < BM * 4;
+    const int arow = (tid >> 2) % BM, apart = tid & 3;
+    const int asrc = Ltok[arow];
+
+    f32x4 acc[S::RT][S::CT];
+#pragma unroll
+    for (int rt = 0; rt < S::RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < S::CT; ++ct)
+            acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = p.Kd / 32;
+    uint4 rah = make_uint4(0, 0, 0, 0), ral = rah;
+    BStage<W> rb;
+    auto load_step = [&](int s) {
+        if (a_loader && asrc >= 0) {
+            const size_t idx = (static_cast<size_t>(asrc) * p.Kd + s * 32 + apart * 8) / 8;
+            rah = reinterpret_cast<const uint4 *>(p.ah)[idx];
+            ral = reinterpret_cast<const uint4 *>(p.al)[idx];
+        } else {
+            rah = ral = make_uint4(0, 0, 0, 0);
+        }
+        rb.load(bmat, p.N, p.Kd, bn, s);
+    };
+    load_step(0);
+    for (int s = 0; s < nsteps; ++s) {
+        if (a_loader) {
+            *reinterpret_cast<uint4 *>(Lah + arow * kLD + apart * 8) = rah;
+            *reinterpret_cast<uint4 *>(Lal + arow * kLD + apart * 8) = ral;
+        }
+        rb.store(Lbh, Lbl, tid);
+        __syncthreads();
+        if (s + 1 < nsteps)
+            load_step(s + 1);
+        bf16x8 fah[S::RT], fal[S::RT];
+#pragma unroll
+        for (int rt = 0; rt < S::RT; ++rt) {
+            const int r = wr * S::TR + rt * 16 + li;
+            fah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Lah + r * kLD + kq * 8));
+            fal[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Lal + r * kLD + kq * 8));
+        }
+#pragma unroll
+        for (int ct = 0; ct < S::CT; ++ct) {
+            const int c = wc * S::TC + ct * 16 + li;
+            const bf16x8 fb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Lbh + c * kLD + kq * 8));
+            bf16x8 fbl;
+            if (kBLo)
+                fbl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(Lbl + c * kLD + kq * 8));
+#pragma unroll
+            for (int rt = 0; rt < S::RT; ++rt) {
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fb, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fal[rt], fb, acc[rt][ct], 0, 0, 0);
+                if (kBLo)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fbl, acc[rt][ct], 0, 0, 0);
+            }
         }
         __syncthreads();
-        mfma_step<HasLo<W>::value>(Ah, Al, Bh, Bl, wr * 32, bcol, lane, acc);
-        __syncthreads();
     }
+    gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
+}
+
+// 2-bit main loop. B arrives in mega-steps of 8 blocks: 8 consecutive lanes
+// read one B row's 8 blocks (64 bytes of codes and 32 of scale/min words), so
+// each wave-wide load touches 8 rows of one matrix; the raw words are held in
+// registers one mega-step ahead, then the codes go to LDS as they are and the
+// scales as fp32. Each wave expands the codes of its own B operands to bf16
+// in registers (8 codes per lane per operand). A: each thread holds BM/32
+// 16-byte pieces (row, part, hi or lo) of 4 consecutive blocks and reloads a
+// block's pieces with the block 4 steps ahead as soon as they are stored.
+// Loads go through buffer descriptors: rows past the end read as zero. The
+// minimum terms run after the loop (from the block sums of A and the minima
+// in global memory).
+constexpr int kMS = 8;           // blocks per mega-step
+// Word 3 of a raw buffer descriptor on gfx9 targets (32-bit data format;
+// offsets past num_records read as zero).
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kRawC = 2 * kMS + 1;   // LDS row stride (dwords) of raw codes
+constexpr int kRawS = kMS + 1;       // LDS row stride (floats) of scales
+
+// 8 codes (16 bits, LSB first) -> bf16 0..3 (exact): the float's upper half
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c16)
+{
+    uint32_t w[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int i = 0; i < 4; ++i) {
+        const float a = static_cast<float>((c16 >> (4 * i)) & 3u);
+        const float b = static_cast<float>((c16 >> (4 * i + 2)) & 3u);
+        w[i] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+template <bool DUAL, int BM>
+__global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
+{
+    using S = GemmShape<BM>;
+    constexpr int AP = BM / 32;            // A pieces per thread per block
+    constexpr int BL = kGN * kMS / 256;    // (row, block) words per thread per mega-step
+    __shared__ __align__(16) uint16_t La[2][BM * kLD];
+    __shared__ __align__(16) uint32_t Lrc[kGN * kRawC];
+    __shared__ float Lsc[kGN * kRawS];
+    __shared__ int Ltok[BM];
+    __shared__ float Lrw[BM];
+    __shared__ int Ltile[3];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, kq = lane >> 4;
+    const int wr = wave / S::WC, wc = wave % S::WC;
+    if (!gemm_tile<BM>(p, Ltile, Ltok, Lrw))
+        return;
+    const int e = Ltile[0], r0 = Ltile[1], nrows = Ltile[2];
+    const int n0 = blockIdx.x * (DUAL ? kGN / 2 : kGN);
+    const int NB = p.Kd / 32;
+    const size_t plane = static_cast<size_t>(p.N) * (p.Kd >> 2);   // bytes of the codes plane
+
+    // B raw words: wave w loads 64 consecutive B rows of one matrix (DUAL:
+    // waves 0-1 gate, 2-3 up), 8 rows per instruction
+    const int bl = tid & 7;
+    const size_t eoff = p.routed ? static_cast<size_t>(e) * p.bstride : 0;
+    const int rowb = p.Kd >> 2;   // bytes of codes per B row
+    const int msel = DUAL ? __builtin_amdgcn_readfirstlane(tid >> 7) : 0;   // wave-uniform
+    const uint8_t *mbase = (msel ? p.b1 : p.b0) + eoff;
+    const __amdgpu_buffer_rsrc_t rcode =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase), 0, static_cast<int>(plane), kBufWord3);
+    const __amdgpu_buffer_rsrc_t rsmw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase + plane), 0, p.N * NB * 4, kBufWord3);
+    const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + ((tid & 63) >> 3);   // local channel of row j: + 8 j
+    const int ch0 = n0 + chl0;
+    uint2 rc[BL];
+    uint32_t rs[BL];
+    auto load_b = [&](int M) {
+        const int blk = M * kMS + bl;
+        const int bb = blk < NB ? blk : 0;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const int col = n0 + bcol[ct] + (lane & 15);
+        for (int j = 0; j < BL; ++j) {
+            const int n = ch0 + 8 * j;
+            rc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, n * rowb + bb * 8, 0, 0));
+            rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rsmw, (n * NB + bb) * 4, 0, 0);
+        }
+    };
+    // LDS B row of local channel c of matrix msel (DUAL: chunks alternate gate / up)
+    auto lds_row = [&](int c) {
+        if (!DUAL)
+            return c;
+        constexpr int chunk = kGN / (2 * S::WC);
+        return (c / chunk) * 2 * chunk + msel * chunk + c % chunk;
+    };
+
+    // A pieces of this thread: piece q -> row q/8, part (q/2)%4, hi (even q)
+    // or lo; one descriptor over hi and lo (lo starts a_lo_off bytes after hi),
+    // padding rows read past its range (zeros)
+    const __amdgpu_buffer_rsrc_t ra_rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.ah), 0, p.a_lo_off + p.a_bytes, kBufWord3);
+    int arow[AP], apart[AP], ahl[AP], aoff[AP];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wr * 32 + rt * 16 + 4 * (lane >> 4) + i;
-                if (r < tr.nrows && col < p.N)
-                    p.out[static_cast<size_t>(tr.r0 + r) * p.N + col] = acc[rt][ct][i];
+    for (int j = 0; j < AP; ++j) {
+        const int q = tid + 256 * j;
+        arow[j] = q >> 3;
+        apart[j] = (q >> 1) & 3;
+        ahl[j] = q & 1;
+        const int src = Ltok[arow[j]];
+        aoff[j] = src >= 0 ? (ahl[j] ? p.a_lo_off : 0) + (src * p.Kd + apart[j] * 8) * 2 : 0x7fff0000;
+    }
+    uint4 ra[4][AP];
+    auto load_a = [&](int slot, int blk) {
+        const int bb = blk < NB ? blk : 0;
+#pragma unroll
+        for (int j = 0; j < AP; ++j)
+            ra[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_rs, aoff[j] + bb * 64, 0, 0));
+    };
+
+    f32x4 acc[S::RT][S::CT];
+#pragma unroll
+    for (int rt = 0; rt < S::RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < S::CT; ++ct)
+            acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_b(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        load_a(u, u);
+    const int nms = (NB + kMS - 1) / kMS;
+    for (int M = 0; M < nms; ++M) {
+        // raw codes and scales of this mega-step to LDS, then the next ones
+        {
+            const bool in = M * kMS + bl < NB;
+#pragma unroll
+            for (int j = 0; j < BL; ++j) {
+                const int row = lds_row(chl0 + 8 * j);
+                Lrc[row * kRawC + 2 * bl] = in ? rc[j].x : 0u;
+                Lrc[row * kRawC + 2 * bl + 1] = in ? rc[j].y : 0u;
+                Lsc[row * kRawS + bl] = in ? f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+            }
+        }
+        if (M + 1 < nms)
+            load_b(M + 1);
+#pragma unroll
+        for (int b = 0; b < kMS; ++b) {
+            const int blk = M * kMS + b;
+            if (blk >= NB)
+                break;
+            const int u = b & 3;
+            // A block blk (ring slot u)
+#pragma unroll
+            for (int j = 0; j < AP; ++j)
+                *reinterpret_cast<uint4 *>(&La[ahl[j]][arow[j] * kLD + apart[j] * 8]) = ra[u][j];
+            load_a(u, blk + 4);
+            __syncthreads();
+            bf16x8 fah[S::RT], fal[S::RT];
+#pragma unroll
+            for (int rt = 0; rt < S::RT; ++rt) {
+                const int r = wr * S::TR + rt * 16 + li;
+                fah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[0][r * kLD + kq * 8]));
+                fal[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[1][r * kLD + kq * 8]));
+            }
+#pragma unroll
+            for (int ct = 0; ct < S::CT; ++ct) {
+                const int c = wc * S::TC + ct * 16 + li;
+                const uint32_t cw = Lrc[c * kRawC + 2 * b + (kq >> 1)];
+                const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu);
+                const float sc = Lsc[c * kRawS + b];
+#pragma unroll
+                for (int rt = 0; rt < S::RT; ++rt) {
+                    f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fal[rt], fb, t, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[rt][ct][i] = fmaf(sc, t[i], acc[rt][ct][i]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // minimum terms: acc += sum_b asum[row][b] * m[col][b], 32 blocks per MFMA
+    for (int b0 = 0; b0 < NB; b0 += 32) {
+        bf16x8 xah[S::RT], xal[S::RT];
+#pragma unroll
+        for (int rt = 0; rt < S::RT; ++rt) {
+            const int src = Ltok[wr * S::TR + rt * 16 + li];
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int b = b0 + kq * 8 + j;
+                v[j] = (src >= 0 && b < NB) ? p.asum[static_cast<size_t>(src) * NB + b] : 0.0f;
+            }
+            split_frag(v, xah[rt], xal[rt]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < S::CT; ++ct) {
+            const int c = wc * S::TC + ct * 16 + li;
+            const uint8_t *cm;
+            const int cn = gemm_brow<DUAL, BM>(p, e, n0, c, cm);
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int b = b0 + kq * 8 + j;
+                v[j] = (cn < p.N && b < NB)
+                           ? f16_to_f32(ld_nt4(cm + plane + (static_cast<size_t>(cn) * NB + b) * 4) >> 16)
+                           : 0.0f;
+            }
+            bf16x8 mh, ml;
+            split_frag(v, mh, ml);
+#pragma unroll
+            for (int rt = 0; rt < S::RT; ++rt) {
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], mh, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], ml, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal[rt], mh, acc[rt][ct], 0, 0, 0);
             }
         }
     }
+    gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
 }
 
 // y[t] = sum_k out[inv[t*K + k]] + g_t * shared[t]   (float4 per thread)
@@ -565,7 +800,9 @@ struct PrefillWs {
     int32_t *ids;
     float *wts, *gate;
     int32_t *counts, *offsets, *perm, *inv, *tile_off;
-    float *hbuf, *hsh, *rout, *sout;
+    uint16_t *hh, *hl, *shh, *shl;   // h of the routed pairs [T*K][I] and of the shared expert [T][Is], bf16 hi/lo
+    float *xsum, *hsum;              // 32-element block sums of x [T][H/32] and of h [T*K][I/32]
+    float *rout, *sout;
 };
 
 static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool carve)
@@ -594,8 +831,12 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.perm = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.inv = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.tile_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (E + 1)));
-    w.hbuf = reinterpret_cast<float *>(take(sizeof(float) * P * I));
-    w.hsh = reinterpret_cast<float *>(take(sizeof(float) * T * Is));
+    w.hh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
+    w.hl = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
+    w.shh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * T * Is));
+    w.shl = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * T * Is));
+    w.xsum = reinterpret_cast<float *>(take(sizeof(float) * T * (H / 32)));
+    w.hsum = reinterpret_cast<float *>(take(sizeof(float) * P * (I / 32)));
     w.rout = reinterpret_cast<float *>(take(sizeof(float) * P * H));
     w.sout = reinterpret_cast<float *>(take(sizeof(float) * T * H));
     w.sort_bytes = off;   // total, when not carving
@@ -607,12 +848,34 @@ size_t prefill_ws_bytes(const moe_layer_desc *d, int T)
     return prefill_carve(nullptr, d, T, false).sort_bytes;
 }
 
+// Rows per routed tile: 32 when the expert groups are small on average (less
+// padding), else 64 (more reuse of each B step).
+static int routed_bm(int64_t P, int E) { return P < 48 * static_cast<int64_t>(E) ? 32 : 64; }
+
+template <typename W, bool DUAL>
+static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s)
+{
+    const dim3 grid((g.N + (DUAL ? kGN / 2 : kGN) - 1) / (DUAL ? kGN / 2 : kGN), tiles), block(256);
+    if constexpr (W::kChunk == 32) {
+        if (bm == 32)
+            hipLaunchKernelGGL((k_ggemm_q2<DUAL, 32>), grid, block, 0, s, g);
+        else
+            hipLaunchKernelGGL((k_ggemm_q2<DUAL, 64>), grid, block, 0, s, g);
+    } else {
+        if (bm == 32)
+            hipLaunchKernelGGL((k_ggemm<W, DUAL, 32>), grid, block, 0, s, g);
+        else
+            hipLaunchKernelGGL((k_ggemm<W, DUAL, 64>), grid, block, 0, s, g);
+    }
+}
+
 template <typename ET, typename ST>
-static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, hipStream_t s)
+static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm, hipStream_t s)
 {
     const int H = d->hidden, E = d->n_experts, K = d->top_k, I = d->inter, Is = d->shared_inter;
     const int64_t P = static_cast<int64_t>(T) * K;
-    const int max_tiles = static_cast<int>((P + kBM - 1) / kBM + E);
+    const int max_tiles = static_cast<int>((P + bm - 1) / bm + E);
+    const int sh_tiles = (T + 63) / 64;
     GemmArgs g{};
     g.T = T;
     g.K = K;
@@ -621,45 +884,62 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, hipStre
     g.offsets = w.offsets;
     g.perm = w.perm;
     g.wts = w.wts;
-    g.xh = w.xh;
-    g.xl = w.xl;
-    // routed gate/up
+    // routed gate/up: A = x rows of the pairs' tokens
     g.routed = 1;
+    g.ah = reinterpret_cast<const uint16_t *>(w.xh);
+    g.a_bytes = static_cast<int>(sizeof(uint16_t) * T * H);
+    g.a_lo_off = static_cast<int>(reinterpret_cast<const uint8_t *>(w.xl) - reinterpret_cast<const uint8_t *>(w.xh));
+    g.al = reinterpret_cast<const uint16_t *>(w.xl);
+    g.a_gather = 1;
     g.b0 = static_cast<const uint8_t *>(d->exp_gate);
     g.b1 = static_cast<const uint8_t *>(d->exp_up);
     g.bstride = mat_bytes<ET>(I, H);
     g.N = I;
     g.Kd = H;
-    g.out = w.hbuf;
-    hipLaunchKernelGGL((k_gemm_gateup<ET>), dim3((I + 63) / 64, max_tiles), dim3(256), 0, s, g);
-    // shared gate/up
+    g.hh = w.hh;
+    g.hl = w.hl;
+    g.asum = w.xsum;
+    g.hsum = ET::kChunk == 32 ? w.hsum : nullptr;
+    launch_ggemm<ET, true>(g, bm, max_tiles, s);
+    // shared gate/up: A = all x rows
     GemmArgs sg = g;
     sg.routed = 0;
+    sg.a_gather = 0;
     sg.b0 = static_cast<const uint8_t *>(d->sh_gate);
     sg.b1 = static_cast<const uint8_t *>(d->sh_up);
     sg.bstride = 0;
     sg.N = Is;
-    sg.out = w.hsh;
-    hipLaunchKernelGGL((k_gemm_gateup<ST>), dim3((Is + 63) / 64, (T + kBM - 1) / kBM), dim3(256), 0, s, sg);
-    // routed down
+    sg.hh = w.shh;
+    sg.hl = w.shl;
+    sg.hsum = nullptr;
+    launch_ggemm<ST, true>(sg, 64, sh_tiles, s);
+    // routed down: A = h of the pairs (sorted order)
     GemmArgs dg = g;
+    dg.ah = w.hh;
+    dg.a_bytes = static_cast<int>(sizeof(uint16_t) * P * I);
+    dg.a_lo_off = static_cast<int>(reinterpret_cast<const uint8_t *>(w.hl) - reinterpret_cast<const uint8_t *>(w.hh));
+    dg.al = w.hl;
+    dg.a_gather = 0;
+    dg.asum = w.hsum;
     dg.b0 = static_cast<const uint8_t *>(d->exp_down);
     dg.b1 = nullptr;
     dg.bstride = mat_bytes<ET>(H, I);
     dg.N = H;
     dg.Kd = I;
-    dg.a32 = w.hbuf;
     dg.out = w.rout;
-    hipLaunchKernelGGL((k_gemm_down<ET>), dim3((H + 127) / 128, max_tiles), dim3(256), 0, s, dg);
+    launch_ggemm<ET, false>(dg, bm, max_tiles, s);
     // shared down
     GemmArgs sd = dg;
     sd.routed = 0;
+    sd.ah = w.shh;
+    sd.a_bytes = static_cast<int>(sizeof(uint16_t) * T * Is);
+    sd.a_lo_off = static_cast<int>(reinterpret_cast<const uint8_t *>(w.shl) - reinterpret_cast<const uint8_t *>(w.shh));
+    sd.al = w.shl;
     sd.b0 = static_cast<const uint8_t *>(d->sh_down);
     sd.bstride = 0;
     sd.Kd = Is;
-    sd.a32 = w.hsh;
     sd.out = w.sout;
-    hipLaunchKernelGGL((k_gemm_down<ST>), dim3((H + 127) / 128, (T + kBM - 1) / kBM), dim3(256), 0, s, sd);
+    launch_ggemm<ST, false>(sd, 64, sh_tiles, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -698,7 +978,8 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
     const int64_t P = static_cast<int64_t>(T) * K;
     const PrefillWs w = prefill_carve(ws, d, T, true);
     const int64_t n8 = static_cast<int64_t>(T) * H / 8;
-    hipLaunchKernelGGL(k_split_x, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, x, n8, w.xh, w.xl);
+    hipLaunchKernelGGL(k_split_x, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, x, n8, w.xh, w.xl,
+                       w.xsum);
     int rc;
     if (ids_in) {
         hipLaunchKernelGGL(k_take_routing, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0, s, ids_in,
@@ -712,14 +993,17 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
     rc = launch_sort_by_expert(w.ids, T, K, E, w.counts, w.offsets, w.perm, w.sort_ws, s, w.inv);
     if (rc != MOE_OK)
         return rc;
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, w.tile_off);
+    const int bm = routed_bm(P, E);
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off);
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32) {
-        rc = et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, s)
-                           : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, s) : run_gemms<Q2, F32>(d, T, w, s));
+        rc = et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s)
+                           : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s)
+                                             : run_gemms<Q2, F32>(d, T, w, bm, s));
     } else {
-        rc = et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, s)
-                           : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, s) : run_gemms<Q2, BF16>(d, T, w, s));
+        rc = et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s)
+                           : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s)
+                                             : run_gemms<Q2, BF16>(d, T, w, bm, s));
     }
     if (rc != MOE_OK)
         return rc;
