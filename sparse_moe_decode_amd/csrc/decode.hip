@@ -763,6 +763,7 @@ struct DownArgs {
     const uint8_t *ed;         // routed down stack
     size_t estride;            // bytes per routed [H][I] matrix
     const uint8_t *sd;         // shared down
+    size_t sbytes;             // bytes of the shared [H][Is] matrix
     const SlotTable *slots;
     const float *hbuf;         // [pairs][Imax]
     int max_pairs;             // R * (K + 1): bound on the (slot, row) pairs
@@ -771,6 +772,18 @@ struct DownArgs {
 constexpr int kDnWaves = 8;    // one output row per wave
 // LDS for the staged h' rows of the down pass; beyond it h' is read from L2
 constexpr size_t kDnStageLds = 144 * 1024;
+
+// The first pieces of a down row are read through buffer descriptors over
+// one matrix: a piece that is not needed gets an offset past the end, which
+// returns zeros without a memory access. Every lane then issues the same
+// loads, so the compiler can count them and wait for just the earlier ones.
+constexpr int kAuxNT = 2;                   // non-temporal
+constexpr uint32_t kPastEnd = 0xFFFFFFF0u;  // an offset beyond every matrix
+constexpr int kRsrcWord3 = 0x00020000;      // raw 32-bit dwords, range-checked
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mat_rsrc(const uint8_t *base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
 
 // Down rows are read in pieces of 8 elements (bf16: 16 bytes; 2-bit: 2 bytes
 // of codes plus the block's scale/min) or 4 elements (fp32: 16 bytes). Lane
@@ -785,6 +798,11 @@ struct DnPiece<BF16> {
     __device__ __forceinline__ void load(const MatRef &M, int j, int c)
     {
         v = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 8) * 2);
+    }
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, const MatRef &M, int j, int c, bool ok)
+    {
+        const uint32_t off = ok ? static_cast<uint32_t>((j * M.cols + c * 8) * 2) : kPastEnd;
+        v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT));
     }
     __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
     {
@@ -811,6 +829,12 @@ struct DnPiece<F32> {
         const uint4 u = ld_nt16(M.base + (static_cast<size_t>(j) * M.cols + c * 4) * 4);
         v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, const MatRef &M, int j, int c, bool ok)
+    {
+        const uint32_t off = ok ? static_cast<uint32_t>((j * M.cols + c * 4) * 4) : kPastEnd;
+        const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT));
+        v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    }
     __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
     {
         const float4 hv = *reinterpret_cast<const float4 *>(h + c * 4);
@@ -828,6 +852,14 @@ struct DnPiece<Q2> {
         const int b = c >> 2;
         codes = ld_nt2(M.base + static_cast<size_t>(j) * (M.cols >> 2) + c * 2);
         sm = ld_nt4(M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) + (static_cast<size_t>(j) * nb + b) * 4);
+    }
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, const MatRef &M, int j, int c, bool ok)
+    {
+        const int nb = M.cols >> 5;
+        const uint32_t oc = ok ? static_cast<uint32_t>(j * (M.cols >> 2) + c * 2) : kPastEnd;
+        const uint32_t os = ok ? static_cast<uint32_t>(M.rows * (M.cols >> 2) + (j * nb + (c >> 2)) * 4) : kPastEnd;
+        codes = __builtin_amdgcn_raw_buffer_load_b16(r, oc, 0, kAuxNT);
+        sm = __builtin_amdgcn_raw_buffer_load_b32(r, os, 0, kAuxNT);
     }
     // sum_i (code_i * s + m) h_i = s * sum_i code_i h_i + m * sum_i h_i
     __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
@@ -863,9 +895,11 @@ struct DnBatch<Q2> {
 //   y[q][j] = sum over routed slots s used by row q of D_s[j] . h'(s, q)
 //             + gate_q * D_shared[j] . h'(0, q)
 // (h' carries the route weight). Only the (slot, row) pairs that carry
-// weight exist, so a few-row call costs one row's arithmetic per slot. The
-// shared piece and the first batch of routed pieces are requested before
-// h' is staged in LDS (STAGED; otherwise h' is read from L2).
+// weight exist, so a few-row call costs one row's arithmetic per slot.
+// Request order: the first part of h' (STAGED: h' goes to LDS; otherwise it
+// is read from L2), then the shared piece and the first batch of routed
+// pieces. Loads complete in order, so h' is in LDS while the weight stream
+// is still arriving, and each piece's products start as soon as it lands.
 template <int R, typename ET, typename ST, bool STAGED>
 __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 {
@@ -879,10 +913,32 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     const int npr = p.I / DnPiece<ET>::kElems, nps = p.Is / DnPiece<ST>::kElems;
     const MatRef SD{p.sd, p.H, p.Is};
 
+    // h' and the slot-table entries for the LDS copies are requested first.
+    // Every load of this prologue is unconditional (indices are clamped;
+    // the weight pieces go through range-checked buffer loads), so the waits
+    // before the LDS writes below cover only these early loads, not the
+    // weight stream behind them; clamped duplicates rewrite equal values.
+    constexpr int kT = kDnWaves * kWave;
+    const int n4 = STAGED ? p.max_pairs * p.Imax / 4 : 1;
+    const float4 *hsrc = reinterpret_cast<const float4 *>(p.hbuf);
+    const int i0 = min(tid, n4 - 1), i1 = min(tid + kT, n4 - 1), i2 = min(tid + 2 * kT, n4 - 1),
+              i3 = min(tid + 3 * kT, n4 - 1);
+    float4 h0, h1, h2, h3;   // separate values, never an indexed array
+    if (STAGED) {
+        h0 = hsrc[i0];
+        h1 = hsrc[i1];
+        h2 = hsrc[i2];
+        h3 = hsrc[i3];
+    }
+    const int ti = min(tid, kMaxRows * kMaxK), tq = min(tid, R - 1);
+    const int t_expert = p.slots->expert[ti];
+    const uint32_t t_rmask = R > 1 ? p.slots->rmask[ti] : 0u;
+    const int t_pstart = R > 1 ? p.slots->pstart[ti] : 0;
+    const float t_gate = p.slots->w[0][tq];
+    __builtin_amdgcn_sched_barrier(0);
     DnPiece<ST> ps;
     DnPiece<ET> pc[B];
-    if (live && lane < nps)
-        ps.load(SD, j, lane);
+    ps.load_b(mat_rsrc(p.sd, p.sbytes), SD, j, lane, live && lane < nps);
     {
         // the first batch's expert ids in one go (16-byte reads of the table)
         constexpr int NV = (B + 4) / 4;
@@ -894,32 +950,34 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
         for (int u = 0; u < B; ++u) {
             const int4 &v = ev[(1 + u) >> 2];
             const int r = (1 + u) & 3;
-            const int e = r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
-            if (live && 1 + u < nslots && lane < npr)
-                pc[u].load(MatRef{p.ed + e * p.estride, p.H, p.I}, j, lane);
+            const bool used = 1 + u < nslots;
+            const int e = used ? (r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w) : 0;
+            const MatRef M{p.ed + e * p.estride, p.H, p.I};
+            pc[u].load_b(mat_rsrc(M.base, p.estride), M, j, lane, live && used && lane < npr);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     // the slot table's pair layout and gates into LDS, beside the h' staging
     __shared__ uint32_t rmask[kMaxRows * kMaxK + 1];
     __shared__ int pstart[kMaxRows * kMaxK + 1];
     __shared__ float gate[kMaxRows];
     __shared__ int expert[kMaxRows * kMaxK + 1];
-    if (R > 1 && tid < nslots) {
-        expert[tid] = p.slots->expert[tid];
-        rmask[tid] = p.slots->rmask[tid];
-        pstart[tid] = p.slots->pstart[tid];
+    expert[ti] = t_expert;
+    if (R > 1) {
+        rmask[ti] = t_rmask;
+        pstart[ti] = t_pstart;
     }
-    if (R == 1 && tid < nslots)
-        expert[tid] = p.slots->expert[tid];
-    if (tid < R)
-        gate[tid] = p.slots->w[0][tid];
+    gate[tq] = t_gate;
     const float *hl = p.hbuf;
     if (STAGED) {
-        float *dst = reinterpret_cast<float *>(lds_raw);
-        const int n4 = p.max_pairs * p.Imax / 4;
-        for (int i = tid; i < n4; i += blockDim.x)
-            reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(p.hbuf)[i];
-        hl = dst;
+        float4 *dst = reinterpret_cast<float4 *>(lds_raw);
+        dst[i0] = h0;
+        dst[i1] = h1;
+        dst[i2] = h2;
+        dst[i3] = h3;
+        for (int i = tid + 4 * kT; i < n4; i += kT)
+            dst[i] = hsrc[i];
+        hl = reinterpret_cast<const float *>(lds_raw);
     }
     __syncthreads();
     if (!live)
@@ -1155,6 +1213,7 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     dn.ed = static_cast<const uint8_t *>(d->exp_down);
     dn.estride = mat_bytes<ET>(H, I);
     dn.sd = static_cast<const uint8_t *>(d->sh_down);
+    dn.sbytes = mat_bytes<ST>(H, Is);
     dn.slots = w.slots;
     dn.hbuf = w.hbuf;
     dn.max_pairs = max_pairs(R, K);
