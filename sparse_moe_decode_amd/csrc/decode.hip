@@ -343,42 +343,32 @@ __device__ __forceinline__ void dot_chunk(BF16, const uint4 &w, int k, const flo
         acc[q] = a;
     }
 }
-// one 32-weight block: s * sum_j code_j x_j + m * sum_j x_j
-template <int R>
-__device__ __forceinline__ void dot_block(const uint2 &cw, uint32_t sm, int b, const float *xs, int H,
-                                          const float *xsum, float (&acc)[R])
+// 2-bit blocks read x one block per lane, 128 bytes apart, which would put
+// eight lanes of every ds_read_b128 quarter on the same banks. x is staged
+// with the 16-byte chunks of block b permuted by c -> c ^ (b & 7) (see
+// stage_x), so step s of a lane reads physical chunk s (an immediate offset)
+// and the lanes of a quarter spread over the banks; the block's code bytes
+// are permuted the same way once per block.
+__device__ __forceinline__ int x_chunk_slot(int b, int c) { return c ^ (b & 7); }
+
+// Code word of a 32-weight block with its 4-weight bytes reordered so that
+// byte s holds the codes of logical chunk s ^ m (m = b & 7).
+__device__ __forceinline__ uint2 codes_for_slots(const uint2 &cw, int m)
 {
-    const float s = f16_to_f32(sm & 0xffffu);
-    const float m = f16_to_f32(sm >> 16);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float *x = xs + q * H + b * 32;
-        float cx = 0.0f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint32_t d = half ? cw.y : cw.x;
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                const float4 xv = *reinterpret_cast<const float4 *>(x + half * 16 + j4 * 4);
-                const uint32_t byte = d >> (8 * j4);
-                cx = fmaf(static_cast<float>(byte & 3u), xv.x, cx);
-                cx = fmaf(static_cast<float>((byte >> 2) & 3u), xv.y, cx);
-                cx = fmaf(static_cast<float>((byte >> 4) & 3u), xv.z, cx);
-                cx = fmaf(static_cast<float>((byte >> 6) & 3u), xv.w, cx);
-            }
-        }
-        acc[q] = fmaf(s, cx, fmaf(m, xsum[q * (H >> 5) + b], acc[q]));
-    }
+    const uint32_t w0 = (m & 4) ? cw.y : cw.x, w1 = (m & 4) ? cw.x : cw.y;
+    const uint32_t sel = 0x03020100u ^ (static_cast<uint32_t>(m & 3) * 0x01010101u);
+    return make_uint2(__builtin_amdgcn_perm(0u, w0, sel), __builtin_amdgcn_perm(0u, w1, sel));
 }
 
 // The gate and up blocks at the same position share their x values: each
 // float4 of x is used for both as soon as it is read.
 template <int R>
-__device__ __forceinline__ void dot_block2(const uint2 &gc, uint32_t gsm, const uint2 &uc, uint32_t usm, int b,
+__device__ __forceinline__ void dot_block2(const uint2 &gc0, uint32_t gsm, const uint2 &uc0, uint32_t usm, int b,
                                            const float *xs, int H, const float *xsum, float (&a)[R], float (&c)[R])
 {
     const float gsc = f16_to_f32(gsm & 0xffffu), gmn = f16_to_f32(gsm >> 16);
     const float usc = f16_to_f32(usm & 0xffffu), umn = f16_to_f32(usm >> 16);
+    const uint2 gc = codes_for_slots(gc0, b & 7), uc = codes_for_slots(uc0, b & 7);
 #pragma unroll
     for (int q = 0; q < R; ++q) {
         const float *x = xs + q * H + b * 32;
@@ -435,8 +425,16 @@ __device__ __forceinline__ void dot_rows(Q2, const RowChunks<Q2> &r, int base, i
 template <int R, typename W>
 __device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float *xsum)
 {
-    for (int i = threadIdx.x; i < R * H / 4; i += blockDim.x)
-        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(x)[i];
+    // 2-bit weights: chunk c of block b of a row at slot x_chunk_slot(b, c)
+    const int n4 = H >> 2;
+    for (int i = threadIdx.x; i < R * n4; i += blockDim.x) {
+        int d = i;
+        if (W::kChunk == 32) {
+            const int q = i / n4, r = i - q * n4;
+            d = q * n4 + (r & ~7) + x_chunk_slot(r >> 3, r & 7);
+        }
+        reinterpret_cast<float4 *>(xs)[d] = reinterpret_cast<const float4 *>(x)[i];
+    }
     __syncthreads();
     if (W::kChunk == 32) {
         for (int i = threadIdx.x; i < R * (H >> 5); i += blockDim.x) {
