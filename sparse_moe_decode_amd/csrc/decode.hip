@@ -60,51 +60,52 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
         }
         return;
     }
+    // lane l < R*K holds selection l (row l / K); the other selections are
+    // broadcast with readlane in uniform loops (no LDS round trips)
     const int RK = R * K;
-    const int lq = lane / K, lk = lane - lq * K;
-    bool first = false;
-    int e = -1;
-    if (lane < RK) {
-        e = rl.sel_e[lq][lk];
-        first = true;
-        for (int q = 0; q <= lq; ++q) {
-            const int kend = q < lq ? K : lk;
-            for (int k = 0; k < kend; ++k)
-                first = first && rl.sel_e[q][k] != e;
+    const bool in = lane < RK;
+    const int lq = in ? lane / K : 0, lk = in ? lane - lq * K : 0;
+    const int e = in ? rl.sel_e[lq][lk] : -1;
+    const float wl = in ? rl.sel_w[lq][lk] : 0.0f;
+    bool first = in;
+    float wq[R];
+    uint32_t rm = 0;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        wq[q] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int j = q * K + k;
+            const int ej = __builtin_amdgcn_readlane(e, j);
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+            const bool m = ej == e;
+            first = first && !(m && j < lane);
+            wq[q] += m ? wj : 0.0f;
+            rm |= m ? 1u << q : 0u;
         }
     }
+    const unsigned long long lt = (1ull << lane) - 1ull;
     const unsigned long long mask = __ballot(first);
-    const int slot = 1 + __popcll(mask & ((1ull << lane) - 1ull));
+    const int slot = 1 + __popcll(mask & lt);
     const int ns = 1 + __popcll(mask);
-    uint32_t rm = 0;
     if (first) {
         rl.slots.expert[slot] = e;
 #pragma unroll
-        for (int q = 0; q < R; ++q) {
-            float w = 0.0f;
-            bool used = false;
-            for (int k = 0; k < K; ++k)
-                if (rl.sel_e[q][k] == e) {
-                    w += rl.sel_w[q][k];
-                    used = true;
-                }
-            rl.slots.w[slot][q] = w;
-            rm |= used ? 1u << q : 0u;
-        }
+        for (int q = 0; q < R; ++q)
+            rl.slots.w[slot][q] = wq[q];
         rl.slots.rmask[slot] = rm;
     }
-    // pair numbering: slot 0 (all rows) first, then the slots in order;
-    // lane l holds the first-appearance flag of slot 1 + (its rank)
+    // pair numbering: slot 0 (all rows) first, then the slots in order; the
+    // prefix of the per-slot pair counts (< 8) from ballots of their bits
     const int cnt = first ? __popc(rm) : 0;
-    int incl = cnt;
+    int excl = 0, total = 0;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(incl, o, kWave);
-        if (lane >= o)
-            incl += t;
+    for (int bit = 0; bit < 3; ++bit) {
+        const unsigned long long mb = __ballot((cnt >> bit) & 1);
+        excl += __popcll(mb & lt) << bit;
+        total += __popcll(mb) << bit;
     }
     if (first)
-        rl.slots.pstart[slot] = R + incl - cnt;
+        rl.slots.pstart[slot] = R + excl;
     if (lane == 0) {
         rl.slots.nslots = ns;
         rl.slots.expert[0] = -1;
@@ -114,8 +115,8 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
         for (int q = 0; q < R; ++q)
             rl.slots.w[0][q] = rl.g[q];
     }
-    if (lane == kWave - 1)
-        rl.slots.pstart[ns] = R + incl;
+    if (lane == 0)
+        rl.slots.pstart[ns] = R + total;
 }
 
 // Pair (row i of hbuf) of row q in `slot`, or -1 if the row does not use it.
