@@ -26,6 +26,7 @@
 #include <cstddef>
 #include <climits>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "device_common.cuh"
@@ -860,24 +861,58 @@ struct DnPiece<Q2> {
         codes = __builtin_amdgcn_raw_buffer_load_b16(r, oc, 0, kAuxNT);
         sm = __builtin_amdgcn_raw_buffer_load_b32(r, os, 0, kAuxNT);
     }
-    // sum_i (code_i * s + m) h_i = s * sum_i code_i h_i + m * sum_i h_i
-    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
+    // The piece as floats: codes (each with one byte conversion), scale, min.
+    struct Dec {
+        float c[8];
+        float s, m;
+    };
+    __device__ __forceinline__ Dec dec() const
     {
-        const float s = f16_to_f32(sm & 0xffffu);
-        const float m = f16_to_f32(sm >> 16);
+        // byte 0 / 1 of wk: code k / k + 4; opaque so that the byte
+        // conversions are not folded back into 2-bit extracts
+        uint32_t w0 = codes & 0x0303u, w1 = (codes >> 2) & 0x0303u, w2 = (codes >> 4) & 0x0303u,
+                 w3 = (codes >> 6) & 0x0303u;
+        asm("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+        Dec d;
+        d.c[0] = static_cast<float>(w0 & 0xffu);
+        d.c[1] = static_cast<float>(w1 & 0xffu);
+        d.c[2] = static_cast<float>(w2 & 0xffu);
+        d.c[3] = static_cast<float>(w3 & 0xffu);
+        d.c[4] = static_cast<float>((w0 >> 8) & 0xffu);
+        d.c[5] = static_cast<float>((w1 >> 8) & 0xffu);
+        d.c[6] = static_cast<float>((w2 >> 8) & 0xffu);
+        d.c[7] = static_cast<float>((w3 >> 8) & 0xffu);
+        d.s = f16_to_f32(sm & 0xffffu);
+        d.m = f16_to_f32(sm >> 16);
+        return d;
+    }
+    // sum of the 8 h values of piece c
+    static __device__ __forceinline__ float hsum(const float *h, int c)
+    {
+        const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
+        const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
+        return ((h0.x + h0.y) + (h0.z + h0.w)) + ((h1.x + h1.y) + (h1.z + h1.w));
+    }
+    // sum_i (code_i * s + m) h_i = s * sum_i code_i h_i + m * sum_i h_i, with
+    // hs = sum_i h_i given
+    static __device__ __forceinline__ void fma_d(const Dec &d, const float *h, int c, float hs, float &acc)
+    {
         const float4 h0 = *reinterpret_cast<const float4 *>(h + c * 8);
         const float4 h1 = *reinterpret_cast<const float4 *>(h + c * 8 + 4);
         float cx = 0.0f;
-        cx = fmaf(static_cast<float>(codes & 3u), h0.x, cx);
-        cx = fmaf(static_cast<float>((codes >> 2) & 3u), h0.y, cx);
-        cx = fmaf(static_cast<float>((codes >> 4) & 3u), h0.z, cx);
-        cx = fmaf(static_cast<float>((codes >> 6) & 3u), h0.w, cx);
-        cx = fmaf(static_cast<float>((codes >> 8) & 3u), h1.x, cx);
-        cx = fmaf(static_cast<float>((codes >> 10) & 3u), h1.y, cx);
-        cx = fmaf(static_cast<float>((codes >> 12) & 3u), h1.z, cx);
-        cx = fmaf(static_cast<float>((codes >> 14) & 3u), h1.w, cx);
-        const float hs = ((h0.x + h0.y) + (h0.z + h0.w)) + ((h1.x + h1.y) + (h1.z + h1.w));
-        acc = fmaf(s, cx, fmaf(m, hs, acc));
+        cx = fmaf(d.c[0], h0.x, cx);
+        cx = fmaf(d.c[1], h0.y, cx);
+        cx = fmaf(d.c[2], h0.z, cx);
+        cx = fmaf(d.c[3], h0.w, cx);
+        cx = fmaf(d.c[4], h1.x, cx);
+        cx = fmaf(d.c[5], h1.y, cx);
+        cx = fmaf(d.c[6], h1.z, cx);
+        cx = fmaf(d.c[7], h1.w, cx);
+        acc = fmaf(d.s, cx, fmaf(d.m, hs, acc));
+    }
+    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
+    {
+        fma_d(dec(), h, c, hsum(h, c), acc);
     }
 };
 
@@ -968,14 +1003,28 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     }
     gate[tq] = t_gate;
     const float *hl = p.hbuf;
+    // One-row calls with 2-bit pieces also use the sum of each 8-value piece
+    // of h': formed here once per workgroup from the two float4 halves held
+    // by lanes 2i, 2i+1 (measured slower with several rows)
+    constexpr bool HS = STAGED && R == 1 && std::is_same<ET, Q2>::value;
+    float *hsl = reinterpret_cast<float *>(lds_raw) + (HS ? p.max_pairs * p.Imax : 0);
     if (STAGED) {
         float4 *dst = reinterpret_cast<float4 *>(lds_raw);
-        dst[i0] = h0;
-        dst[i1] = h1;
-        dst[i2] = h2;
-        dst[i3] = h3;
+        auto put = [&](int i, int ic, const float4 &v) {
+            dst[ic] = v;
+            if constexpr (HS) {
+                const float part = (v.x + v.y) + (v.z + v.w);
+                const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0xB1, 0xF, 0xF, false));
+                if ((i & 1) == 0 && i < n4)
+                    hsl[i >> 1] = part + other;
+            }
+        };
+        put(tid, i0, h0);
+        put(tid + kT, i1, h1);
+        put(tid + 2 * kT, i2, h2);
+        put(tid + 3 * kT, i3, h3);
         for (int i = tid + 4 * kT; i < n4; i += kT)
-            dst[i] = hsrc[i];
+            put(i, i, hsrc[i]);
         hl = reinterpret_cast<const float *>(lds_raw);
     }
     __syncthreads();
@@ -1010,7 +1059,11 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
 #pragma unroll
             for (int u = 0; u < B; ++u) {
                 if (s0 + u < nslots && c < npr) {
-                    if constexpr (R == 1) {
+                    if constexpr (HS) {
+                        // pair = slot; the piece's h' sum from LDS
+                        const float *h = hl + static_cast<size_t>(s0 + u) * p.Imax;
+                        DnPiece<Q2>::fma_d(pc[u].dec(), h, c, hsl[(s0 + u) * (p.Imax >> 3) + c], acc[0]);
+                    } else if constexpr (R == 1) {
                         pc[u].fma1(hl + static_cast<size_t>(s0 + u) * p.Imax, c, acc[0]);   // pair = slot
                     } else {
                         const uint32_t m = rmask[s0 + u];
@@ -1217,7 +1270,9 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     dn.hbuf = w.hbuf;
     dn.max_pairs = max_pairs(R, K);
     const dim3 dgrid((H + kDnWaves - 1) / kDnWaves), dblock(kDnWaves * kWave);
-    const size_t stage = static_cast<size_t>(dn.max_pairs) * Imax * sizeof(float);
+    // staged h' (and, for one row with 2-bit experts, one sum per 8-value piece)
+    const size_t stage =
+        static_cast<size_t>(dn.max_pairs) * Imax * sizeof(float) * (R == 1 && std::is_same<ET, Q2>::value ? 9 : 8) / 8;
     if (stage <= kDnStageLds) {
         switch (R) {
         case 1: hipLaunchKernelGGL((k_down<1, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
