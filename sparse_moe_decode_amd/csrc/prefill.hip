@@ -5,7 +5,8 @@
 //   k_split_x         x (fp32) -> x_hi + x_lo (bf16 pair; x - hi - lo is
 //                     below 2^-17 |x|)
 //   k_logits64        router logits [T][E] and shared-gate logits [T] in
-//                     fp64: exact products, a fixed summation order
+//                     fp64 (v_mfma_f64_16x16x4_f64): exact products, a fixed
+//                     summation order
 //   k_select_rows     exact top-K per row (one wave per row), softmax weights,
 //                     sigmoid gate
 //   sort (sort.hip)   stable counting sort of the T*K (row, slot) pairs by
@@ -78,93 +79,102 @@ __global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uin
 
 // =========================================================== fp64 logits
 
-constexpr int kLgTile = 64;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// One 64x64 tile of logits (rows t, experts e; expert index E is the
-// shared-gate vector). 16x16 threads, 4x4 outputs each, k in steps of 32.
+constexpr int kLmT = 64;    // rows (tokens) per workgroup
+constexpr int kLmE = 32;    // experts per workgroup (column E is the gate vector)
+constexpr int kLmK = 32;    // reduction depth per LDS stage
+constexpr int kLmLD = 33;   // LDS row stride in doubles
+
+// One 64 x 32 tile of logits (rows t, experts e; expert index E is the
+// shared-gate vector) with v_mfma_f64_16x16x4_f64: each product of an fp32
+// activation and a bf16/fp32 weight is exact in fp64, and the hardware's
+// summation order is fixed. Wave w owns rows 16w..16w+15 and both 16-column
+// halves. Operands are converted to fp64 once, as they are staged in LDS
+// (double buffered; the next stage's global loads are in flight during the
+// current stage's MFMAs).
 template <typename RT>
 __global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, int E, const uint8_t *router_w,
                                                   const uint8_t *gate_w, const float *bias, double *logits,
                                                   double *z)
 {
-    __shared__ float xs[kLgTile][33];
-    __shared__ float wsm[kLgTile][33];
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int e0 = blockIdx.x * kLgTile, t0 = blockIdx.y * kLgTile;
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    __shared__ double Lx[2][kLmT][kLmLD];
+    __shared__ double Lw[2][kLmE][kLmLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e0 = blockIdx.x * kLmE, t0 = blockIdx.y * kLmT;
+    // loaders: x rows tid / 4 (8 values at k (tid % 4) * 8), weight rows
+    // tid / 8 (4 values at k (tid % 8) * 4); rows past the end read as 0
+    const int xr = tid >> 2, xk = (tid & 3) * 8;
+    const int wr = tid >> 3, wk = (tid & 7) * 4;
+    const int t = t0 + xr, e = e0 + wr;
+    const bool tin = t < T, ein = e <= E;
+    const float *xrow = x + static_cast<size_t>(tin ? t : 0) * H;
+    const uint8_t *wrow = (ein && e < E) ? router_w + static_cast<size_t>(e) * H * (RT::kChunk == 4 ? 4 : 2) : gate_w;
+    float xv[8], wv[4];
+    auto fetch = [&](int k0) {
+        const float4 a = *reinterpret_cast<const float4 *>(xrow + k0 + xk);
+        const float4 b = *reinterpret_cast<const float4 *>(xrow + k0 + xk + 4);
+        xv[0] = tin ? a.x : 0.f; xv[1] = tin ? a.y : 0.f; xv[2] = tin ? a.z : 0.f; xv[3] = tin ? a.w : 0.f;
+        xv[4] = tin ? b.x : 0.f; xv[5] = tin ? b.y : 0.f; xv[6] = tin ? b.z : 0.f; xv[7] = tin ? b.w : 0.f;
+        if (RT::kChunk == 4) {
+            const float4 c = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(wrow) + k0 + wk);
+            wv[0] = c.x; wv[1] = c.y; wv[2] = c.z; wv[3] = c.w;
+        } else {
+            const uint2 c = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(wrow) + k0 + wk);
+            wv[0] = bf16_lo(c.x); wv[1] = bf16_hi(c.x); wv[2] = bf16_lo(c.y); wv[3] = bf16_hi(c.y);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = 0.0;
-    const int lr = tid >> 2, lp = tid & 3;   // loader: row, 8-element part
-    for (int k0 = 0; k0 < H; k0 += 32) {
-        {
-            const int t = t0 + lr;
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (t < T) {
-                const float4 a = *reinterpret_cast<const float4 *>(x + static_cast<size_t>(t) * H + k0 + lp * 8);
-                const float4 b = *reinterpret_cast<const float4 *>(x + static_cast<size_t>(t) * H + k0 + lp * 8 + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            wv[j] = ein ? wv[j] : 0.f;
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            Lx[buf][xr][xk + j] = static_cast<double>(xv[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            Lw[buf][wr][wk + j] = static_cast<double>(wv[j]);
+    };
+    f64x4 acc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int li = lane & 15, lk = lane >> 4;
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    const int nk = H / kLmK;
+    for (int kb = 0; kb < nk; ++kb) {
+        const int buf = kb & 1;
+        if (kb + 1 < nk)
+            fetch((kb + 1) * kLmK);
+#pragma unroll
+        for (int ks = 0; ks < kLmK / 4; ++ks) {
+            const double av = Lx[buf][wave * 16 + li][ks * 4 + lk];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const double bv = Lw[buf][c * 16 + li][ks * 4 + lk];
+                acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                xs[lr][lp * 8 + j] = v[j];
         }
-        {
-            const int e = e0 + lr;
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (e <= E) {
-                if (RT::kChunk == 4) {
-                    const float *row = reinterpret_cast<const float *>(e < E ? router_w + static_cast<size_t>(e) * H * 4
-                                                                             : gate_w);
-                    const float4 a = *reinterpret_cast<const float4 *>(row + k0 + lp * 8);
-                    const float4 b = *reinterpret_cast<const float4 *>(row + k0 + lp * 8 + 4);
-                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-                } else {
-                    const uint16_t *row = reinterpret_cast<const uint16_t *>(
-                        e < E ? router_w + static_cast<size_t>(e) * H * 2 : gate_w);
-                    const uint4 u = *reinterpret_cast<const uint4 *>(row + k0 + lp * 8);
-                    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-                    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                wsm[lr][lp * 8 + j] = v[j];
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int k = 0; k < 32; ++k) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = static_cast<double>(xs[ty * 4 + i][k]);
-                b[i] = static_cast<double>(wsm[tx * 4 + i][k]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = fma(a[i], b[j], acc[i][j]);
-        }
+        if (kb + 1 < nk)
+            stage(buf ^ 1);
         __syncthreads();
     }
+    // D[r][c] of a 16x16 fp64 tile: lane l holds rows l / 16 + 4 i (i < 4),
+    // column l % 16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty * 4 + i;
-        if (t >= T)
-            continue;
+    for (int c = 0; c < 2; ++c) {
+        const int ee = e0 + c * 16 + li;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tx * 4 + j;
-            if (e < E)
-                logits[static_cast<size_t>(t) * E + e] = acc[i][j] + (bias ? static_cast<double>(bias[e]) : 0.0);
-            else if (e == E)
-                z[t] = acc[i][j];
+        for (int i = 0; i < 4; ++i) {
+            const int tt = t0 + wave * 16 + lk + 4 * i;
+            if (tt >= T)
+                continue;
+            if (ee < E)
+                logits[static_cast<size_t>(tt) * E + ee] = acc[c][i] + (bias ? static_cast<double>(bias[ee]) : 0.0);
+            else if (ee == E)
+                z[tt] = acc[c][i];
         }
     }
 }
@@ -949,7 +959,7 @@ static int prefill_route(const moe_layer_desc *d, const float *x, int T, const P
                          float *wts_out, float *gate_out, hipStream_t s)
 {
     const int H = d->hidden, E = d->n_experts, K = d->top_k;
-    const dim3 lg((E + 1 + kLgTile - 1) / kLgTile, (T + kLgTile - 1) / kLgTile);
+    const dim3 lg((E + 1 + kLmE - 1) / kLmE, (T + kLmT - 1) / kLmT);
     if (d->router_t == MOE_F32)
         hipLaunchKernelGGL((k_logits64<F32>), lg, dim3(256), 0, s, x, T, H, E,
                            static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
