@@ -198,6 +198,42 @@ def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0):
     return wl, ms, wall
 
 
+EXTRA_WORKLOADS = [("decode_q2", 2, 1, 1000), ("fewrow_q2_R2", 3, 2, 500), ("fewrow_q2_R3", 3, 3, 333),
+                   ("prefill_q2", 4, 2048, 1)]
+
+
+def run_extra(args, keys):
+    """The 2-bit decode, few-row and prefill workloads (all, or those in keys)."""
+    import torch
+    cfg = mi.CONFIGS[1]
+    extra = {}
+    for key, idx, rows, ncalls in EXTRA_WORKLOADS:
+        if keys is not None and key not in keys:
+            continue
+        c = mi.CONFIGS[idx].with_(rows_per_call=rows)
+        print(f"[bench] {key}", file=sys.stderr, flush=True)
+        w2, m2, _ = measure(c, rows, ncalls, args.rotate if rows < 2048 else 1,
+                            max(2, args.steps // 2), 1, x_instance=rows if idx == 3 else 0)
+        u = w2.union_sizes()
+        per_call = m2 / 1e3 / ncalls
+        rec = {"ms_per_step": round(m2, 4), "calls": ncalls, "rows_per_call": rows,
+               "rows_per_s": round(rows * ncalls / (m2 / 1e3), 1), "us_per_call": round(per_call * 1e6, 3)}
+        if rows < 2048:
+            b = float(np.mean([call_bytes(c, rows, n) for n in u]))
+            rec.update({"bytes_per_call": round(b), "mean_expert_union": round(float(u.mean()), 3),
+                        "GBps": round(b / per_call / 1e9, 1),
+                        "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4)})
+        else:
+            flops = 2.0 * rows * (cfg.K * 3 * cfg.H * cfg.I + 3 * cfg.H * cfg.Is + cfg.E * cfg.H)
+            rec.update({"useful_GFLOP": round(flops / 1e9, 2),
+                        "TFLOPs": round(flops / per_call / 1e12, 2),
+                        "mfma_frac": round(flops / per_call / 1e12 / BF16_PEAK_TFLOPS, 4)})
+        extra[key] = rec
+        del w2
+        torch.cuda.empty_cache()
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +243,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
+    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2"],
+                    help="run just this one of the other workloads (for profiling); prints its record")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -219,6 +257,11 @@ def main():
     moe.lib()                                     # fails loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.only:
+        extra = run_extra(args, [args.only])
+        print(json.dumps({"workload": args.only, **extra[args.only]}), flush=True)
+        return
 
     cfg = mi.CONFIGS[1]
     print(f"[bench] building {cfg.name} workload, {args.rotate} dense-weight instances", file=sys.stderr, flush=True)
@@ -248,29 +291,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extra:
-        for key, idx, rows, ncalls in [("decode_q2", 2, 1, 1000), ("fewrow_q2_R2", 3, 2, 500),
-                                       ("fewrow_q2_R3", 3, 3, 333), ("prefill_q2", 4, 2048, 1)]:
-            c = mi.CONFIGS[idx].with_(rows_per_call=rows)
-            print(f"[bench] {key}", file=sys.stderr, flush=True)
-            w2, m2, _ = measure(c, rows, ncalls, args.rotate if rows < 2048 else 1,
-                                max(2, args.steps // 2), 1, x_instance=rows if idx == 3 else 0)
-            u = w2.union_sizes()
-            per_call = m2 / 1e3 / ncalls
-            rec = {"ms_per_step": round(m2, 4), "calls": ncalls, "rows_per_call": rows,
-                   "rows_per_s": round(rows * ncalls / (m2 / 1e3), 1), "us_per_call": round(per_call * 1e6, 3)}
-            if rows < 2048:
-                b = float(np.mean([call_bytes(c, rows, n) for n in u]))
-                rec.update({"bytes_per_call": round(b), "mean_expert_union": round(float(u.mean()), 3),
-                            "GBps": round(b / per_call / 1e9, 1),
-                            "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4)})
-            else:
-                flops = 2.0 * rows * (cfg.K * 3 * cfg.H * cfg.I + 3 * cfg.H * cfg.Is + cfg.E * cfg.H)
-                rec.update({"useful_GFLOP": round(flops / 1e9, 2),
-                            "TFLOPs": round(flops / per_call / 1e12, 2),
-                            "mfma_frac": round(flops / per_call / 1e12 / BF16_PEAK_TFLOPS, 4)})
-            extra[key] = rec
-            del w2
-            torch.cuda.empty_cache()
+        extra.update(run_extra(args, None))
 
     line = {
         "metric": "MoE-layer decode tokens/s and % of HBM roofline (expert bytes read/s)",

@@ -11,7 +11,10 @@ summaries of kernel traces and of HBM traffic counters.
         --copy-fetch DIR --copy-write DIR --key KEY --kernels k1,k2,... --out FILE
         turns two counter runs of a workload and two of the copy kernel into
         HBM bytes per call (each listed kernel once per call) and records them,
-        keyed by KEY and the kernel-source hash, in profiles/traffic.json.
+        keyed by KEY and the kernel-source hash, in profiles/traffic.json;
+    python -m sparse_moe_decode_amd.profiling counters DIR --out FILE --cmd "..."
+        summarizes every counter of a `rocprofv3 --pmc` run: mean per
+        dispatch, by kernel.
 """
 from __future__ import annotations
 
@@ -170,6 +173,35 @@ def cmd_traffic(args) -> int:
     return 0
 
 
+def cmd_counters(args) -> int:
+    files = _find(args.dir, "counter_collection.csv")
+    if not files:
+        print(f"no counter_collection.csv under {args.dir}", file=sys.stderr)
+        return 1
+    names = set()
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                names.add(r["Counter_Name"])
+    names = sorted(names)
+    per = {n: _counter_means(args.dir, n) for n in names}
+    kernels = sorted({k for n in names for k in per[n]})
+    out = [f"# rocprofv3 counters: {args.title}", "", f"command: {args.cmd}", "",
+           "mean value per dispatch", "",
+           "| kernel | dispatches | " + " | ".join(names) + " |",
+           "|---|---|" + "---|" * len(names)]
+    for k in kernels:
+        n_disp = max(per[n].get(k, (0, 0))[1] for n in names)
+        vals = [f"{per[n][k][0]:,.4g}" if k in per[n] else "-" for n in names]
+        out.append(f"| `{k[:80]}` | {n_disp} | " + " | ".join(vals) + " |")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="rocprofv3 helpers")
     sub = ap.add_subparsers(dest="action", required=True)
@@ -191,8 +223,13 @@ def main(argv=None) -> int:
     r.add_argument("--fetch-cmd", default="")
     r.add_argument("--write-cmd", default="")
     r.add_argument("--copy-cmd", default="")
+    k = sub.add_parser("counters")
+    k.add_argument("dir")
+    k.add_argument("--out", default="")
+    k.add_argument("--title", default="")
+    k.add_argument("--cmd", default="")
     args = ap.parse_args(argv)
-    return {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic}[args.action](args)
+    return {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[args.action](args)
 
 
 if __name__ == "__main__":
