@@ -200,6 +200,27 @@ def test_wide_rows_and_large_pair_sets(fmt):
         assert_parity(run_calls(G, x, rows), ref, f"wide {fmt} rows={rows}")
 
 
+def test_maximum_sizes():
+    """The largest H, I and Is the ABI accepts (8192, 4096, 4096) with bf16
+    weights: the streamed gate/up rows, the unstaged down pass (four rows) and
+    the prefill GEMMs at their largest reduction depths."""
+    H, E, K, I, Is = 8192, 4, 2, 4096, 4096
+    _say(f"case: maximum sizes H={H} I={I} Is={Is} E={E} K={K}")
+    rng = np.random.default_rng(4096)
+    a = _random_arrays(rng, H, E, K, I, Is, rstd=0.02, estd=0.01)
+    b = dict(a)
+    for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+        b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    del a
+    x = rng.standard_normal((7, H)).astype(np.float32)
+    L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    ref = _oracle_ref(L, x)
+    for rows in (1, 4, 7):   # decode, few-row (h' read from L2), prefill
+        err = assert_parity(run_calls(G, x, rows), ref, f"maximum sizes rows={rows}")
+        _say(f"rows={rows}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
 def test_given_routing_entry():
     """moe_forward with ids_in/wts_in/gate_in uses the routing as given."""
     _say("case: caller-supplied routing")
