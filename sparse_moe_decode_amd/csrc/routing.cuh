@@ -24,6 +24,14 @@ struct RouteLds {
     SlotTable slots;
 };
 
+// v[l] + v[l ^ 32] on every lane, with one VALU swap of the wave's halves
+// (v_permlane32_swap: each returned register holds one half of each).
+__device__ __forceinline__ int add_halves(int v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] + r[1];
+}
+
 // Order-preserving integer key of a float: a > b iff key(a) > key(b).
 __device__ __forceinline__ uint32_t f32_key(float v)
 {
@@ -149,7 +157,7 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         gt += (o[j].x > v) + (o[j].y > v) + (o[j].z > v) + (o[j].w > v);
-    gt += __shfl_xor(gt, 32);
+    gt = add_halves(gt);
     // exactly K-1 above: the K-th largest; with ties at that value no lane
     // may see K-1, then: fewer than K above and at least K at or above
     unsigned long long hit = __ballot(lane < 32 && gt == K - 1);
@@ -158,7 +166,7 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             ge += (o[j].x >= v) + (o[j].y >= v) + (o[j].z >= v) + (o[j].w >= v);
-        ge += __shfl_xor(ge, 32);
+        ge = add_halves(ge);
         hit = __ballot(lane < 32 && gt < K && ge >= K);
     }
     const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), __builtin_ctzll(hit)));
@@ -189,20 +197,32 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
     }
     if (C <= kWave) {
         // 3. rank by packed key (padding 0 is below every candidate and
-        // shares no key with one)
-        const int C4 = (C + 3) & ~3;
-        if (lane >= C && lane < C4)
+        // shares no key with one); up to 16 candidates (the usual case) are
+        // read in one unrolled batch
+        const int CP = C <= 16 ? 16 : (C + 3) & ~3;
+        if (lane >= C && lane < CP)
             rl.cand_p[q][lane] = 0;
         __builtin_amdgcn_wave_barrier();
         const uint64_t p = rl.cand_p[q][lane];
         const uint32_t pk = static_cast<uint32_t>(p >> 32);
         int rank = 0, tie = 0;
-        for (int j = 0; j < C; j += 4) {
-            const ulonglong2 a = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]);
-            const ulonglong2 b = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]);
+        auto count4 = [&](const ulonglong2 &a, const ulonglong2 &b) {
             rank += (a.x > p) + (a.y > p) + (b.x > p) + (b.y > p);
             tie += (static_cast<uint32_t>(a.x >> 32) == pk) + (static_cast<uint32_t>(a.y >> 32) == pk) +
                    (static_cast<uint32_t>(b.x >> 32) == pk) + (static_cast<uint32_t>(b.y >> 32) == pk);
+        };
+        if (C <= 16) {
+            ulonglong2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][2 * u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                count4(v[2 * u], v[2 * u + 1]);
+        } else {
+            for (int j = 0; j < C; j += 4)
+                count4(*reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]),
+                       *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]));
         }
         const bool live = lane < C;
         if (__ballot(live && rank <= K && tie > 1) == 0) {
