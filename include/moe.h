@@ -17,7 +17,9 @@
  *   - All pointers are raw. "device" means memory of the current HIP device
  *     (hipMalloc or a framework allocator), "host" means ordinary CPU memory.
  *   - The caller owns every buffer; the library never allocates or frees
- *     device memory and keeps no global mutable state.
+ *     device memory and keeps no device state between calls (its only
+ *     global state is a host-side, mutex-guarded cache of occupancy queries
+ *     per kernel and device).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). GPU
  *     work is enqueued on it and the call returns without waiting.
  *   - Arguments are validated on the host before any launch; a failed check
