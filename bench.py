@@ -234,6 +234,29 @@ def run_extra(args, keys):
     return extra
 
 
+def rows_sweep(args):
+    """Throughput of calls of R rows on the 2-bit layer: one decode row, the
+    few-row path up to 4 rows, the grouped prefill path above (the crossover
+    of the two). Calls take consecutive rows of one 2048-row stream."""
+    cfg = mi.CONFIGS[3].with_(rows_per_call=1)
+    total = 2048
+    print("[bench] rows sweep", file=sys.stderr, flush=True)
+    wl = Workload(cfg, 1, total, 1)
+    out = {}
+    for R in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64, 256, 2048):
+        wl.R = R
+        wl.ncalls = max(1, min(total // R, 256))
+        wl.ws = wl.layers[0].workspace(R)
+        wl.capture()
+        ms, _ = time_steps(wl, max(2, args.steps // 2), 1)
+        per_call = ms / 1e3 / wl.ncalls
+        # the library's choice for this layer (4-row launches fit its shapes)
+        out[str(R)] = {"path": "decode" if R == 1 else ("few-row" if R <= 32 else "prefill"),
+                       "calls": wl.ncalls, "us_per_call": round(per_call * 1e6, 3),
+                       "rows_per_s": round(R / per_call, 1)}
+    return {"workload": "rows_sweep", "config": cfg.name, "rows": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +268,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
     ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2"],
                     help="run just this one of the other workloads (for profiling); prints its record")
+    ap.add_argument("--rows-sweep", action="store_true",
+                    help="rows per call from 1 to 2048 on the 2-bit layer (decode, few-row, prefill paths); "
+                         "prints one record of rows/s per call size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -258,6 +284,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.rows_sweep:
+        print(json.dumps(rows_sweep(args)), flush=True)
+        return
     if args.only:
         extra = run_extra(args, [args.only])
         print(json.dumps({"workload": args.only, **extra[args.only]}), flush=True)

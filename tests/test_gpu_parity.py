@@ -139,8 +139,9 @@ def test_edge_shapes(case):
     L = oracle_layer_from_arrays(a, renormalize=renorm)
     G = gpu_layer_from_arrays(a, renormalize=renorm)
     ref = _oracle_ref(L, x)
-    for rows in (1, 3, 4, T):   # decode, few-row, few-row, prefill (one call)
+    for rows in (1, 3, 4, T):   # decode, few-row, few-row, T rows in one call
         assert_parity(run_calls(G, x, rows), ref, f"{case} rows={rows}")
+    assert_parity(run_calls(G, x, T, force_path="prefill"), ref, f"{case} prefill")
 
 
 def test_bf16_and_q2_small_shapes():
@@ -157,6 +158,7 @@ def test_bf16_and_q2_small_shapes():
     ref = _oracle_ref(L, x)
     for rows in (1, 2, 4, 11):
         assert_parity(run_calls(G, x, rows), ref, f"bf16 rows={rows}")
+    assert_parity(run_calls(G, x, 11, force_path="prefill"), ref, "bf16 prefill")
     _say("case: small 2-bit experts")
     import oracle
     q = dict(b)
@@ -169,6 +171,7 @@ def test_bf16_and_q2_small_shapes():
     ref = _oracle_ref(Lq, x)
     for rows in (1, 3, 11):
         assert_parity(run_calls(Gq, x, rows), ref, f"q2 rows={rows}")
+    assert_parity(run_calls(Gq, x, 11, force_path="prefill"), ref, "q2 prefill")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "q2"])
@@ -216,9 +219,34 @@ def test_maximum_sizes():
     L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
     G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
     ref = _oracle_ref(L, x)
-    for rows in (1, 4, 7):   # decode, few-row (h' read from L2), prefill
-        err = assert_parity(run_calls(G, x, rows), ref, f"maximum sizes rows={rows}")
+    for rows, path in ((1, None), (4, None), (7, "prefill")):   # decode, few-row (h' read from L2), prefill
+        err = assert_parity(run_calls(G, x, rows, force_path=path), ref, f"maximum sizes rows={rows}")
         _say(f"rows={rows}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
+def test_cache_aware_routing_bias():
+    """The opt-in cache-aware routing variant: logits z + lambda * Delta *
+    cached_e (Research notes page, section 4, the cache-aware routing row),
+    given to the layer as its per-expert router bias. Parity with the oracle,
+    and the bias moves selections toward the cached experts."""
+    _say("case: cache-aware routing bias")
+    rng = np.random.default_rng(2412)
+    a = _random_arrays(rng, 256, 64, 6, 64, 64, rstd=0.1)
+    cached = (rng.random(64) < 0.25).astype(np.float32)
+    x = rng.standard_normal((24, 256)).astype(np.float32)
+    base = _oracle_ref(oracle_layer_from_arrays(a), x)
+    hits0 = cached[base[0]].sum()
+    for lam_delta in (0.25, 1.0):
+        b = dict(a, router_bias=(lam_delta * cached).astype(np.float32))
+        L = oracle_layer_from_arrays(b)
+        G = gpu_layer_from_arrays(b)
+        ref = _oracle_ref(L, x)
+        for rows in (1, 3, 24):
+            assert_parity(run_calls(G, x, rows), ref, f"cache bias {lam_delta} rows={rows}")
+        hits = cached[ref[0]].sum()
+        assert hits >= hits0, (lam_delta, hits, hits0)
+        hits0 = hits
+    assert hits0 > cached[base[0]].sum()
 
 
 def test_given_routing_entry():
@@ -275,7 +303,7 @@ def test_prefill_small(fmt, T):
         L = oracle_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
         G = gpu_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
     ref = _oracle_ref(L, x)
-    assert_parity(run_calls(G, x, T), ref, f"prefill {fmt} T={T}")
+    assert_parity(run_calls(G, x, T, force_path="prefill"), ref, f"prefill {fmt} T={T}")
 
 
 def test_prefill_forced_on_small_calls():
