@@ -212,8 +212,11 @@ def run_extra(args, keys):
             continue
         c = mi.CONFIGS[idx].with_(rows_per_call=rows)
         print(f"[bench] {key}", file=sys.stderr, flush=True)
+        # one prefill call is about a millisecond: time more of them, after a
+        # longer warm-up, so that clock ramp-up does not show in the figure
+        steps, warm = (max(2, args.steps // 2), 1) if rows < 2048 else (max(20, args.steps), 5)
         w2, m2, _ = measure(c, rows, ncalls, args.rotate if rows < 2048 else 1,
-                            max(2, args.steps // 2), 1, x_instance=rows if idx == 3 else 0)
+                            steps, warm, x_instance=rows if idx == 3 else 0)
         u = w2.union_sizes()
         per_call = m2 / 1e3 / ncalls
         rec = {"ms_per_step": round(m2, 4), "calls": ncalls, "rows_per_call": rows,

@@ -96,7 +96,7 @@ constexpr int kLmLD = 33;   // LDS row stride in doubles
 template <typename RT>
 __global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, int E, const uint8_t *router_w,
                                                   const uint8_t *gate_w, const float *bias, double *logits,
-                                                  double *z)
+                                                  double *z, double *part)
 {
     __shared__ double Lx[2][kLmT][kLmLD];
     __shared__ double Lw[2][kLmE][kLmLD];
@@ -140,13 +140,15 @@ __global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, 
     for (int c = 0; c < 2; ++c)
         acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
     const int li = lane & 15, lk = lane >> 4;
-    fetch(0);
+    // reduction slice of this workgroup (split K: blockIdx.z of gridDim.z)
+    const int nk = H / kLmK, ks = gridDim.z;
+    const int kb0 = static_cast<int>(blockIdx.z) * nk / ks, kb1 = (static_cast<int>(blockIdx.z) + 1) * nk / ks;
+    fetch(kb0 * kLmK);
     stage(0);
     __syncthreads();
-    const int nk = H / kLmK;
-    for (int kb = 0; kb < nk; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nk)
+    for (int kb = kb0; kb < kb1; ++kb) {
+        const int buf = (kb - kb0) & 1;
+        if (kb + 1 < kb1)
             fetch((kb + 1) * kLmK);
 #pragma unroll
         for (int ks = 0; ks < kLmK / 4; ++ks) {
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, 
                 acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
             }
         }
-        if (kb + 1 < nk)
+        if (kb + 1 < kb1)
             stage(buf ^ 1);
         __syncthreads();
     }
@@ -171,12 +173,43 @@ __global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, 
             const int tt = t0 + wave * 16 + lk + 4 * i;
             if (tt >= T)
                 continue;
-            if (ee < E)
+            if (ks > 1) {
+                // partial over this slice; k_logits_sum adds the slices in order
+                if (ee <= E)
+                    part[(static_cast<size_t>(blockIdx.z) * T + tt) * (E + 1) + ee] = acc[c][i];
+            } else if (ee < E) {
                 logits[static_cast<size_t>(tt) * E + ee] = acc[c][i] + (bias ? static_cast<double>(bias[ee]) : 0.0);
-            else if (ee == E)
+            } else if (ee == E) {
                 z[tt] = acc[c][i];
+            }
         }
     }
+}
+
+// Split-K logits: the sum of the slices' partials in slice order, then the bias.
+__global__ void __launch_bounds__(256) k_logits_sum(const double *part, int ks, int T, int E, const float *bias,
+                                                    double *logits, double *z)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(T) * (E + 1);
+    if (i >= n)
+        return;
+    const int t = static_cast<int>(i / (E + 1)), e = static_cast<int>(i - static_cast<int64_t>(t) * (E + 1));
+    // slices in order, their loads issued eight at a time
+    double s = 0.0;
+    for (int k0 = 0; k0 < ks; k0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = k0 + u < ks ? part[static_cast<size_t>(k0 + u) * n + i] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            s += v[u];
+    }
+    if (e < E)
+        logits[static_cast<size_t>(t) * E + e] = s + (bias ? static_cast<double>(bias[e]) : 0.0);
+    else
+        z[t] = s;
 }
 
 // ============================================================ selection
@@ -298,6 +331,8 @@ struct GemmArgs {
     uint16_t *hh, *hl;         // dual: h hi/lo [rows][N]
     float *hsum;               // dual, optional: block sums of h [rows][N/32]
     float *out;                // single: [rows][N]
+    float *kpart;              // split K (dense, non-routed; gridDim.z slices): fp32 partial sums,
+                               // dual [z][rows][2][N] (gate, up), single [z][rows][N]
 };
 
 // 8 fp32 -> bf16 hi and lo = bf16(v - hi), packed as the MFMA operand.
@@ -514,10 +549,14 @@ __global__ void __launch_bounds__(256) k_ggemm(GemmArgs p)
         for (int ct = 0; ct < S::CT; ++ct)
             acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nsteps = p.Kd / 32;
+    // reduction slice (split K over gridDim.z)
+    const int nsteps_all = p.Kd / 32, ks = gridDim.z;
+    const int s_begin = static_cast<int>(blockIdx.z) * nsteps_all / ks;
+    const int nsteps = (static_cast<int>(blockIdx.z) + 1) * nsteps_all / ks - s_begin;
     uint4 rah = make_uint4(0, 0, 0, 0), ral = rah;
     BStage<W> rb;
     auto load_step = [&](int s) {
+        s += s_begin;
         if (a_loader && asrc >= 0) {
             const size_t idx = (static_cast<size_t>(asrc) * p.Kd + s * 32 + apart * 8) / 8;
             rah = reinterpret_cast<const uint4 *>(p.ah)[idx];
@@ -561,7 +600,86 @@ __global__ void __launch_bounds__(256) k_ggemm(GemmArgs p)
         }
         __syncthreads();
     }
+    if (ks > 1) {
+        // partial sums of this slice; k_dual_sum / k_single_sum finish them
+        const size_t zr = static_cast<size_t>(blockIdx.z) * p.T;
+#pragma unroll
+        for (int rt = 0; rt < S::RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < S::CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wr * S::TR + rt * 16 + 4 * kq + i;
+                    if (r >= nrows)
+                        continue;
+                    const size_t row = zr + r0 + r;
+                    if (DUAL) {
+                        constexpr int chunk = kGN / (2 * S::WC);
+                        const int half = ct / (S::CT / 2), cc = ct % (S::CT / 2);
+                        const int ch = n0 + wc * chunk + cc * 16 + li;
+                        if (ch < p.N)
+                            p.kpart[(row * 2 + half) * p.N + ch] = acc[rt][ct][i];
+                    } else {
+                        const int col = n0 + wc * S::TC + ct * 16 + li;
+                        if (col < p.N)
+                            p.kpart[row * p.N + col] = acc[rt][ct][i];
+                    }
+                }
+        return;
+    }
     gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
+}
+
+// Split-K finish of the dense dual GEMM (non-routed rows, weight 1): the
+// slices' gate and up sums in slice order (loads issued eight slices at a
+// time), then the SwiGLU and bf16 hi/lo split of gemm_epilogue.
+__global__ void __launch_bounds__(256) k_dual_sum(const float *part, int ks, int T, int N, uint16_t *hh,
+                                                  uint16_t *hl)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // row * N + ch
+    if (i >= static_cast<int64_t>(T) * N)
+        return;
+    const int64_t t = i / N, ch = i - t * N;
+    float g = 0.0f, u = 0.0f;
+    for (int z0 = 0; z0 < ks; z0 += 8) {
+        float vg[8], vu[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const size_t row = static_cast<size_t>(z0 + k) * T + t;
+            const bool ok = z0 + k < ks;
+            vg[k] = ok ? part[(row * 2 + 0) * N + ch] : 0.0f;
+            vu[k] = ok ? part[(row * 2 + 1) * N + ch] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            g += vg[k];
+            u += vu[k];
+        }
+    }
+    const float h = silu_mul(g, u) * 1.0f;
+    const uint32_t hb = bf16_rne_bits(h);
+    hh[i] = static_cast<uint16_t>(hb);
+    hl[i] = static_cast<uint16_t>(bf16_rne_bits(h - __uint_as_float(hb << 16)));
+}
+
+// Split-K finish of the dense single GEMM: the slices' sums in slice order.
+__global__ void __launch_bounds__(256) k_single_sum(const float *part, int ks, int T, int N, float *out)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(T) * N;
+    if (i >= n)
+        return;
+    float s = 0.0f;
+    for (int z0 = 0; z0 < ks; z0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = z0 + k < ks ? part[static_cast<size_t>(z0 + k) * n + i] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            s += v[k];
+    }
+    out[i] = s;
 }
 
 // 2-bit main loop. B arrives in mega-steps of 8 blocks: 8 consecutive lanes
@@ -802,11 +920,57 @@ __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const 
 
 // ============================================================ workspace
 
+// Reduction slices of the fp64 router GEMM: up to about 1024 workgroups
+// when there are few rows; two slices once the tiles alone fill the chip
+// (measured on the 2048-row chunk: 140 -> 123 us plus 7 us for the sum).
+static int logit_splits(const moe_layer_desc *d, int T)
+{
+    const int base = ((d->n_experts + 1 + kLmE - 1) / kLmE) * ((T + kLmT - 1) / kLmT);
+    const int nk = d->hidden / kLmK;
+    if (base >= 512)
+        return nk >= 2 ? 2 : 1;
+    int ks = 1;
+    while (base * ks * 2 <= 1024 && ks * 2 <= nk)
+        ks *= 2;
+    return ks;
+}
+
+// Reduction slices of a dense (shared-expert) GEMM with `blocks` output
+// workgroups and Kd-deep rows: up to about 512 workgroups in all, at least
+// one 32-deep step per slice.
+static int dense_splits(int blocks, int Kd)
+{
+    int ks = 1;
+    while (blocks * ks * 2 <= 512 && ks * 2 <= Kd / 32 && ks < 64)
+        ks *= 2;
+    return ks;
+}
+static int shared_gu_splits(const moe_layer_desc *d, int T)
+{
+    return dense_splits(((d->shared_inter + kGN / 2 - 1) / (kGN / 2)) * ((T + 63) / 64), d->hidden);
+}
+static int shared_dn_splits(const moe_layer_desc *d, int T)
+{
+    // the down GEMM gains from slices only while it has few workgroups
+    // (measured: at 256 workgroups two slices plus their sum were slower)
+    const int blocks = ((d->hidden + kGN - 1) / kGN) * ((T + 63) / 64);
+    return blocks < 128 ? dense_splits(blocks, d->shared_inter) : 1;
+}
+static size_t shared_kpart_bytes(const moe_layer_desc *d, int T)
+{
+    const int a = shared_gu_splits(d, T), b = shared_dn_splits(d, T);
+    const size_t gu = a > 1 ? sizeof(float) * a * static_cast<size_t>(T) * 2 * d->shared_inter : 0;
+    const size_t dn = b > 1 ? sizeof(float) * b * static_cast<size_t>(T) * d->hidden : 0;
+    return gu > dn ? gu : dn;
+}
+
 struct PrefillWs {
     uint8_t *sort_ws;
     size_t sort_bytes;
     uint4 *xh, *xl;
     double *logits, *z;
+    double *lpart;                   // split-K partial logits [ks][T][E+1] (empty when ks == 1)
+    float *kpart;                    // split-K partial sums of the shared expert's GEMMs
     int32_t *ids;
     float *wts, *gate;
     int32_t *counts, *offsets, *perm, *inv, *tile_off;
@@ -833,6 +997,7 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.xl = reinterpret_cast<uint4 *>(take(sizeof(uint16_t) * T * H));
     w.logits = reinterpret_cast<double *>(take(sizeof(double) * T * E));
     w.z = reinterpret_cast<double *>(take(sizeof(double) * T));
+    w.lpart = reinterpret_cast<double *>(take(sizeof(double) * logit_splits(d, T) * T * (E + 1) * (logit_splits(d, T) > 1)));
     w.ids = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.wts = reinterpret_cast<float *>(take(sizeof(float) * P));
     w.gate = reinterpret_cast<float *>(take(sizeof(float) * T));
@@ -849,6 +1014,7 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.hsum = reinterpret_cast<float *>(take(sizeof(float) * P * (I / 32)));
     w.rout = reinterpret_cast<float *>(take(sizeof(float) * P * H));
     w.sout = reinterpret_cast<float *>(take(sizeof(float) * T * H));
+    w.kpart = reinterpret_cast<float *>(take(shared_kpart_bytes(d, T)));
     w.sort_bytes = off;   // total, when not carving
     return w;
 }
@@ -863,9 +1029,9 @@ size_t prefill_ws_bytes(const moe_layer_desc *d, int T)
 static int routed_bm(int64_t P, int E) { return P < 48 * static_cast<int64_t>(E) ? 32 : 64; }
 
 template <typename W, bool DUAL>
-static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s)
+static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s, int ks = 1)
 {
-    const dim3 grid((g.N + (DUAL ? kGN / 2 : kGN) - 1) / (DUAL ? kGN / 2 : kGN), tiles), block(256);
+    const dim3 grid((g.N + (DUAL ? kGN / 2 : kGN) - 1) / (DUAL ? kGN / 2 : kGN), tiles, ks), block(256);
     if constexpr (W::kChunk == 32) {
         if (bm == 32)
             hipLaunchKernelGGL((k_ggemm_q2<DUAL, 32>), grid, block, 0, s, g);
@@ -922,7 +1088,14 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sg.hh = w.shh;
     sg.hl = w.shl;
     sg.hsum = nullptr;
-    launch_ggemm<ST, true>(sg, 64, sh_tiles, s);
+    sg.kpart = w.kpart;
+    const int gks = shared_gu_splits(d, T);
+    launch_ggemm<ST, true>(sg, 64, sh_tiles, s, gks);
+    if (gks > 1) {
+        const int64_t n = static_cast<int64_t>(T) * Is;
+        hipLaunchKernelGGL(k_dual_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart, gks, T,
+                           Is, w.shh, w.shl);
+    }
     // routed down: A = h of the pairs (sorted order)
     GemmArgs dg = g;
     dg.ah = w.hh;
@@ -949,7 +1122,14 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sd.bstride = 0;
     sd.Kd = Is;
     sd.out = w.sout;
-    launch_ggemm<ST, false>(sd, 64, sh_tiles, s);
+    sd.kpart = w.kpart;
+    const int dks = shared_dn_splits(d, T);
+    launch_ggemm<ST, false>(sd, 64, sh_tiles, s, dks);
+    if (dks > 1) {
+        const int64_t n = static_cast<int64_t>(T) * H;
+        hipLaunchKernelGGL(k_single_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart, dks,
+                           T, H, w.sout);
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -959,15 +1139,21 @@ static int prefill_route(const moe_layer_desc *d, const float *x, int T, const P
                          float *wts_out, float *gate_out, hipStream_t s)
 {
     const int H = d->hidden, E = d->n_experts, K = d->top_k;
-    const dim3 lg((E + 1 + kLmE - 1) / kLmE, (T + kLmT - 1) / kLmT);
+    const int ks = logit_splits(d, T);
+    const dim3 lg((E + 1 + kLmE - 1) / kLmE, (T + kLmT - 1) / kLmT, ks);
     if (d->router_t == MOE_F32)
         hipLaunchKernelGGL((k_logits64<F32>), lg, dim3(256), 0, s, x, T, H, E,
                            static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, w.logits, w.z);
+                           d->router_bias, w.logits, w.z, w.lpart);
     else
         hipLaunchKernelGGL((k_logits64<BF16>), lg, dim3(256), 0, s, x, T, H, E,
                            static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, w.logits, w.z);
+                           d->router_bias, w.logits, w.z, w.lpart);
+    if (ks > 1) {
+        const int64_t n = static_cast<int64_t>(T) * (E + 1);
+        hipLaunchKernelGGL(k_logits_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.lpart, ks, T,
+                           E, d->router_bias, w.logits, w.z);
+    }
     hipLaunchKernelGGL(k_select_rows, dim3((T + 3) / 4), dim3(256), 0, s, w.logits, w.z, T, E, K, d->renormalize,
                        w.ids, w.wts, w.gate, ids_out, wts_out, gate_out);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
