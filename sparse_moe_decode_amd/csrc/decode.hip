@@ -140,11 +140,132 @@ struct RouteArgs {
 
 constexpr int kRouteThreads = 256;   // threads of every workgroup that routes
 
-// Routing of the call's R rows inside one workgroup of kRouteThreads: wave
-// q selects row q from the logits (staged in `lg`, R rows of (E+1)&~1
-// doubles), or the caller's selection is taken as given (ids outside [0, E)
-// become expert 0 with weight 0); then wave 0 builds the slot table. Ends
-// with a workgroup barrier, after which `lg` may be reused.
+static_assert(kRouteThreads == 4 * kWave, "one-row routing compacts four waves' candidates");
+
+// One row routed by the whole workgroup: thread i holds experts i + 256 j
+// (j < PT). The maxima of the fp32 keys over groups of 8 lanes (32 groups)
+// give the threshold (kth_of_32: at or below the K-th largest logit), each
+// wave compacts its own candidates, and wave 0 ranks them (rank_packed) while
+// wave 1 evaluates the gate and writes the fixed part of the slot table. More
+// than 64 candidates (massive ties) fall back to wave_route on the staged
+// logits; keys shared near the boundary to exact fp64 ranking.
+template <int PT>
+__device__ __forceinline__ void route_block1(const RouteArgs &a, double *lg, RouteLds &rl)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int E = a.E, K = a.K;
+    double v[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int e = tid + j * kRouteThreads;
+        v[j] = e < E ? a.logits[e] : 0.0;
+    }
+    const double z = a.zlogit[0];
+    uint32_t key[PT], mk = 0;   // 0 is below every key of a non-NaN value
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int e = tid + j * kRouteThreads;
+        if (e < E)
+            lg[e] = v[j];   // staged for the fallbacks and the softmax over all E
+        key[j] = e < E ? f32_key(static_cast<float>(v[j])) : 0u;
+        mk = key[j] > mk ? key[j] : mk;
+    }
+    // maximum over 8 lanes: quad permutations [1,0,3,2] and [2,3,0,1], then
+    // the mirror within each half row
+    uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mk), 0xB1, 0xF, 0xF, false));
+    mk = o > mk ? o : mk;
+    o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mk), 0x4E, 0xF, 0xF, false));
+    mk = o > mk ? o : mk;
+    o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mk), 0x141, 0xF, 0xF, false));
+    mk = o > mk ? o : mk;
+    if ((lane & 7) == 0)
+        rl.pmax[0][wave * 8 + (lane >> 3)] = mk;
+    __syncthreads();
+    const uint32_t t = kth_of_32(rl.pmax[0], K, lane);
+    // compaction within the wave: exclusive prefix of the per-lane counts
+    bool c[PT];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        c[j] = (key[j] >= t) & (key[j] != 0);
+        cnt += c[j];
+    }
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int pos = 0, Cw = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= PT; ++b) {
+        const unsigned long long mb = __ballot((cnt >> b) & 1);
+        pos += __popcll(mb & lt) << b;
+        Cw += __popcll(mb) << b;
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        if (c[j] && pos < kWave) {
+            const int e = tid + j * kRouteThreads;
+            rl.seg_p[wave][pos] = (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(~e);
+        }
+        pos += c[j];
+    }
+    if (lane == 0)
+        rl.seg_n[wave] = Cw;
+    __syncthreads();
+    const int4 n = *reinterpret_cast<const int4 *>(rl.seg_n);
+    const int C = n.x + n.y + n.z + n.w;
+    if (wave == 0) {
+        if (C <= kWave) {
+            // lane l takes candidate l of the concatenated segments
+            const int o1 = n.x, o2 = o1 + n.y, o3 = o2 + n.z;
+            const int sw = (lane >= o1) + (lane >= o2) + (lane >= o3);
+            const int si = lane - (sw == 0 ? 0 : sw == 1 ? o1 : sw == 2 ? o2 : o3);
+            uint64_t p = 0;
+            double val = 0.0;
+            if (lane < C) {
+                p = rl.seg_p[sw][si];
+                val = lg[~static_cast<uint32_t>(p)];
+                rl.cand_p[0][lane] = p;
+            }
+            if (!rank_packed(C, K, a.renorm, E, lg, z, false, 0, rl, lane, [&](uint64_t) { return val; },
+                             &rl.slots)) {
+                if (lane < C) {
+                    rl.cand[0][lane] = static_cast<int>(~static_cast<uint32_t>(p));
+                    rl.cand_v[0][lane] = val;
+                }
+                rank_exact(C, K, 0, rl, lane);
+                wave_weights(lg, E, K, a.renorm, z, 0, rl, lane, false);
+                if (lane < K) {
+                    rl.slots.expert[lane + 1] = rl.sel_e[0][lane];
+                    rl.slots.w[lane + 1][0] = rl.sel_w[0][lane];
+                }
+            }
+        } else {
+            wave_route(lg, E, K, a.renorm, z, 0, rl, lane);
+            build_slots<1>(rl, K, lane);
+        }
+    } else if (wave == 1 && C <= kWave) {
+        // the gate and the slots' fixed part (slot 0 = shared expert)
+        if (lane == 0) {
+            const float g = 1.0f / (1.0f + expf(static_cast<float>(-z)));
+            rl.g[0] = g;
+            rl.slots.w[0][0] = g;
+            rl.slots.expert[0] = -1;
+            rl.slots.nslots = K + 1;
+            rl.slots.pstart[K + 1] = K + 1;
+        }
+        if (lane <= K) {
+            rl.slots.rmask[lane] = 1u;
+            rl.slots.pstart[lane] = lane;
+        }
+    }
+    __syncthreads();
+}
+
+// Routing of the call's R rows inside one workgroup of kRouteThreads: one
+// row by the whole workgroup (route_block1), or wave q selects row q from the
+// logits (staged in `lg`, R rows of (E+1)&~1 doubles) and wave 0 then builds
+// the slot table; or the caller's selection is taken as given (ids outside
+// [0, E) become expert 0 with weight 0). Ends with a workgroup barrier, after
+// which `lg` may be reused.
 template <int R>
 __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
 {
@@ -160,6 +281,14 @@ __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, Rout
         }
         if (tid < R)
             rl.g[tid] = a.gate_in[tid];
+    } else if (R == 1) {
+        if (a.E <= kRouteThreads)
+            route_block1<1>(a, lg, rl);
+        else if (a.E <= 2 * kRouteThreads)
+            route_block1<2>(a, lg, rl);
+        else
+            route_block1<kMaxE / kRouteThreads>(a, lg, rl);
+        return;   // ends with a workgroup barrier
     } else {
         // every load is issued before the first LDS store
         constexpr int PT = kMaxE / kRouteThreads;

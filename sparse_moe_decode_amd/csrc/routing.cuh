@@ -20,6 +20,10 @@ struct RouteLds {
     alignas(16) double cand_v[kMaxRows][kWave];
     alignas(16) uint64_t cand_p[kMaxRows][kWave];
     alignas(16) uint32_t pmax[kMaxRows][kWave / 2];
+    // one row routed by a whole workgroup of 4 waves: each wave's candidates
+    // (packed as in cand_p) and their counts
+    alignas(16) uint64_t seg_p[4][kWave];
+    alignas(16) int seg_n[4];
     float g[kMaxRows];
     SlotTable slots;
 };
@@ -81,7 +85,7 @@ __device__ __forceinline__ void rank_exact(int C, int K, int q, RouteLds &rl, in
 // evaluates exp(l_k - l_0), lane K evaluates exp(-z), in one pass; sums are
 // wave reductions in a fixed order.
 __device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
-                                             int lane)
+                                             int lane, bool gate = true)
 {
     __builtin_amdgcn_wave_barrier();
     const double l0 = rl.sel_l[q][0];
@@ -103,9 +107,115 @@ __device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int
     const float r = (lane < K ? v : 1.0f) / (lane < K ? denom : 1.0f + v);
     if (lane < K)
         rl.sel_w[q][lane] = r;
-    if (lane == K)
+    if (gate && lane == K)
         rl.g[q] = r;
     __builtin_amdgcn_wave_barrier();
+}
+
+// The K-th largest of 32 keys gm[0..32) (LDS), or, if it is tied, a value
+// with fewer than K keys above it and at least K at or above: lane l counts
+// the keys above key l%32 in half l/32 of the array; the halves are added.
+__device__ __forceinline__ uint32_t kth_of_32(const uint32_t *gm, int K, int lane)
+{
+    const uint32_t v = gm[lane & 31];
+    const uint32_t *half = gm + 16 * (lane >> 5);
+    uint4 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = *reinterpret_cast<const uint4 *>(half + 4 * j);
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        gt += (o[j].x > v) + (o[j].y > v) + (o[j].z > v) + (o[j].w > v);
+    gt = add_halves(gt);
+    // exactly K-1 above: the K-th largest; with ties at that value no lane
+    // may see K-1, then: fewer than K above and at least K at or above
+    unsigned long long hit = __ballot(lane < 32 && gt == K - 1);
+    if (hit == 0) {
+        int ge = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ge += (o[j].x >= v) + (o[j].y >= v) + (o[j].z >= v) + (o[j].w >= v);
+        ge = add_halves(ge);
+        hit = __ballot(lane < 32 && gt < K && ge >= K);
+    }
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), __builtin_ctzll(hit)));
+}
+
+// Ranking of the C <= 64 candidates of row q compacted in rl.cand_p[q][0..C)
+// as packed (fp32 key, ~id) words; value(p) gives the fp64 logit of the
+// lane's candidate p. Distinct keys order their values exactly: unless one of
+// the first K+1 shares its key with another candidate, the selection, its
+// weights (as in wave_weights) and, if `gate`, the gate are written (and the
+// routed slots 1..K of `st`, if given) and true is returned; else nothing is
+// written and the candidates need exact fp64 ranking.
+template <typename ValueOf>
+__device__ __forceinline__ bool rank_packed(int C, int K, int renorm, int E, const double *lg, double z, bool gate,
+                                            int q, RouteLds &rl, int lane, ValueOf value, SlotTable *st)
+{
+    // padding 0 is below every candidate and shares no key with one; up to
+    // 16 candidates (the usual case) are read in one unrolled batch
+    const int CP = C <= 16 ? 16 : (C + 3) & ~3;
+    if (lane >= C && lane < CP)
+        rl.cand_p[q][lane] = 0;
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t p = rl.cand_p[q][lane];
+    const uint32_t pk = static_cast<uint32_t>(p >> 32);
+    int rank = 0, tie = 0;
+    auto count4 = [&](const ulonglong2 &a, const ulonglong2 &b) {
+        rank += (a.x > p) + (a.y > p) + (b.x > p) + (b.y > p);
+        tie += (static_cast<uint32_t>(a.x >> 32) == pk) + (static_cast<uint32_t>(a.y >> 32) == pk) +
+               (static_cast<uint32_t>(b.x >> 32) == pk) + (static_cast<uint32_t>(b.y >> 32) == pk);
+    };
+    if (C <= 16) {
+        ulonglong2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][2 * u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            count4(v[2 * u], v[2 * u + 1]);
+    } else {
+        for (int j = 0; j < C; j += 4)
+            count4(*reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]),
+                   *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]));
+    }
+    const bool live = lane < C;
+    if (__ballot(live && rank <= K && tie > 1) != 0)
+        return false;
+    const int e = static_cast<int>(~static_cast<uint32_t>(p));
+    const double val = live ? value(p) : 0.0;
+    // l_0: the value of the candidate ranked first
+    const int r0 = __builtin_ctzll(__ballot(live && rank == 0));
+    const long long vb = __double_as_longlong(val);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(vb & 0xffffffff), r0);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(vb >> 32), r0);
+    const double l0 = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+    const bool sel = live && rank < K;
+    const float ex = sel ? expf(static_cast<float>(val - l0)) : 0.0f;
+    float denom;
+    if (renorm) {
+        denom = wave_sum(ex);
+    } else {
+        float sum = 0.0f;
+        for (int e2 = lane; e2 < E; e2 += kWave)
+            sum += expf(static_cast<float>(lg[e2] - l0));
+        denom = wave_sum(sum);
+    }
+    if (sel) {
+        const float w = ex / denom;
+        rl.sel_e[q][rank] = e;
+        rl.sel_l[q][rank] = val;
+        rl.sel_w[q][rank] = w;
+        if (st) {
+            st->expert[rank + 1] = e;
+            st->w[rank + 1][0] = w;
+        }
+    }
+    if (gate && lane == 0)
+        rl.g[q] = 1.0f / (1.0f + expf(static_cast<float>(-z)));
+    __builtin_amdgcn_wave_barrier();
+    return true;
 }
 
 // Routing of one row of E logits (double, in LDS) by one wave: the top K
@@ -146,30 +256,7 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
     if ((lane & 1) == 0)
         rl.pmax[q][lane >> 1] = pm;
     __builtin_amdgcn_wave_barrier();
-    // lane l counts the pair maxima above pair maximum l%32 in half l/32
-    const uint32_t v = rl.pmax[q][lane & 31];
-    const uint32_t *half = &rl.pmax[q][16 * (lane >> 5)];
-    uint4 o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        o[j] = *reinterpret_cast<const uint4 *>(half + 4 * j);
-    int gt = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        gt += (o[j].x > v) + (o[j].y > v) + (o[j].z > v) + (o[j].w > v);
-    gt = add_halves(gt);
-    // exactly K-1 above: the K-th largest; with ties at that value no lane
-    // may see K-1, then: fewer than K above and at least K at or above
-    unsigned long long hit = __ballot(lane < 32 && gt == K - 1);
-    if (hit == 0) {
-        int ge = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ge += (o[j].x >= v) + (o[j].y >= v) + (o[j].z >= v) + (o[j].w >= v);
-        ge = add_halves(ge);
-        hit = __ballot(lane < 32 && gt < K && ge >= K);
-    }
-    const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), __builtin_ctzll(hit)));
+    const uint32_t t = kth_of_32(rl.pmax[q], K, lane);
 
     // 2. compaction: exclusive prefix of the per-lane counts from ballots of
     // their bits
@@ -196,67 +283,12 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
         pos += c;
     }
     if (C <= kWave) {
-        // 3. rank by packed key (padding 0 is below every candidate and
-        // shares no key with one); up to 16 candidates (the usual case) are
-        // read in one unrolled batch
-        const int CP = C <= 16 ? 16 : (C + 3) & ~3;
-        if (lane >= C && lane < CP)
-            rl.cand_p[q][lane] = 0;
-        __builtin_amdgcn_wave_barrier();
-        const uint64_t p = rl.cand_p[q][lane];
-        const uint32_t pk = static_cast<uint32_t>(p >> 32);
-        int rank = 0, tie = 0;
-        auto count4 = [&](const ulonglong2 &a, const ulonglong2 &b) {
-            rank += (a.x > p) + (a.y > p) + (b.x > p) + (b.y > p);
-            tie += (static_cast<uint32_t>(a.x >> 32) == pk) + (static_cast<uint32_t>(a.y >> 32) == pk) +
-                   (static_cast<uint32_t>(b.x >> 32) == pk) + (static_cast<uint32_t>(b.y >> 32) == pk);
-        };
-        if (C <= 16) {
-            ulonglong2 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][2 * u]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                count4(v[2 * u], v[2 * u + 1]);
-        } else {
-            for (int j = 0; j < C; j += 4)
-                count4(*reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j]),
-                       *reinterpret_cast<const ulonglong2 *>(&rl.cand_p[q][j + 2]));
-        }
-        const bool live = lane < C;
-        if (__ballot(live && rank <= K && tie > 1) == 0) {
-            const int e = static_cast<int>(~static_cast<uint32_t>(p));
-            const double val = live ? lg[e] : 0.0;
-            // l_0: the value of the candidate ranked first
-            const int r0 = __builtin_ctzll(__ballot(live && rank == 0));
-            const long long vb = __double_as_longlong(val);
-            const int lo = __builtin_amdgcn_readlane(static_cast<int>(vb & 0xffffffff), r0);
-            const int hi = __builtin_amdgcn_readlane(static_cast<int>(vb >> 32), r0);
-            const double l0 = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
-            const bool sel = live && rank < K;
-            const float ex = sel ? expf(static_cast<float>(val - l0)) : 0.0f;
-            float denom;
-            if (renorm) {
-                denom = wave_sum(ex);
-            } else {
-                float sum = 0.0f;
-                for (int e2 = lane; e2 < E; e2 += kWave)
-                    sum += expf(static_cast<float>(lg[e2] - l0));
-                denom = wave_sum(sum);
-            }
-            if (sel) {
-                rl.sel_e[q][rank] = e;
-                rl.sel_l[q][rank] = val;
-                rl.sel_w[q][rank] = ex / denom;
-            }
-            if (lane == 0)
-                rl.g[q] = 1.0f / (1.0f + expf(static_cast<float>(-z)));
-            __builtin_amdgcn_wave_barrier();
+        // 3. rank by packed key
+        if (rank_packed(C, K, renorm, E, lg, z, true, q, rl, lane,
+                        [&](uint64_t p) { return lg[~static_cast<uint32_t>(p)]; }, nullptr))
             return;
-        }
         // a key shared near the boundary: exact fp64 ranking
-        if (live)
+        if (lane < C)
             rl.cand_v[q][lane] = lg[rl.cand[q][lane]];
         rank_exact(C, K, q, rl, lane);
     } else {

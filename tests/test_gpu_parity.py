@@ -92,16 +92,24 @@ def test_route_only_entry_point():
     assert tolerance_ok(gate.cpu().numpy(), rg).all()
 
 
-def test_duplicate_router_rows_tie_on_gpu():
+@pytest.mark.parametrize("layout", ["pairs64", "twins512"])
+def test_duplicate_router_rows_tie_on_gpu(layout):
     """Bit-equal logits from duplicated router rows: the lower id must win
     on the GPU exactly as in the oracle, at every boundary position."""
-    _say("case: exact-tie fixture")
+    _say(f"case: exact-tie fixture {layout}")
     rng = np.random.default_rng(31)
-    H, E, K = 256, 64, 6
-    a = _random_arrays(rng, H, E, K, 64, 64)
-    # pairs of identical rows across the whole expert range
-    for lo, hi in [(1, 40), (5, 6), (10, 63), (20, 21), (33, 50)]:
-        a["router_w"][hi] = a["router_w"][lo]
+    if layout == "pairs64":
+        H, E, K = 256, 64, 6
+        a = _random_arrays(rng, H, E, K, 64, 64)
+        # pairs of identical rows across the whole expert range
+        for lo, hi in [(1, 40), (5, 6), (10, 63), (20, 21), (33, 50)]:
+            a["router_w"][hi] = a["router_w"][lo]
+    else:
+        # every logit has a twin 256 ids away: with K odd the K-th and the
+        # (K+1)-th are always equal
+        H, E, K = 128, 512, 5
+        a = _random_arrays(rng, H, E, K, 32, 32)
+        a["router_w"][256:] = a["router_w"][:256]
     x = rng.standard_normal((200, H)).astype(np.float32)
     L = oracle_layer_from_arrays(a)
     ri, _, _, logits = L.route(x)
@@ -113,7 +121,7 @@ def test_duplicate_router_rows_tie_on_gpu():
         assert_parity(got, ref, f"tie fixture rows={rows}")
 
 
-@pytest.mark.parametrize("case", ["k_equals_e", "single_expert", "no_renorm", "bias", "zero_x", "wide"])
+@pytest.mark.parametrize("case", ["k_equals_e", "single_expert", "no_renorm", "bias", "zero_x", "zero_x_many", "wide"])
 def test_edge_shapes(case):
     _say(f"case: edge {case}")
     rng = np.random.default_rng(hash(case) % 2 ** 32)
@@ -130,11 +138,13 @@ def test_edge_shapes(case):
         a["router_bias"] = rng.standard_normal(48).astype(np.float32)
     elif case == "zero_x":
         a = _random_arrays(rng, 64, 16, 4, 32, 32)
+    elif case == "zero_x_many":   # 512 equal logits: more candidates than a wave holds
+        a = _random_arrays(rng, 64, 512, 10, 32, 32)
     else:   # wide: K = 16, E = 1024, odd intermediate sizes
         a = _random_arrays(rng, 256, 1024, 16, 96, 160, rstd=0.1)
     T = 9
     x = rng.standard_normal((T, a["H"])).astype(np.float32)
-    if case == "zero_x":
+    if case.startswith("zero_x"):
         x[:] = 0
     L = oracle_layer_from_arrays(a, renormalize=renorm)
     G = gpu_layer_from_arrays(a, renormalize=renorm)
