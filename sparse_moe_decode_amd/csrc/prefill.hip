@@ -700,17 +700,23 @@ constexpr int kBufWord3 = 0x00020000;
 constexpr int kRawC = 2 * kMS + 1;   // LDS row stride (dwords) of raw codes
 constexpr int kRawS = kMS + 1;       // LDS row stride (floats) of scales
 
-// 8 codes (16 bits, LSB first) -> bf16 0..3 (exact): the float's upper half
-__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c16)
+// 8 codes (16 bits, code i at bits 2i..2i+1) -> the bf16 values 1 + c/4
+// (exact): each code becomes the top two mantissa bits of 1.0 (0x3F80), so
+// one block's dot product with A is asum + (sum of a*c)/4 and the weight
+// s*c + m equals (4s)*v + (m - 4s). y holds code 2j at bit 4j and code 2j+1
+// at bit 4j+16; each bf16 pair is then one mask and one shift of y.
+// one2 = 0x3F803F80 (a pair of bf16 1.0) in a register the compiler cannot
+// see through, so that each (shifted y & mask) | one2 is one bit-field insert
+// (one2 has no bits under the mask).
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c16, uint32_t one2)
 {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float a = static_cast<float>((c16 >> (4 * i)) & 3u);
-        const float b = static_cast<float>((c16 >> (4 * i + 2)) & 3u);
-        w[i] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-    }
-    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    constexpr uint32_t m = 0x00600060u;
+    const uint32_t y = c16 | (c16 << 14);
+    const uint32_t w0 = ((y << 5) & m) | (one2 & ~m);
+    const uint32_t w1 = ((y << 1) & m) | (one2 & ~m);
+    const uint32_t w2 = ((y >> 3) & m) | (one2 & ~m);
+    const uint32_t w3 = ((y >> 7) & m) | (one2 & ~m);
+    return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
 }
 
 template <bool DUAL, int BM>
@@ -798,6 +804,8 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         for (int ct = 0; ct < S::CT; ++ct)
             acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    uint32_t one2 = 0x3F803F80u;   // see codes_bf16
+    asm volatile("" : "+v"(one2));
     load_b(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -812,7 +820,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
                 const int row = lds_row(chl0 + 8 * j);
                 Lrc[row * kRawC + 2 * bl] = in ? rc[j].x : 0u;
                 Lrc[row * kRawC + 2 * bl + 1] = in ? rc[j].y : 0u;
-                Lsc[row * kRawS + bl] = in ? f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+                Lsc[row * kRawS + bl] = in ? 4.0f * f16_to_f32(rs[j] & 0xffffu) : 0.0f;
             }
         }
         if (M + 1 < nms)
@@ -840,7 +848,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
             for (int ct = 0; ct < S::CT; ++ct) {
                 const int c = wc * S::TC + ct * 16 + li;
                 const uint32_t cw = Lrc[c * kRawC + 2 * b + (kq >> 1)];
-                const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu);
+                const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu, one2);
                 const float sc = Lsc[c * kRawS + b];
 #pragma unroll
                 for (int rt = 0; rt < S::RT; ++rt) {
@@ -855,7 +863,9 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         }
     }
 
-    // minimum terms: acc += sum_b asum[row][b] * m[col][b], 32 blocks per MFMA
+    // minimum terms: acc += sum_b asum[row][b] * (m[col][b] - 4 s[col][b])
+    // (the offset of the 1 + c/4 code values), 32 blocks per MFMA; m and -4s
+    // are fp16 values, exact as bf16 hi + lo, and enter separately
     for (int b0 = 0; b0 < NB; b0 += 32) {
         bf16x8 xah[S::RT], xal[S::RT];
 #pragma unroll
@@ -874,21 +884,26 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
             const int c = wc * S::TC + ct * 16 + li;
             const uint8_t *cm;
             const int cn = gemm_brow<DUAL, BM>(p, e, n0, c, cm);
-            float v[8];
+            float vm[8], vs[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int b = b0 + kq * 8 + j;
-                v[j] = (cn < p.N && b < NB)
-                           ? f16_to_f32(ld_nt4(cm + plane + (static_cast<size_t>(cn) * NB + b) * 4) >> 16)
-                           : 0.0f;
+                const uint32_t w =
+                    (cn < p.N && b < NB) ? ld_nt4(cm + plane + (static_cast<size_t>(cn) * NB + b) * 4) : 0u;
+                vm[j] = f16_to_f32(w >> 16);
+                vs[j] = -4.0f * f16_to_f32(w & 0xffffu);
             }
-            bf16x8 mh, ml;
-            split_frag(v, mh, ml);
+            bf16x8 mh, ml, sh, sl;
+            split_frag(vm, mh, ml);
+            split_frag(vs, sh, sl);
 #pragma unroll
             for (int rt = 0; rt < S::RT; ++rt) {
                 acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], mh, acc[rt][ct], 0, 0, 0);
                 acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], ml, acc[rt][ct], 0, 0, 0);
                 acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal[rt], mh, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], sh, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], sl, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal[rt], sh, acc[rt][ct], 0, 0, 0);
             }
         }
     }
