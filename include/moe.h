@@ -102,10 +102,9 @@ const char *moe_strerror(int status);
 
 /*
  * Bytes of device workspace moe_route / moe_forward need for T rows (0 on an
- * invalid descriptor). The workspace must be zero-filled once after it is
- * allocated; its counters return to zero at the end of every call, so it can
- * be reused without clearing. Calls that run at the same time (different
- * streams) need different workspaces.
+ * invalid descriptor). The workspace needs no initialization and holds no
+ * state between calls; calls that run at the same time (different streams)
+ * need different workspaces.
  */
 size_t moe_workspace_bytes(const moe_layer_desc *d, int32_t T);
 
@@ -151,8 +150,8 @@ int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y,
  *   perm    [T*K]  int32 device (out): pair index t*K+k, grouped by expert in
  *                  increasing expert order, increasing t*K+k within a group
  * ids outside [0, E) are skipped (their pairs are not placed).
- * ws: device workspace of at least moe_sort_workspace_bytes(T, K, E) bytes,
- * zero-filled once after allocation (its ticket returns to zero per call).
+ * ws: device workspace of at least moe_sort_workspace_bytes(T, K, E) bytes
+ * (per-chunk histograms; no initialization needed).
  */
 size_t moe_sort_workspace_bytes(int32_t T, int32_t K, int32_t E);
 int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E,

@@ -242,9 +242,10 @@ __device__ __forceinline__ int next_pow2(int v)
 //   slot table  : nslots, slot_expert[S], slot_w[S][R] (S = R*K + 1)
 //   hbuf        : [S][R][Imax] fp32   (weighted SwiGLU activations, one row
 //                 per (slot, row) pair; at most R*(K+1) rows are used)
+// Reserved header at the start of every workspace (no kernel keeps state
+// in it; the workspaces need no initialization).
 struct Control {
-    unsigned int route_done;   // last-block ticket of the route kernel
-    unsigned int pad[63];
+    unsigned int reserved[64];
 };
 
 // Slots of a decode / few-row call: slot 0 is the shared expert, slots

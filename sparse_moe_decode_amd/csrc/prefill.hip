@@ -688,12 +688,14 @@ __global__ void __launch_bounds__(256) k_single_sum(const float *part, int ks, i
 // registers one mega-step ahead, then the codes go to LDS as they are and the
 // scales as fp32. Each wave expands the codes of its own B operands to bf16
 // in registers (8 codes per lane per operand). A: each thread holds BM/32
-// 16-byte pieces (row, part, hi or lo) of 4 consecutive blocks and reloads a
-// block's pieces with the block 4 steps ahead as soon as they are stored.
+// 16-byte pieces (row, part, hi or lo) of 4 consecutive blocks; a group of 4
+// blocks goes to LDS at once (one barrier per group) and each block's pieces
+// are reloaded with the block 4 steps ahead as soon as they are stored.
 // Loads go through buffer descriptors: rows past the end read as zero. The
 // minimum terms run after the loop (from the block sums of A and the minima
 // in global memory).
 constexpr int kMS = 8;           // blocks per mega-step
+constexpr int kAG = 4;           // A blocks per LDS group (and register ring slots)
 // Word 3 of a raw buffer descriptor on gfx9 targets (32-bit data format;
 // offsets past num_records read as zero).
 constexpr int kBufWord3 = 0x00020000;
@@ -725,7 +727,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
     using S = GemmShape<BM>;
     constexpr int AP = BM / 32;            // A pieces per thread per block
     constexpr int BL = kGN * kMS / 256;    // (row, block) words per thread per mega-step
-    __shared__ __align__(16) uint16_t La[2][BM * kLD];
+    __shared__ __align__(16) uint16_t La[kAG][2][BM * kLD];
     __shared__ __align__(16) uint32_t Lrc[kGN * kRawC];
     __shared__ float Lsc[kGN * kRawS];
     __shared__ int Ltok[BM];
@@ -789,7 +791,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         const int src = Ltok[arow[j]];
         aoff[j] = src >= 0 ? (ahl[j] ? p.a_lo_off : 0) + (src * p.Kd + apart[j] * 8) * 2 : 0x7fff0000;
     }
-    uint4 ra[4][AP];
+    uint4 ra[kAG][AP];
     auto load_a = [&](int slot, int blk) {
         const int bb = blk < NB ? blk : 0;
 #pragma unroll
@@ -808,7 +810,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
     asm volatile("" : "+v"(one2));
     load_b(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kAG; ++u)
         load_a(u, u);
     const int nms = (NB + kMS - 1) / kMS;
     for (int M = 0; M < nms; ++M) {
@@ -825,38 +827,48 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         }
         if (M + 1 < nms)
             load_b(M + 1);
+        // A in groups of kAG blocks (the register ring): the group goes to
+        // LDS, its slots are refilled kAG blocks ahead, one barrier, then the
+        // group's blocks are computed
 #pragma unroll
-        for (int b = 0; b < kMS; ++b) {
-            const int blk = M * kMS + b;
-            if (blk >= NB)
+        for (int g = 0; g < kMS; g += kAG) {
+            if (M * kMS + g >= NB)
                 break;
-            const int u = b & 3;
-            // A block blk (ring slot u)
 #pragma unroll
-            for (int j = 0; j < AP; ++j)
-                *reinterpret_cast<uint4 *>(&La[ahl[j]][arow[j] * kLD + apart[j] * 8]) = ra[u][j];
-            load_a(u, blk + 4);
-            __syncthreads();
-            bf16x8 fah[S::RT], fal[S::RT];
+            for (int u = 0; u < kAG; ++u) {
 #pragma unroll
-            for (int rt = 0; rt < S::RT; ++rt) {
-                const int r = wr * S::TR + rt * 16 + li;
-                fah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[0][r * kLD + kq * 8]));
-                fal[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[1][r * kLD + kq * 8]));
+                for (int j = 0; j < AP; ++j)
+                    *reinterpret_cast<uint4 *>(&La[u][ahl[j]][arow[j] * kLD + apart[j] * 8]) = ra[u][j];
+                load_a(u, M * kMS + g + u + kAG);
             }
+            __syncthreads();
 #pragma unroll
-            for (int ct = 0; ct < S::CT; ++ct) {
-                const int c = wc * S::TC + ct * 16 + li;
-                const uint32_t cw = Lrc[c * kRawC + 2 * b + (kq >> 1)];
-                const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu, one2);
-                const float sc = Lsc[c * kRawS + b];
+            for (int u = 0; u < kAG; ++u) {
+                const int b = g + u;
+                if (M * kMS + b >= NB)
+                    break;
+                bf16x8 fah[S::RT], fal[S::RT];
 #pragma unroll
                 for (int rt = 0; rt < S::RT; ++rt) {
-                    f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fal[rt], fb, t, 0, 0, 0);
+                    const int r = wr * S::TR + rt * 16 + li;
+                    fah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[u][0][r * kLD + kq * 8]));
+                    fal[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[u][1][r * kLD + kq * 8]));
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[rt][ct][i] = fmaf(sc, t[i], acc[rt][ct][i]);
+                for (int ct = 0; ct < S::CT; ++ct) {
+                    const int c = wc * S::TC + ct * 16 + li;
+                    const uint32_t cw = Lrc[c * kRawC + 2 * b + (kq >> 1)];
+                    const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu, one2);
+                    const float sc = Lsc[c * kRawS + b];
+#pragma unroll
+                    for (int rt = 0; rt < S::RT; ++rt) {
+                        f32x4 t =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fal[rt], fb, t, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[rt][ct][i] = fmaf(sc, t[i], acc[rt][ct][i]);
+                    }
                 }
             }
             __syncthreads();

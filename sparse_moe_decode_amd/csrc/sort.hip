@@ -1,12 +1,15 @@
 // Prefill grouping: stable counting sort of the T*K (row, slot) pairs by
 // expert id (pairs keep their t*K+k order inside each expert group).
-//   k_sort_hist     per-chunk expert histograms; the last-arriving workgroup
-//                   scans them into counts, offsets and per-(chunk, expert)
-//                   base positions.
-//   k_sort_scatter  each pair's rank among earlier pairs of its chunk with the
-//                   same expert gives its slot: perm[base + rank] = pair.
-// Integer-only and deterministic; the result is unique. Optionally also the
-// inverse permutation inv[pair] = sorted position.
+//   k_sort_hist     per-chunk expert histograms (LDS counters).
+//   k_sort_scan     one workgroup: per expert, the pairs of earlier chunks
+//                   (running sums over the chunks, loads batched 8 chunks at
+//                   a time), then counts and offsets (a scan over experts).
+//   k_sort_scatter  per chunk: per-wave histograms give the pairs of earlier
+//                   waves, a broadcast loop the earlier lanes of the same
+//                   wave; perm[offset + earlier chunks + earlier waves +
+//                   earlier lanes] = pair.
+// Integer-only and deterministic (LDS atomics only count); the result is
+// unique. Optionally also the inverse permutation inv[pair] = sorted position.
 #include <hip/hip_runtime.h>
 
 #include "device_common.cuh"
@@ -14,7 +17,8 @@
 
 namespace moe {
 
-constexpr int kSortChunk = 1024;   // pairs per workgroup
+constexpr int kSortChunk = 1024;                  // pairs per workgroup
+constexpr int kSortWaves = kSortChunk / kWave;    // one pair per thread
 
 size_t sort_ws_bytes_tke(int64_t n, int E)
 {
@@ -22,90 +26,99 @@ size_t sort_ws_bytes_tke(int64_t n, int E)
     return align256(sizeof(Control)) + align256(sizeof(int) * static_cast<size_t>(chunks) * E);
 }
 
-__global__ void __launch_bounds__(1024) k_sort_hist(const int32_t *ids, int n, int E, int *table, int32_t *counts,
-                                                   int32_t *offsets, unsigned int *ticket)
+__global__ void __launch_bounds__(kSortChunk) k_sort_hist(const int32_t *ids, int n, int E, int *table)
 {
     __shared__ int hist[kMaxE];
-    __shared__ int scan[kMaxE];
-    __shared__ int is_last;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x)
         hist[e] = 0;
     __syncthreads();
-    const int base = blockIdx.x * kSortChunk;
-    for (int i = tid; i < kSortChunk && base + i < n; i += blockDim.x) {
-        const int e = ids[base + i];
+    const int i = blockIdx.x * kSortChunk + tid;
+    if (i < n) {
+        const int e = ids[i];
         if (e >= 0 && e < E)
             atomicAdd(&hist[e], 1);
     }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x)
         table[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        is_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
-    const int C = gridDim.x;
-    // per expert: running base over chunks (relative to the expert's group)
-    for (int e = tid; e < E; e += blockDim.x) {
-        int run = 0;
-        for (int c = 0; c < C; ++c) {
-            const int v = table[static_cast<size_t>(c) * E + e];
-            table[static_cast<size_t>(c) * E + e] = run;
-            run += v;
+}
+
+// table[c][e] becomes the pairs of expert e in chunks before c; counts and
+// offsets (exclusive scan over experts, Hillis-Steele in LDS).
+__global__ void __launch_bounds__(kSortChunk) k_sort_scan(int C, int E, int *table, int32_t *counts,
+                                                         int32_t *offsets)
+{
+    __shared__ int sc[kMaxE];
+    const int tid = threadIdx.x;
+    int total = 0;
+    if (tid < E) {
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = c0 + k < C ? table[static_cast<size_t>(c0 + k) * E + tid] : 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (c0 + k < C) {
+                    table[static_cast<size_t>(c0 + k) * E + tid] = total;
+                    total += v[k];
+                }
         }
-        scan[e] = run;
-        counts[e] = run;
+        sc[tid] = total;
     }
     __syncthreads();
-    // exclusive scan of counts over experts (Hillis-Steele on an inclusive copy)
     for (int off = 1; off < E; off <<= 1) {
-        int v = 0;
-        if (tid < E && tid >= off)
-            v = scan[tid - off];
+        const int v = (tid < E && tid >= off) ? sc[tid - off] : 0;
         __syncthreads();
         if (tid < E)
-            scan[tid] += v;
+            sc[tid] += v;
         __syncthreads();
     }
-    for (int e = tid; e < E; e += blockDim.x) {
-        const int excl = scan[e] - counts[e];
-        offsets[e] = excl;
-        for (int c = 0; c < C; ++c)
-            table[static_cast<size_t>(c) * E + e] += excl;
-    }
-    if (tid == 0) {
-        offsets[E] = scan[E - 1];
-        *ticket = 0u;
+    if (tid < E) {
+        counts[tid] = total;
+        offsets[tid] = sc[tid] - total;
+        if (tid == E - 1)
+            offsets[E] = sc[tid];
     }
 }
 
-__global__ void __launch_bounds__(1024) k_sort_scatter(const int32_t *ids, int n, int E, const int *table,
-                                                      int32_t *perm, int32_t *inv)
+__global__ void __launch_bounds__(kSortChunk) k_sort_scatter(const int32_t *ids, int n, int E, const int *table,
+                                                            const int32_t *offsets, int32_t *perm, int32_t *inv)
 {
-    __shared__ int le[kSortChunk];
-    const int tid = threadIdx.x;
-    const int base = blockIdx.x * kSortChunk;
-    const int len = min(kSortChunk, n - base);
-    for (int i = tid; i < len; i += blockDim.x)
-        le[i] = ids[base + i];
+    __shared__ int wh[kSortWaves][kMaxE];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int w = 0; w < kSortWaves; ++w)
+        for (int e = tid; e < E; e += blockDim.x)
+            wh[w][e] = 0;
     __syncthreads();
-    for (int i = tid; i < len; i += blockDim.x) {
-        const int e = le[i];
-        if (e < 0 || e >= E)
-            continue;
-        int rank = 0;
-        for (int j = 0; j < i; ++j)
-            rank += (le[j] == e);
-        const int pos = table[static_cast<size_t>(blockIdx.x) * E + e] + rank;
-        perm[pos] = base + i;
+    const int i = blockIdx.x * kSortChunk + tid;
+    const int e = i < n ? ids[i] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (valid)
+        atomicAdd(&wh[wave][e], 1);
+    __syncthreads();
+    // per expert: first position of each wave's pairs
+    for (int x = tid; x < E; x += blockDim.x) {
+        int run = offsets[x] + table[static_cast<size_t>(blockIdx.x) * E + x];
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int h = wh[w][x];
+            wh[w][x] = run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    // earlier lanes of this wave with the same expert
+    int r = 0;
+    for (int j = 0; j < kWave; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        r += (ej == e) & (j < lane);
+    }
+    if (valid) {
+        const int pos = wh[wave][e] + r;
+        perm[pos] = i;
         if (inv)
-            inv[base + i] = pos;
+            inv[i] = pos;
     }
 }
 
@@ -115,12 +128,10 @@ int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *coun
     const int n = T * K;
     const int chunks = (n + kSortChunk - 1) / kSortChunk;
     uint8_t *p = static_cast<uint8_t *>(ws);
-    unsigned int *ticket = reinterpret_cast<unsigned int *>(p);
     int *table = reinterpret_cast<int *>(p + align256(sizeof(Control)));
-    hipLaunchKernelGGL(k_sort_hist, dim3(chunks), dim3(1024), 0, s, ids, n, E, table, counts, offsets, ticket);
-    if (hipGetLastError() != hipSuccess)
-        return MOE_EHIP;
-    hipLaunchKernelGGL(k_sort_scatter, dim3(chunks), dim3(1024), 0, s, ids, n, E, table, perm, inv);
+    hipLaunchKernelGGL(k_sort_hist, dim3(chunks), dim3(kSortChunk), 0, s, ids, n, E, table);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortChunk), 0, s, chunks, E, table, counts, offsets);
+    hipLaunchKernelGGL(k_sort_scatter, dim3(chunks), dim3(kSortChunk), 0, s, ids, n, E, table, offsets, perm, inv);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -390,28 +390,35 @@ def test_q2_unpack_of_packed_expert_weights():
 
 # ---------------------------------------------------------------- grouping
 
-@pytest.mark.parametrize("T,K,E,skew", [(2048, 10, 512, True), (5, 3, 8, False), (1, 1, 1, False),
-                                        (3000, 16, 1024, True), (777, 10, 512, False)])
-def test_sort_by_expert(T, K, E, skew):
-    _say(f"case: sort T={T} K={K} E={E}")
+@pytest.mark.parametrize("T,K,E,skew,invalid", [(2048, 10, 512, True, False), (5, 3, 8, False, False),
+                                                (1, 1, 1, False, False), (3000, 16, 1024, True, False),
+                                                (777, 10, 512, False, False), (300, 4, 16, False, True)])
+def test_sort_by_expert(T, K, E, skew, invalid):
+    _say(f"case: sort T={T} K={K} E={E} invalid={invalid}")
     import sparse_moe_decode_amd as moe
     rng = np.random.default_rng(T * 31 + K)
     p = rng.dirichlet(np.full(E, 0.3 if skew else 5.0))
     ids = np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    if invalid:   # ids outside [0, E) are skipped
+        flat_ids = ids.reshape(-1)
+        flat_ids[rng.choice(flat_ids.size, size=flat_ids.size // 7, replace=False)] = -1
+        flat_ids[rng.choice(flat_ids.size, size=flat_ids.size // 11, replace=False)] = E
     dev = torch.from_numpy(ids).cuda()
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(T * K, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(moe.sort_workspace_bytes(T, K, E), dtype=torch.uint8, device="cuda")
-    for _ in range(2):   # the second call checks the self-resetting ticket
+    # the workspace needs no initialization: start from arbitrary bytes
+    ws = torch.full((moe.sort_workspace_bytes(T, K, E),), 0xA5, dtype=torch.uint8, device="cuda")
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    ref_perm = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    ref_counts = np.bincount(flat[valid], minlength=E)
+    for _ in range(2):   # the second call reuses the workspace as the first left it
         moe.sort_by_expert(dev, E, counts, offsets, perm, ws)
         torch.cuda.synchronize()
-        flat = ids.reshape(-1)
-        ref_perm = np.argsort(flat, kind="stable")
-        ref_counts = np.bincount(flat, minlength=E)
         np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts)
         np.testing.assert_array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(ref_counts)]))
-        np.testing.assert_array_equal(perm.cpu().numpy(), ref_perm)
+        np.testing.assert_array_equal(perm.cpu().numpy()[:ref_perm.size], ref_perm)
 
 
 # ------------------------------------------------------- full-size workloads
