@@ -799,36 +799,6 @@ struct LogitArgs {
     double *zlogit;          // [R]
 };
 
-template <int R>
-__device__ __forceinline__ void router_chunk(F32, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
-{
-    const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float4 xv = *reinterpret_cast<const float4 *>(xs + q * H + c * 4);
-        acc[q] = fma(static_cast<double>(w[0]), static_cast<double>(xv.x), acc[q]);
-        acc[q] = fma(static_cast<double>(w[1]), static_cast<double>(xv.y), acc[q]);
-        acc[q] = fma(static_cast<double>(w[2]), static_cast<double>(xv.z), acc[q]);
-        acc[q] = fma(static_cast<double>(w[3]), static_cast<double>(xv.w), acc[q]);
-    }
-}
-
-template <int R>
-__device__ __forceinline__ void router_chunk(BF16, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
-{
-    const float wf[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8);
-        const float4 x1 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8 + 4);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[q] = fma(static_cast<double>(wf[i]), static_cast<double>(xv[i]), acc[q]);
-    }
-}
-
 constexpr int kLgPrefetch = 4;   // 16-byte chunks per lane loaded before x is staged
 
 // Router logits of a call, one row per wave; row E is the shared-gate vector.

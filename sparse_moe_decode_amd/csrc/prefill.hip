@@ -27,6 +27,8 @@
 // dropped lo*lo terms are below 2^-16 of each product.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "device_common.cuh"
 #include "internal.h"
 #include "routing.cuh"
@@ -57,8 +59,19 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4 &hi, uint4 &lo
 
 // ============================================================== split x
 
-__global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uint4 *xh, uint4 *xl, float *xsum)
+template <typename RT>
+__device__ void router_norm(const uint8_t *router_w, int E, int H, float *wn, int e, int lane);
+
+// Blocks [0, nbx): x split; blocks from nbx on (when wn is given): norms of
+// the router rows, one wave per row (router_norm).
+template <typename RT>
+__global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uint4 *xh, uint4 *xl, float *xsum,
+                                                 int nbx, const uint8_t *router_w, int E, int H, float *wn)
 {
+    if (static_cast<int>(blockIdx.x) >= nbx) {
+        router_norm<RT>(router_w, E, H, wn, (blockIdx.x - nbx) * 4 + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
+        return;
+    }
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n8)   // n8 is a multiple of 4: a lane quad is all in or all out
         return;
@@ -77,159 +90,255 @@ __global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uin
         xsum[i >> 2] = s;
 }
 
-// =========================================================== fp64 logits
-
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kLmT = 64;    // rows (tokens) per workgroup
-constexpr int kLmE = 32;    // experts per workgroup (column E is the gate vector)
-constexpr int kLmK = 32;    // reduction depth per LDS stage
-constexpr int kLmLD = 33;   // LDS row stride in doubles
-
-// One 64 x 32 tile of logits (rows t, experts e; expert index E is the
-// shared-gate vector) with v_mfma_f64_16x16x4_f64: each product of an fp32
-// activation and a bf16/fp32 weight is exact in fp64, and the hardware's
-// summation order is fixed. Wave w owns rows 16w..16w+15 and both 16-column
-// halves. Operands are converted to fp64 once, as they are staged in LDS
-// (double buffered; the next stage's global loads are in flight during the
-// current stage's MFMAs).
-template <typename RT>
-__global__ void __launch_bounds__(256) k_logits64(const float *x, int T, int H, int E, const uint8_t *router_w,
-                                                  const uint8_t *gate_w, const float *bias, double *logits,
-                                                  double *z, double *part)
-{
-    __shared__ double Lx[2][kLmT][kLmLD];
-    __shared__ double Lw[2][kLmE][kLmLD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e0 = blockIdx.x * kLmE, t0 = blockIdx.y * kLmT;
-    // loaders: x rows tid / 4 (8 values at k (tid % 4) * 8), weight rows
-    // tid / 8 (4 values at k (tid % 8) * 4); rows past the end read as 0
-    const int xr = tid >> 2, xk = (tid & 3) * 8;
-    const int wr = tid >> 3, wk = (tid & 7) * 4;
-    const int t = t0 + xr, e = e0 + wr;
-    const bool tin = t < T, ein = e <= E;
-    const float *xrow = x + static_cast<size_t>(tin ? t : 0) * H;
-    const uint8_t *wrow = (ein && e < E) ? router_w + static_cast<size_t>(e) * H * (RT::kChunk == 4 ? 4 : 2) : gate_w;
-    float xv[8], wv[4];
-    auto fetch = [&](int k0) {
-        const float4 a = *reinterpret_cast<const float4 *>(xrow + k0 + xk);
-        const float4 b = *reinterpret_cast<const float4 *>(xrow + k0 + xk + 4);
-        xv[0] = tin ? a.x : 0.f; xv[1] = tin ? a.y : 0.f; xv[2] = tin ? a.z : 0.f; xv[3] = tin ? a.w : 0.f;
-        xv[4] = tin ? b.x : 0.f; xv[5] = tin ? b.y : 0.f; xv[6] = tin ? b.z : 0.f; xv[7] = tin ? b.w : 0.f;
-        if (RT::kChunk == 4) {
-            const float4 c = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(wrow) + k0 + wk);
-            wv[0] = c.x; wv[1] = c.y; wv[2] = c.z; wv[3] = c.w;
-        } else {
-            const uint2 c = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(wrow) + k0 + wk);
-            wv[0] = bf16_lo(c.x); wv[1] = bf16_hi(c.x); wv[2] = bf16_lo(c.y); wv[3] = bf16_hi(c.y);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wv[j] = ein ? wv[j] : 0.f;
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            Lx[buf][xr][xk + j] = static_cast<double>(xv[j]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            Lw[buf][wr][wk + j] = static_cast<double>(wv[j]);
-    };
-    f64x4 acc[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-        acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
-    const int li = lane & 15, lk = lane >> 4;
-    // reduction slice of this workgroup (split K: blockIdx.z of gridDim.z)
-    const int nk = H / kLmK, ks = gridDim.z;
-    const int kb0 = static_cast<int>(blockIdx.z) * nk / ks, kb1 = (static_cast<int>(blockIdx.z) + 1) * nk / ks;
-    fetch(kb0 * kLmK);
-    stage(0);
-    __syncthreads();
-    for (int kb = kb0; kb < kb1; ++kb) {
-        const int buf = (kb - kb0) & 1;
-        if (kb + 1 < kb1)
-            fetch((kb + 1) * kLmK);
-#pragma unroll
-        for (int ks = 0; ks < kLmK / 4; ++ks) {
-            const double av = Lx[buf][wave * 16 + li][ks * 4 + lk];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const double bv = Lw[buf][c * 16 + li][ks * 4 + lk];
-                acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[c], 0, 0, 0);
-            }
-        }
-        if (kb + 1 < kb1)
-            stage(buf ^ 1);
-        __syncthreads();
-    }
-    // D[r][c] of a 16x16 fp64 tile: lane l holds rows l / 16 + 4 i (i < 4),
-    // column l % 16
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int ee = e0 + c * 16 + li;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tt = t0 + wave * 16 + lk + 4 * i;
-            if (tt >= T)
-                continue;
-            if (ks > 1) {
-                // partial over this slice; k_logits_sum adds the slices in order
-                if (ee <= E)
-                    part[(static_cast<size_t>(blockIdx.z) * T + tt) * (E + 1) + ee] = acc[c][i];
-            } else if (ee < E) {
-                logits[static_cast<size_t>(tt) * E + ee] = acc[c][i] + (bias ? static_cast<double>(bias[ee]) : 0.0);
-            } else if (ee == E) {
-                z[tt] = acc[c][i];
-            }
-        }
-    }
-}
-
-// Split-K logits: the sum of the slices' partials in slice order, then the bias.
-__global__ void __launch_bounds__(256) k_logits_sum(const double *part, int ks, int T, int E, const float *bias,
-                                                    double *logits, double *z)
-{
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t n = static_cast<int64_t>(T) * (E + 1);
-    if (i >= n)
-        return;
-    const int t = static_cast<int>(i / (E + 1)), e = static_cast<int>(i - static_cast<int64_t>(t) * (E + 1));
-    // slices in order, their loads issued eight at a time
-    double s = 0.0;
-    for (int k0 = 0; k0 < ks; k0 += 8) {
-        double v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = k0 + u < ks ? part[static_cast<size_t>(k0 + u) * n + i] : 0.0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            s += v[u];
-    }
-    if (e < E)
-        logits[static_cast<size_t>(t) * E + e] = s + (bias ? static_cast<double>(bias[e]) : 0.0);
-    else
-        z[t] = s;
-}
-
 // ============================================================ selection
 
-// One wave per row: exact top-K, weights, gate (routing.cuh).
-__global__ void __launch_bounds__(256) k_select_rows(const double *logits, const double *z, int T, int E, int K,
-                                                     int renorm, int32_t *ids, float *wts, float *gate,
-                                                     int32_t *ids_out, float *wts_out, float *gate_out)
+// Routing of many rows from approximate logits. L' = x W^T comes from the
+// dense bf16 GEMM below (x as hi + lo bf16, each product exact, fp32 sums);
+// for every row t and expert e
+//   |L'_te - sum_k x_tk w_ek| <= c_H ||x_t|| ||w_e||,
+//   c_H = 1.01 (3 * 2^-16 + (3H + 64) * 2^-23),
+// which covers the dropped low parts (of x, and of fp32 weights), any order
+// of at most 3H + 64 fp32 additions with an error of up to one ulp each, and
+// sum |x w| <= ||x|| ||w|| (Cauchy-Schwarz). With lower and upper bounds
+// lo_e <= logit_e <= hi_e, the K-th largest lower bound is at or below the
+// K-th largest logit, so an expert of the exact top K has hi_e at or above
+// any value at or below it: those are the candidates. Their logits are then
+// computed exactly in fp64 in the order of the decode path (router_chunk,
+// wave_sum, + bias) and ranked exactly. More than 64 candidates, or weights
+// over all E logits, take every logit exactly.
+
+// ||w_e||, rounded up, of router row e by one wave.
+template <typename RT>
+__device__ void router_norm(const uint8_t *router_w, int E, int H, float *wn, int e, int lane)
 {
-    __shared__ RouteLds rl;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int t = blockIdx.x * (blockDim.x / kWave) + wave;
-    if (t >= T)
+    if (e >= E)
         return;
-    const double *lg = logits + static_cast<size_t>(t) * E;
-    wave_route(lg, E, K, renorm, z[t], wave, rl, lane);
+    const size_t rb = static_cast<size_t>(H) * (RT::kChunk == 4 ? 4 : 2);
+    const uint8_t *row = router_w + e * rb;
+    const int nch = static_cast<int>(rb / 16);
+    double ss = 0.0;
+    for (int c = lane; c < nch; c += kWave) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(row + static_cast<size_t>(c) * 16);
+        if (RT::kChunk == 4) {
+            const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ss = fma(static_cast<double>(w[i]), static_cast<double>(w[i]), ss);
+        } else {
+            const float w[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                                bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ss = fma(static_cast<double>(w[i]), static_cast<double>(w[i]), ss);
+        }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0)
+        wn[e] = static_cast<float>(sqrt(ss) * (1.0 + 1e-6));
+}
+
+// Exact fp64 dot product of a router row (or the gate vector) with the x row
+// in LDS, by the whole wave (the decode path's order).
+template <typename RT>
+__device__ __forceinline__ double exact_dot(const uint8_t *row, int nch, const float *xs, int H, int lane)
+{
+    double acc[1] = {0.0};
+    for (int c0 = lane; c0 < nch; c0 += 4 * kWave) {
+        uint4 u4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * kWave;
+            u4[u] = *reinterpret_cast<const uint4 *>(row + static_cast<size_t>(c < nch ? c : 0) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < nch)
+                router_chunk<1>(RT{}, u4[u], c, xs, H, acc);
+        }
+    }
+    return wave_sum(acc[0]);
+}
+
+// Exact logits of experts cand[j] (cand null: expert j), j = j0, j0 + step,
+// ... < n, by one wave, two at a time so that the second row's loads overlap
+// the first one's sums; lane 0 stores them in out[j].
+template <typename RT>
+__device__ __forceinline__ void exact_logits(const int *cand, int j0, int step, int n, const uint8_t *router_w,
+                                             size_t rb, int nch, const float *bias, const float *xs, int H, int lane,
+                                             double *out)
+{
+    for (int j = j0; j < n; j += 2 * step) {
+        const int ja = j, jb = j + step < n ? j + step : j;
+        const int ea = cand ? cand[ja] : ja, eb = cand ? cand[jb] : jb;
+        double a0[1] = {0.0}, a1[1] = {0.0};
+        // four chunks per lane of both rows requested at once
+        for (int c0 = lane; c0 < nch; c0 += 4 * kWave) {
+            uint4 ua[4], ub[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * kWave;
+                const size_t o = static_cast<size_t>(c < nch ? c : 0) * 16;
+                ua[u] = *reinterpret_cast<const uint4 *>(router_w + ea * rb + o);
+                ub[u] = *reinterpret_cast<const uint4 *>(router_w + eb * rb + o);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < nch) {
+                    router_chunk<1>(RT{}, ua[u], c, xs, H, a0);
+                    router_chunk<1>(RT{}, ub[u], c, xs, H, a1);
+                }
+            }
+        }
+        const double va = wave_sum(a0[0]) + (bias ? static_cast<double>(bias[ea]) : 0.0);
+        const double vb = wave_sum(a1[0]) + (bias ? static_cast<double>(bias[eb]) : 0.0);
+        if (lane == 0) {
+            out[ja] = va;
+            out[jb] = vb;
+        }
+    }
+}
+
+constexpr int kSelWaves = 4;          // waves per row in k_select_approx
+constexpr int kMaxRouterSplits = 8;   // K slices of the router GEMM, summed by k_select_approx
+
+// One row per workgroup of kSelWaves waves: the x row in LDS; wave 0 sums
+// the approximate logits of the GEMM's ks slices (lap [ks][T][E]), forms the
+// bounds and the candidates; all waves compute exact logits (of the
+// candidates, or of all E experts); one wave the gate logit; wave 0 ranks
+// and writes the routing.
+template <typename RT, int PL>
+__global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
+    const float *x, const float *lap, int ks, const float *wn, const uint8_t *router_w, const uint8_t *gate_w,
+    const float *bias, int T, int H, int E, int K, int renorm, double cH, int32_t *ids, float *wts, float *gate,
+    int32_t *ids_out, float *wts_out, float *gate_out)
+{
+    extern __shared__ __align__(16) float xs[];   // [H] x row, then [E] exact logits (all-E path)
+    __shared__ RouteLds rl;
+    __shared__ double xss[kSelWaves];
+    __shared__ double zsh;
+    __shared__ int csh;   // candidates, or -1: every logit exactly
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, t = blockIdx.x;
+    const size_t rb = static_cast<size_t>(H) * (RT::kChunk == 4 ? 4 : 2);
+    const int nch = static_cast<int>(rb / 16);
+    double *lg = reinterpret_cast<double *>(xs + ((H + 3) & ~3));
+    // x row to LDS; ||x|| in fp64 (rounded up)
+    double ss = 0.0;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + static_cast<size_t>(t) * H);
+    for (int i = tid; i < H / 4; i += blockDim.x) {
+        const float4 v = xr[i];
+        reinterpret_cast<float4 *>(xs)[i] = v;
+        ss = fma(static_cast<double>(v.x), static_cast<double>(v.x), ss);
+        ss = fma(static_cast<double>(v.y), static_cast<double>(v.y), ss);
+        ss = fma(static_cast<double>(v.z), static_cast<double>(v.z), ss);
+        ss = fma(static_cast<double>(v.w), static_cast<double>(v.w), ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0)
+        xss[wave] = ss;
+    __syncthreads();
+    if (wave == 0) {
+        double sx = 0.0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w)
+            sx += xss[w];
+        const double xb = cH * sqrt(sx) * (1.0 + 1e-6);
+        // the GEMM's K slices (at most kMaxRouterSplits), all requested
+        // first, then added in slice order (within the bound)
+        float lsum[PL];
+#pragma unroll
+        for (int m = 0; m < PL; ++m) {
+            const int e = lane + m * kWave;
+            float v[kMaxRouterSplits];
+#pragma unroll
+            for (int z = 0; z < kMaxRouterSplits; ++z)
+                v[z] = (e < E && z < ks) ? lap[(static_cast<size_t>(z) * T + t) * E + e] : 0.0f;
+            lsum[m] = v[0];
+#pragma unroll
+            for (int z = 1; z < kMaxRouterSplits; ++z)
+                lsum[m] += v[z];
+        }
+        // bounds as fp32 keys, lower bounds rounded down and upper bounds up
+        uint32_t klo[PL], khi[PL];
+        uint32_t mk = 0;
+#pragma unroll
+        for (int m = 0; m < PL; ++m) {
+            const int e = lane + m * kWave;
+            klo[m] = khi[m] = 0u;
+            if (e < E) {
+                const double lp = lsum[m];
+                const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+                const double v = lp + b;
+                const double B = (xb * wn[e] + 1e-15 * (fabs(lp) + fabs(b)) + 1e-30) * (1.0 + 1e-9);
+                const double lo = v - B, hi = v + B;
+                klo[m] = f32_key(static_cast<float>(lo - fabs(lo) * 1e-6 - 1e-30));
+                khi[m] = f32_key(static_cast<float>(hi + fabs(hi) * 1e-6 + 1e-30));
+            }
+            mk = klo[m] > mk ? klo[m] : mk;
+        }
+        // threshold at or below the K-th largest lower bound: the K-th
+        // largest of the 32 lane-pair maxima
+        const uint32_t other =
+            static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mk), 0xB1, 0xF, 0xF, false));
+        const uint32_t pm = other > mk ? other : mk;
+        if ((lane & 1) == 0)
+            rl.pmax[0][lane >> 1] = pm;
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t th = kth_of_32(rl.pmax[0], K, lane);
+        // candidates: upper bound at or above the threshold
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < PL; ++m)
+            cnt += (khi[m] >= th) & (khi[m] != 0);
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        int pos = 0, C = 0;
+#pragma unroll
+        for (int b = 0; (1 << b) <= PL; ++b) {
+            const unsigned long long mb = __ballot((cnt >> b) & 1);
+            pos += __popcll(mb & lt) << b;
+            C += __popcll(mb) << b;
+        }
+#pragma unroll
+        for (int m = 0; m < PL; ++m) {
+            const bool c = (khi[m] >= th) & (khi[m] != 0);
+            if (c && pos < kWave)
+                rl.cand[0][pos] = lane + m * kWave;
+            pos += c;
+        }
+        if (lane == 0)
+            csh = (C <= kWave && renorm) ? C : -1;
+    }
+    __syncthreads();
+    const int C = csh;
+    if (C >= 0) {
+        exact_logits<RT>(rl.cand[0], wave, kSelWaves, C, router_w, rb, nch, bias, xs, H, lane, rl.cand_v[0]);
+        if (wave == (C + kSelWaves - 1) % kSelWaves) {   // the wave with the fewest candidates
+            const double z = exact_dot<RT>(gate_w, nch, xs, H, lane);
+            if (lane == 0)
+                zsh = z;
+        }
+    } else {
+        exact_logits<RT>(nullptr, wave, kSelWaves, E, router_w, rb, nch, bias, xs, H, lane, lg);
+        if (wave == (E + kSelWaves - 1) % kSelWaves) {
+            const double z = exact_dot<RT>(gate_w, nch, xs, H, lane);
+            if (lane == 0)
+                zsh = z;
+        }
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    if (C >= 0) {
+        rank_exact(C, K, 0, rl, lane);
+        wave_weights(nullptr, E, K, renorm, zsh, 0, rl, lane);
+    } else {
+        wave_route(lg, E, K, renorm, zsh, 0, rl, lane);
+    }
     __builtin_amdgcn_wave_barrier();
     if (lane < K) {
-        const int e = rl.sel_e[wave][lane];
-        const float w = rl.sel_w[wave][lane];
+        const int e = rl.sel_e[0][lane];
+        const float w = rl.sel_w[0][lane];
         ids[t * K + lane] = e;
         wts[t * K + lane] = w;
         if (ids_out)
@@ -238,9 +347,9 @@ __global__ void __launch_bounds__(256) k_select_rows(const double *logits, const
             wts_out[t * K + lane] = w;
     }
     if (lane == 0) {
-        gate[t] = rl.g[wave];
+        gate[t] = rl.g[0];
         if (gate_out)
-            gate_out[t] = rl.g[wave];
+            gate_out[t] = rl.g[0];
     }
 }
 
@@ -947,21 +1056,6 @@ __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const 
 
 // ============================================================ workspace
 
-// Reduction slices of the fp64 router GEMM: up to about 1024 workgroups
-// when there are few rows; two slices once the tiles alone fill the chip
-// (measured on the 2048-row chunk: 140 -> 123 us plus 7 us for the sum).
-static int logit_splits(const moe_layer_desc *d, int T)
-{
-    const int base = ((d->n_experts + 1 + kLmE - 1) / kLmE) * ((T + kLmT - 1) / kLmT);
-    const int nk = d->hidden / kLmK;
-    if (base >= 512)
-        return nk >= 2 ? 2 : 1;
-    int ks = 1;
-    while (base * ks * 2 <= 1024 && ks * 2 <= nk)
-        ks *= 2;
-    return ks;
-}
-
 // Reduction slices of a dense (shared-expert) GEMM with `blocks` output
 // workgroups and Kd-deep rows: up to about 512 workgroups in all, at least
 // one 32-deep step per slice.
@@ -983,21 +1077,29 @@ static int shared_dn_splits(const moe_layer_desc *d, int T)
     const int blocks = ((d->hidden + kGN - 1) / kGN) * ((T + 63) / 64);
     return blocks < 128 ? dense_splits(blocks, d->shared_inter) : 1;
 }
-static size_t shared_kpart_bytes(const moe_layer_desc *d, int T)
+// The selection kernel sums the router GEMM's slices itself.
+static int router_splits(const moe_layer_desc *d, int T)
 {
-    const int a = shared_gu_splits(d, T), b = shared_dn_splits(d, T);
+    const int ks = dense_splits(((d->n_experts + kGN - 1) / kGN) * ((T + 63) / 64), d->hidden);
+    return ks < kMaxRouterSplits ? ks : kMaxRouterSplits;
+}
+static size_t kpart_bytes(const moe_layer_desc *d, int T)
+{
+    const int a = shared_gu_splits(d, T), b = shared_dn_splits(d, T), c = router_splits(d, T);
     const size_t gu = a > 1 ? sizeof(float) * a * static_cast<size_t>(T) * 2 * d->shared_inter : 0;
     const size_t dn = b > 1 ? sizeof(float) * b * static_cast<size_t>(T) * d->hidden : 0;
-    return gu > dn ? gu : dn;
+    const size_t lg = c > 1 ? sizeof(float) * c * static_cast<size_t>(T) * d->n_experts : 0;
+    const size_t m = gu > dn ? gu : dn;
+    return m > lg ? m : lg;
 }
 
 struct PrefillWs {
     uint8_t *sort_ws;
     size_t sort_bytes;
     uint4 *xh, *xl;
-    double *logits, *z;
-    double *lpart;                   // split-K partial logits [ks][T][E+1] (empty when ks == 1)
-    float *kpart;                    // split-K partial sums of the shared expert's GEMMs
+    float *lap;                      // approximate router logits [T][E]
+    float *wn;                       // norms of the router rows [E]
+    float *kpart;                    // split-K partial sums of the dense GEMMs (router, shared expert)
     int32_t *ids;
     float *wts, *gate;
     int32_t *counts, *offsets, *perm, *inv, *tile_off;
@@ -1022,9 +1124,8 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.sort_ws = take(w.sort_bytes);
     w.xh = reinterpret_cast<uint4 *>(take(sizeof(uint16_t) * T * H));
     w.xl = reinterpret_cast<uint4 *>(take(sizeof(uint16_t) * T * H));
-    w.logits = reinterpret_cast<double *>(take(sizeof(double) * T * E));
-    w.z = reinterpret_cast<double *>(take(sizeof(double) * T));
-    w.lpart = reinterpret_cast<double *>(take(sizeof(double) * logit_splits(d, T) * T * (E + 1) * (logit_splits(d, T) > 1)));
+    w.lap = reinterpret_cast<float *>(take(sizeof(float) * T * E));
+    w.wn = reinterpret_cast<float *>(take(sizeof(float) * E));
     w.ids = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.wts = reinterpret_cast<float *>(take(sizeof(float) * P));
     w.gate = reinterpret_cast<float *>(take(sizeof(float) * T));
@@ -1041,7 +1142,7 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.hsum = reinterpret_cast<float *>(take(sizeof(float) * P * (I / 32)));
     w.rout = reinterpret_cast<float *>(take(sizeof(float) * P * H));
     w.sout = reinterpret_cast<float *>(take(sizeof(float) * T * H));
-    w.kpart = reinterpret_cast<float *>(take(shared_kpart_bytes(d, T)));
+    w.kpart = reinterpret_cast<float *>(take(kpart_bytes(d, T)));
     w.sort_bytes = off;   // total, when not carving
     return w;
 }
@@ -1160,36 +1261,78 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-// Router logits and the exact per-row routing (ids / weights / gate in the
-// workspace, and in the caller's outputs when given).
+// The per-row routing (ids / weights / gate in the workspace, and in the
+// caller's outputs when given): router norms, approximate logits from the
+// dense GEMM of x (hi + lo, from k_split_x), then candidates and their exact
+// logits (k_select_approx).
+template <typename RT>
+static void prefill_route_t(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, int32_t *ids_out,
+                            float *wts_out, float *gate_out, hipStream_t s)
+{
+    const int H = d->hidden, E = d->n_experts, K = d->top_k;
+    GemmArgs g{};
+    g.T = T;
+    g.K = K;
+    g.E = E;
+    g.routed = 0;
+    g.a_gather = 0;
+    g.ah = reinterpret_cast<const uint16_t *>(w.xh);
+    g.al = reinterpret_cast<const uint16_t *>(w.xl);
+    g.a_bytes = static_cast<int>(sizeof(uint16_t) * T * H);
+    g.a_lo_off = static_cast<int>(reinterpret_cast<const uint8_t *>(w.xl) - reinterpret_cast<const uint8_t *>(w.xh));
+    g.b0 = static_cast<const uint8_t *>(d->router_w);
+    g.bstride = 0;
+    g.N = E;
+    g.Kd = H;
+    g.out = w.lap;
+    g.kpart = w.kpart;
+    const int ks = router_splits(d, T);
+    launch_ggemm<RT, false>(g, 64, (T + 63) / 64, s, ks);
+    const float *lap = ks > 1 ? w.kpart : w.lap;
+    const double cH = 1.01 * (3.0 * std::ldexp(1.0, -16) + (3.0 * H + 64.0) * std::ldexp(1.0, -23));
+    const size_t lds = sizeof(float) * ((H + 3) & ~3) + sizeof(double) * E;
+    if (E <= 8 * kWave)
+        hipLaunchKernelGGL((k_select_approx<RT, 8>), dim3(T), dim3(kSelWaves * kWave), lds, s, x, lap, ks, w.wn,
+                           static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
+                           d->router_bias, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
+                           gate_out);
+    else
+        hipLaunchKernelGGL((k_select_approx<RT, kMaxE / kWave>), dim3(T), dim3(kSelWaves * kWave), lds, s, x, lap, ks, w.wn,
+                           static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
+                           d->router_bias, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
+                           gate_out);
+}
+
 static int prefill_route(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, int32_t *ids_out,
                          float *wts_out, float *gate_out, hipStream_t s)
 {
-    const int H = d->hidden, E = d->n_experts, K = d->top_k;
-    const int ks = logit_splits(d, T);
-    const dim3 lg((E + 1 + kLmE - 1) / kLmE, (T + kLmT - 1) / kLmT, ks);
     if (d->router_t == MOE_F32)
-        hipLaunchKernelGGL((k_logits64<F32>), lg, dim3(256), 0, s, x, T, H, E,
-                           static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, w.logits, w.z, w.lpart);
+        prefill_route_t<F32>(d, x, T, w, ids_out, wts_out, gate_out, s);
     else
-        hipLaunchKernelGGL((k_logits64<BF16>), lg, dim3(256), 0, s, x, T, H, E,
-                           static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, w.logits, w.z, w.lpart);
-    if (ks > 1) {
-        const int64_t n = static_cast<int64_t>(T) * (E + 1);
-        hipLaunchKernelGGL(k_logits_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.lpart, ks, T,
-                           E, d->router_bias, w.logits, w.z);
-    }
-    hipLaunchKernelGGL(k_select_rows, dim3((T + 3) / 4), dim3(256), 0, s, w.logits, w.z, T, E, K, d->renormalize,
-                       w.ids, w.wts, w.gate, ids_out, wts_out, gate_out);
+        prefill_route_t<BF16>(d, x, T, w, ids_out, wts_out, gate_out, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// x hi/lo and block sums; with `norms`, also the router row norms (for the
+// routing) in trailing blocks of the same launch.
+static void split_x(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, bool norms, hipStream_t s)
+{
+    const int H = d->hidden, E = d->n_experts;
+    const int64_t n8 = static_cast<int64_t>(T) * H / 8;
+    const int nbx = static_cast<int>((n8 + 255) / 256);
+    const dim3 grid(nbx + (norms ? (E + 3) / 4 : 0));
+    const uint8_t *rw = static_cast<const uint8_t *>(d->router_w);
+    if (d->router_t == MOE_F32)
+        hipLaunchKernelGGL((k_split_x<F32>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
+    else
+        hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
 }
 
 int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t *ids, float *wts, float *gate,
                          void *ws, hipStream_t s)
 {
     const PrefillWs w = prefill_carve(ws, d, T, true);
+    split_x(d, x, T, w, true, s);
     return prefill_route(d, x, T, w, ids, wts, gate, s);
 }
 
@@ -1200,9 +1343,7 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
     const int H = d->hidden, E = d->n_experts, K = d->top_k;
     const int64_t P = static_cast<int64_t>(T) * K;
     const PrefillWs w = prefill_carve(ws, d, T, true);
-    const int64_t n8 = static_cast<int64_t>(T) * H / 8;
-    hipLaunchKernelGGL(k_split_x, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, x, n8, w.xh, w.xl,
-                       w.xsum);
+    split_x(d, x, T, w, ids_in == nullptr, s);
     int rc;
     if (ids_in) {
         hipLaunchKernelGGL(k_take_routing, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0, s, ids_in,

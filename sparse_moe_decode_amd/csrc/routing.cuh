@@ -28,6 +28,42 @@ struct RouteLds {
     SlotTable slots;
 };
 
+// Router dot products in fp64 (exact products of an fp32 activation and a
+// bf16/fp32 weight): one 16-byte chunk c of a router row (4 fp32 or 8 bf16
+// weights) against x (fp32, R rows of H in `xs`), accumulated in element order.
+// Every path that needs an exact logit sums chunks c = lane, lane + 64, ...
+// in this order per lane, then wave_sum, then adds the bias, so all paths
+// produce the same bits.
+template <int R>
+__device__ __forceinline__ void router_chunk(F32, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
+{
+    const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 xv = *reinterpret_cast<const float4 *>(xs + q * H + c * 4);
+        acc[q] = fma(static_cast<double>(w[0]), static_cast<double>(xv.x), acc[q]);
+        acc[q] = fma(static_cast<double>(w[1]), static_cast<double>(xv.y), acc[q]);
+        acc[q] = fma(static_cast<double>(w[2]), static_cast<double>(xv.z), acc[q]);
+        acc[q] = fma(static_cast<double>(w[3]), static_cast<double>(xv.w), acc[q]);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void router_chunk(BF16, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
+{
+    const float wf[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(xs + q * H + c * 8 + 4);
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[q] = fma(static_cast<double>(wf[i]), static_cast<double>(xv[i]), acc[q]);
+    }
+}
+
 // v[l] + v[l ^ 32] on every lane, with one VALU swap of the wave's halves
 // (v_permlane32_swap: each returned register holds one half of each).
 __device__ __forceinline__ int add_halves(int v)

@@ -181,3 +181,34 @@ def test_packer_rejects_bad_input():
     dst = np.zeros(16, np.uint8)
     assert L.moe_q2_pack(src.ctypes.data, 2, 64, dst.ctypes.data, 16) == moe.MOE_EWORKSPACE
     assert L.moe_q2_pack(src.ctypes.data, 2, 48, dst.ctypes.data, 1 << 20) == moe.MOE_EINVAL
+
+
+def _bf16_rne(v: np.ndarray) -> np.ndarray:
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def test_router_candidate_bound():
+    """The prefill routing takes candidates from approximate logits: x as a
+    bf16 hi + lo pair times bf16 router weights, summed in fp32 in any order.
+    Its bound |L' - L| <= c_H ||x|| ||w_e|| (c_H as the kernel computes it)
+    must hold, here with sequential fp32 sums in a shuffled order and a large
+    common offset in x (cancellation)."""
+    rng = np.random.default_rng(5)
+    H, E = 2048, 64
+    c_h = 1.01 * (3 * 2.0 ** -16 + (3 * H + 64) * 2.0 ** -23)
+    w = _bf16_rne((rng.standard_normal((E, H)) * 0.03).astype(np.float32)).astype(np.float64)
+    for shift in (0.0, 50.0):
+        x = (rng.standard_normal(H) + shift).astype(np.float32)
+        hi = _bf16_rne(x)
+        lo = _bf16_rne(x - hi)
+        assert np.all(np.abs(x.astype(np.float64) - hi - lo) <= 2.0 ** -16 * np.abs(x))
+        terms = np.concatenate([w * hi.astype(np.float64)[None, :], w * lo.astype(np.float64)[None, :]], axis=1)
+        terms = terms[:, rng.permutation(2 * H)].astype(np.float32)   # each product exact in fp32
+        acc = np.zeros(E, np.float32)
+        for k in range(terms.shape[1]):
+            acc += terms[:, k]
+        exact = w @ x.astype(np.float64)
+        bound = c_h * np.linalg.norm(x.astype(np.float64)) * np.linalg.norm(w, axis=1)
+        assert np.all(np.abs(acc.astype(np.float64) - exact) <= bound)
