@@ -223,6 +223,23 @@ __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
     const size_t rb = static_cast<size_t>(H) * (RT::kChunk == 4 ? 4 : 2);
     const int nch = static_cast<int>(rb / 16);
     double *lg = reinterpret_cast<double *>(xs + ((H + 3) & ~3));
+    // wave 0 requests what its bounds need before the x row: the GEMM's K
+    // slices (at most kMaxRouterSplits), the norms and the bias, all with
+    // clamped indices so that the loads are unconditional and are waited for
+    // together
+    float lv[PL][kMaxRouterSplits], wv[PL], bv[PL];
+    if (wave == 0) {
+        const float *bp = bias ? bias : wn;
+#pragma unroll
+        for (int m = 0; m < PL; ++m) {
+            const int e = lane + m * kWave, ec = e < E ? e : 0;
+#pragma unroll
+            for (int z = 0; z < kMaxRouterSplits; ++z)
+                lv[m][z] = lap[(static_cast<size_t>(z < ks ? z : 0) * T + t) * E + ec];
+            wv[m] = wn[ec];
+            bv[m] = bp[ec];
+        }
+    }
     // x row to LDS; ||x|| in fp64 (rounded up)
     double ss = 0.0;
     const float4 *xr = reinterpret_cast<const float4 *>(x + static_cast<size_t>(t) * H);
@@ -244,20 +261,14 @@ __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
         for (int w = 0; w < kSelWaves; ++w)
             sx += xss[w];
         const double xb = cH * sqrt(sx) * (1.0 + 1e-6);
-        // the GEMM's K slices (at most kMaxRouterSplits), all requested
-        // first, then added in slice order (within the bound)
+        // the slices added in slice order (within the bound)
         float lsum[PL];
 #pragma unroll
         for (int m = 0; m < PL; ++m) {
-            const int e = lane + m * kWave;
-            float v[kMaxRouterSplits];
-#pragma unroll
-            for (int z = 0; z < kMaxRouterSplits; ++z)
-                v[z] = (e < E && z < ks) ? lap[(static_cast<size_t>(z) * T + t) * E + e] : 0.0f;
-            lsum[m] = v[0];
+            lsum[m] = lv[m][0];
 #pragma unroll
             for (int z = 1; z < kMaxRouterSplits; ++z)
-                lsum[m] += v[z];
+                lsum[m] += z < ks ? lv[m][z] : 0.0f;
         }
         // bounds as fp32 keys, lower bounds rounded down and upper bounds up
         uint32_t klo[PL], khi[PL];
@@ -268,9 +279,9 @@ __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
             klo[m] = khi[m] = 0u;
             if (e < E) {
                 const double lp = lsum[m];
-                const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+                const double b = bias ? static_cast<double>(bv[m]) : 0.0;
                 const double v = lp + b;
-                const double B = (xb * wn[e] + 1e-15 * (fabs(lp) + fabs(b)) + 1e-30) * (1.0 + 1e-9);
+                const double B = (xb * wv[m] + 1e-15 * (fabs(lp) + fabs(b)) + 1e-30) * (1.0 + 1e-9);
                 const double lo = v - B, hi = v + B;
                 klo[m] = f32_key(static_cast<float>(lo - fabs(lo) * 1e-6 - 1e-30));
                 khi[m] = f32_key(static_cast<float>(hi + fabs(hi) * 1e-6 + 1e-30));
