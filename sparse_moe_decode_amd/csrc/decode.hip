@@ -386,8 +386,11 @@ static_assert(kGuWaves * kWave == kRouteThreads, "gate/up workgroups route");
 // and then repeats the routing late.
 constexpr int kGuMinWaves = 6;
 // Few-row calls: four waves per SIMD (128 registers), enough for the two
-// sets of rows in flight.
+// sets of rows in flight of 2-bit rows; bf16 / fp32 rows (four 16-byte
+// chunks per row and lane) get three (168 registers: at four they spilled,
+// and R = 2 / 3 calls of the bf16 layer took 45 / 71 us instead of 41 / 58).
 constexpr int kGuMinWavesRows = 4;
+constexpr int kGuMinWavesRowsWide = 3;
 // Chunks per lane in flight per row: four 16-byte chunks (a 2048-wide bf16
 // row per wave), or one 2-bit block (a 2048-wide row per wave; wider rows
 // stream in steps).
@@ -685,7 +688,9 @@ __device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G,
 // 1 + b / wg_per_slot; workgroup b == 0 publishes the routing for the down pass
 // and the caller.
 template <int R, typename ET, typename ST>
-__global__ void __launch_bounds__(kGuWaves * kWave, R == 1 ? kGuMinWaves : kGuMinWavesRows) k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
+__global__ void __launch_bounds__(kGuWaves * kWave,
+                                  R == 1 ? kGuMinWaves : (ET::kChunk == 32 ? kGuMinWavesRows : kGuMinWavesRowsWide))
+    k_gateup(GateUpArgs p, RouteArgs ra, int n_sh)
 {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     float *xs = reinterpret_cast<float *>(lds_raw);   // [R][H]
