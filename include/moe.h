@@ -17,11 +17,18 @@
  *   - All pointers are raw. "device" means memory of the current HIP device
  *     (hipMalloc or a framework allocator), "host" means ordinary CPU memory.
  *   - The caller owns every buffer; the library never allocates or frees
- *     device memory and keeps no device state between calls (its only
- *     global state is a host-side, mutex-guarded cache of occupancy queries
- *     per kernel and device).
+ *     device memory and keeps no device state between calls. Its global
+ *     state is host-side and mutex-guarded: a cache of occupancy queries per
+ *     kernel and device, and per device one side stream with two events,
+ *     created by the first prefill call outside a stream capture and kept
+ *     until the process ends.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). GPU
- *     work is enqueued on it and the call returns without waiting.
+ *     work is enqueued on it and the call returns without waiting. A prefill
+ *     call (moe_forward with many rows) forks the shared expert's GEMMs onto
+ *     the side stream after an event on `stream` and joins them back with a
+ *     second event before its last kernel, so all of its work is still
+ *     ordered after earlier work on `stream` and before later work; inside a
+ *     stream capture this is a fork and join of the captured graph.
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns a negative moe_status and enqueues nothing. Device-side faults
  *     surface at the caller's next synchronization.

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "device_common.cuh"
 #include "internal.h"
@@ -1094,14 +1095,17 @@ static int router_splits(const moe_layer_desc *d, int T)
     const int ks = dense_splits(((d->n_experts + kGN - 1) / kGN) * ((T + 63) / 64), d->hidden);
     return ks < kMaxRouterSplits ? ks : kMaxRouterSplits;
 }
-static size_t kpart_bytes(const moe_layer_desc *d, int T)
+static size_t shared_kpart_bytes(const moe_layer_desc *d, int T)
 {
-    const int a = shared_gu_splits(d, T), b = shared_dn_splits(d, T), c = router_splits(d, T);
+    const int a = shared_gu_splits(d, T), b = shared_dn_splits(d, T);
     const size_t gu = a > 1 ? sizeof(float) * a * static_cast<size_t>(T) * 2 * d->shared_inter : 0;
     const size_t dn = b > 1 ? sizeof(float) * b * static_cast<size_t>(T) * d->hidden : 0;
-    const size_t lg = c > 1 ? sizeof(float) * c * static_cast<size_t>(T) * d->n_experts : 0;
-    const size_t m = gu > dn ? gu : dn;
-    return m > lg ? m : lg;
+    return gu > dn ? gu : dn;
+}
+static size_t router_kpart_bytes(const moe_layer_desc *d, int T)
+{
+    const int c = router_splits(d, T);
+    return c > 1 ? sizeof(float) * c * static_cast<size_t>(T) * d->n_experts : 0;
 }
 
 struct PrefillWs {
@@ -1110,7 +1114,8 @@ struct PrefillWs {
     uint4 *xh, *xl;
     float *lap;                      // approximate router logits [T][E]
     float *wn;                       // norms of the router rows [E]
-    float *kpart;                    // split-K partial sums of the dense GEMMs (router, shared expert)
+    float *kpart;                    // split-K partial sums of the router GEMM
+    float *kpart_sh;                 // split-K partial sums of the shared expert's GEMMs
     int32_t *ids;
     float *wts, *gate;
     int32_t *counts, *offsets, *perm, *inv, *tile_off;
@@ -1153,7 +1158,8 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.hsum = reinterpret_cast<float *>(take(sizeof(float) * P * (I / 32)));
     w.rout = reinterpret_cast<float *>(take(sizeof(float) * P * H));
     w.sout = reinterpret_cast<float *>(take(sizeof(float) * T * H));
-    w.kpart = reinterpret_cast<float *>(take(kpart_bytes(d, T)));
+    w.kpart = reinterpret_cast<float *>(take(router_kpart_bytes(d, T)));
+    w.kpart_sh = reinterpret_cast<float *>(take(shared_kpart_bytes(d, T)));
     w.sort_bytes = off;   // total, when not carving
     return w;
 }
@@ -1184,8 +1190,10 @@ static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s, in
     }
 }
 
+// Routed GEMMs on stream s; the shared expert's GEMMs on stream ss (s itself,
+// or a side stream that waits for the x split).
 template <typename ET, typename ST>
-static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm, hipStream_t s)
+static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm, hipStream_t s, hipStream_t ss)
 {
     const int H = d->hidden, E = d->n_experts, K = d->top_k, I = d->inter, Is = d->shared_inter;
     const int64_t P = static_cast<int64_t>(T) * K;
@@ -1227,12 +1235,12 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sg.hh = w.shh;
     sg.hl = w.shl;
     sg.hsum = nullptr;
-    sg.kpart = w.kpart;
+    sg.kpart = w.kpart_sh;
     const int gks = shared_gu_splits(d, T);
-    launch_ggemm<ST, true>(sg, 64, sh_tiles, s, gks);
+    launch_ggemm<ST, true>(sg, 64, sh_tiles, ss, gks);
     if (gks > 1) {
         const int64_t n = static_cast<int64_t>(T) * Is;
-        hipLaunchKernelGGL(k_dual_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart, gks, T,
+        hipLaunchKernelGGL(k_dual_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, ss, w.kpart_sh, gks, T,
                            Is, w.shh, w.shl);
     }
     // routed down: A = h of the pairs (sorted order)
@@ -1261,12 +1269,12 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sd.bstride = 0;
     sd.Kd = Is;
     sd.out = w.sout;
-    sd.kpart = w.kpart;
+    sd.kpart = w.kpart_sh;
     const int dks = shared_dn_splits(d, T);
-    launch_ggemm<ST, false>(sd, 64, sh_tiles, s, dks);
+    launch_ggemm<ST, false>(sd, 64, sh_tiles, ss, dks);
     if (dks > 1) {
         const int64_t n = static_cast<int64_t>(T) * H;
-        hipLaunchKernelGGL(k_single_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart, dks,
+        hipLaunchKernelGGL(k_single_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, ss, w.kpart_sh, dks,
                            T, H, w.sout);
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -1339,6 +1347,73 @@ static void split_x(const moe_layer_desc *d, const float *x, int T, const Prefil
         hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
 }
 
+// A side stream for the shared expert's GEMMs, which need only the x split
+// and so run beside the routing, sorting and routed GEMMs. One per device,
+// created on first use (not while the caller's stream is being captured),
+// with a fork and a join event; a mutex per device keeps each call's
+// record / wait sequence whole when calls come from several host threads.
+// Without it (creation failed, or first use inside a capture) the shared
+// GEMMs run on the caller's stream.
+class SideStream {
+public:
+    explicit SideStream(hipStream_t s) : s_(s)
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+            (void)hipGetLastError();
+            return;
+        }
+        Slot &sl = slots()[dev];
+        lock_ = std::unique_lock<std::mutex>(sl.mu);
+        if (!sl.ss) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+                (void)hipGetLastError();
+                return;
+            }
+            hipStream_t ss = nullptr;
+            hipEvent_t f = nullptr, j = nullptr;
+            if (hipStreamCreateWithFlags(&ss, hipStreamNonBlocking) != hipSuccess ||
+                hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                return;   // (handles that were created are kept unused)
+            }
+            sl.ss = ss;
+            sl.fork = f;
+            sl.join = j;
+        }
+        if (hipEventRecord(sl.fork, s) != hipSuccess || hipStreamWaitEvent(sl.ss, sl.fork, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        slot_ = &sl;
+    }
+    ~SideStream()
+    {
+        if (slot_ && (hipEventRecord(slot_->join, slot_->ss) != hipSuccess ||
+                      hipStreamWaitEvent(s_, slot_->join, 0) != hipSuccess))
+            (void)hipGetLastError();
+    }
+    hipStream_t stream() const { return slot_ ? slot_->ss : s_; }
+
+private:
+    static constexpr int kMaxDevices = 64;
+    struct Slot {
+        std::mutex mu;
+        hipStream_t ss = nullptr;
+        hipEvent_t fork = nullptr, join = nullptr;
+    };
+    static Slot *slots()
+    {
+        static Slot table[kMaxDevices];
+        return table;
+    }
+    hipStream_t s_;
+    Slot *slot_ = nullptr;
+    std::unique_lock<std::mutex> lock_;
+};
+
 int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t *ids, float *wts, float *gate,
                          void *ws, hipStream_t s)
 {
@@ -1347,14 +1422,14 @@ int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t
     return prefill_route(d, x, T, w, ids, wts, gate, s);
 }
 
-int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float *y, const int32_t *ids_in,
-                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
-                           float *gate_out, void *ws, hipStream_t s)
+// Everything between the x split and the combine: the routing (computed or
+// given), the sort, the tiles and the GEMMs (the shared expert's on ss).
+static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, const int32_t *ids_in,
+                          const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
+                          float *gate_out, hipStream_t s, hipStream_t ss)
 {
-    const int H = d->hidden, E = d->n_experts, K = d->top_k;
+    const int E = d->n_experts, K = d->top_k;
     const int64_t P = static_cast<int64_t>(T) * K;
-    const PrefillWs w = prefill_carve(ws, d, T, true);
-    split_x(d, x, T, w, ids_in == nullptr, s);
     int rc;
     if (ids_in) {
         hipLaunchKernelGGL(k_take_routing, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0, s, ids_in,
@@ -1371,15 +1446,27 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
     const int bm = routed_bm(P, E);
     hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off);
     const int et = d->expert_t, st = d->shared_t;
-    if (st == MOE_F32) {
-        rc = et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s)
-                           : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s)
-                                             : run_gemms<Q2, F32>(d, T, w, bm, s));
-    } else {
-        rc = et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s)
-                           : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s)
-                                             : run_gemms<Q2, BF16>(d, T, w, bm, s));
-    }
+    if (st == MOE_F32)
+        return et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s, ss)
+                             : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s, ss)
+                                               : run_gemms<Q2, F32>(d, T, w, bm, s, ss));
+    return et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s, ss)
+                         : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s, ss)
+                                           : run_gemms<Q2, BF16>(d, T, w, bm, s, ss));
+}
+
+int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float *y, const int32_t *ids_in,
+                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
+                           float *gate_out, void *ws, hipStream_t s)
+{
+    const int H = d->hidden, K = d->top_k;
+    const PrefillWs w = prefill_carve(ws, d, T, true);
+    split_x(d, x, T, w, ids_in == nullptr, s);
+    int rc;
+    {
+        const SideStream side(s);
+        rc = prefill_middle(d, x, T, w, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, s, side.stream());
+    }   // the side stream's work joins s here
     if (rc != MOE_OK)
         return rc;
     const int64_t n4 = static_cast<int64_t>(T) * H / 4;
