@@ -3,11 +3,11 @@
 // section "Chat defaults", processes 2048 prompt tokens per pass).
 //
 //   k_split_x         x (fp32) -> x_hi + x_lo (bf16 pair; x - hi - lo is
-//                     below 2^-17 |x|)
-//   k_logits64        router logits [T][E] and shared-gate logits [T] in
-//                     fp64 (v_mfma_f64_16x16x4_f64): exact products, a fixed
-//                     summation order
-//   k_select_rows     exact top-K per row (one wave per row), softmax weights,
+//                     below 2^-17 |x|), and the router row norms
+//   k_ggemm (router)  approximate router logits [T][E] (bf16 MFMA, bounded
+//                     error)
+//   k_select_approx   per row: the experts the bound cannot rule out, their
+//                     logits exactly in fp64, exact top-K, softmax weights,
 //                     sigmoid gate
 //   sort (sort.hip)   stable counting sort of the T*K (row, slot) pairs by
 //                     expert, with the inverse permutation
@@ -18,13 +18,15 @@
 //   k_ggemm           per (expert row tile, 256-column block): h times the
 //                     expert's down rows -> one output row per (row, slot)
 //   k_combine         y[t] = sum_k out[(t, k)] + g_t * shared(t)
-// The shared expert uses the same GEMM kernels over all rows.
+// The shared expert uses the same GEMM kernels over all rows, on a side
+// stream (SideStream) beside the routing and the routed GEMMs.
 //
 // MFMA precision: activations enter as bf16 hi+lo pairs; 2-bit weights as
-// their exact codes with the block scale applied to each 32-deep partial sum
-// and the block minima as a separate small GEMM; bf16 weights exactly; fp32
-// weights as hi+lo pairs. v_mfma_f32_16x16x32_bf16 accumulates in fp32; the
-// dropped lo*lo terms are below 2^-16 of each product.
+// the exact bf16 values 1 + c/4 of their codes with 4 x the block scale
+// applied to each 32-deep partial sum and (minimum - 4 scale) as a separate
+// small GEMM; bf16 weights exactly; fp32 weights as hi+lo pairs.
+// v_mfma_f32_16x16x32_bf16 accumulates in fp32; the dropped lo*lo terms are
+// below 2^-16 of each product.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -412,11 +414,12 @@ __global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, in
 //   A: bf16 hi/lo pairs of fp32 values (x - hi - lo below 2^-17 |x|); rows
 //      gathered by token (gate/up) or taken in sorted order (down).
 //   B: 2-bit blocks, bf16 (exact) or fp32 (as hi/lo pairs).
-// 2-bit weights enter as their codes, exact in bf16: each 32-deep step is one
-// block, t = A_hi.c + A_lo.c, acc += s * t with the block's scale s (per B
-// row); the minimum terms sum_b m[n][b] * asum[r][b] (asum: block sums of A,
-// m: block minima) are a second small GEMM with K = blocks (3 passes over
-// hi/lo pairs). bf16 weights: two passes (A_hi.w + A_lo.w); fp32 weights:
+// 2-bit weights enter as the bf16 values v = 1 + c/4 of their codes (exact):
+// each 32-deep step is one block, t = A_hi.v + A_lo.v, acc += 4s * t with the
+// block's scale s (per B row); the remaining terms
+// sum_b (m[n][b] - 4 s[n][b]) * asum[r][b] (asum: block sums of A, m: block
+// minima) are a second small GEMM with K = blocks (m and -4s as separate
+// operands, 3 passes over hi/lo pairs each). bf16 weights: two passes (A_hi.w + A_lo.w); fp32 weights:
 // three (A_hi.w_hi + A_hi.w_lo + A_lo.w_hi).
 // Workgroup: 4 waves, BM rows x kGN B rows. Gate/up (DUAL) puts the gate and
 // up rows of the same channels in the same wave (the LDS B rows alternate
