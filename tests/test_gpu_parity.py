@@ -283,6 +283,53 @@ def test_given_routing_entry():
         assert tolerance_ok(out.cpu().numpy(), y64).all()
 
 
+# --------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("rows", [1, 3, 300])   # decode, few-row, prefill (side stream)
+def test_graph_replay_matches_eager(rows):
+    """Calls captured into a HIP graph (as bench.py runs them) give the eager
+    results bit for bit on every replay, with other eager work on the same
+    layer and synchronizations between the replays. The prefill call forks
+    the shared expert's GEMMs onto the library's side stream inside the
+    capture."""
+    _say(f"case: graph replay rows={rows}")
+    import torch
+    import sparse_moe_decode_amd as moe
+    rng = np.random.default_rng(77 + rows)
+    a = _random_arrays(rng, 256, 32, 4, 96, 64, rstd=0.05)
+    a["router_bias"] = rng.standard_normal(32).astype(np.float32) * 0.5
+    G = gpu_layer_from_arrays(a)
+    T = 600 if rows == 300 else 12
+    x = torch.from_numpy(rng.standard_normal((T, 256)).astype(np.float32)).cuda()
+    other = torch.from_numpy(rng.standard_normal((T, 256)).astype(np.float32)).cuda()
+    ws = G.workspace(rows)
+
+    def run(src, y, ids):
+        for t in range(0, T, rows):
+            moe.forward(G.desc, src[t:t + rows], y[t:t + rows], ws, ids_out=ids[t:t + rows])
+
+    y_eager = torch.empty((T, 256), dtype=torch.float32, device="cuda")
+    ids_eager = torch.empty((T, 4), dtype=torch.int32, device="cuda")
+    run(x, y_eager, ids_eager)
+    torch.cuda.synchronize()
+    y_g = torch.full((T, 256), float("nan"), dtype=torch.float32, device="cuda")
+    ids_g = torch.full((T, 4), -1, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(x, y_g, ids_g)
+    torch.cuda.synchronize()
+    y_o = torch.empty_like(y_eager)
+    ids_o = torch.empty_like(ids_eager)
+    for rep in range(3):
+        y_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids_g.cpu().numpy(), ids_eager.cpu().numpy())
+        np.testing.assert_array_equal(y_g.cpu().numpy().view(np.uint32), y_eager.cpu().numpy().view(np.uint32))
+        run(other, y_o, ids_o)   # eager work between the replays
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------- prefill
 
 @pytest.mark.parametrize("fmt", ["f32", "bf16", "q2"])
