@@ -280,8 +280,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single "
-              f"MI355X in this build).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's kernels run on "
+              f"one MI355X; several GPUs would shard experts with one all-reduce of y, not implemented).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -60,12 +60,11 @@ int max_rows(const moe_layer_desc *d)
     return 1;
 }
 
-// Calls of up to this many rows run as few-row launches of up to kMaxRows
-// rows each when the layer allows groups of kMaxRows; larger calls take the
-// grouped prefill path. Measured on the 2-bit layer: four-row launches give
-// ~75k rows/s, while the prefill path pays a fixed cost that it recovers
-// only around 32 rows (5 rows: 17k rows/s, 32: 73k, 64: 121k).
-constexpr int kFewRowMaxT = 32;
+// Calls of up to this many rows run as few-row launches (see group_at) when
+// the layer allows groups of kMaxRows; larger calls take the grouped prefill
+// path. Measured on the 2-bit layer (us per call, few-row / prefill): 8 rows
+// 104 / 154, 12 rows 151 / 164, 14 rows 179 / 169, 16 rows 204 / 187.
+constexpr int kFewRowMaxT = 13;
 
 Path choose_path(const moe_layer_desc *d, int T)
 {
