@@ -1379,8 +1379,15 @@ public:
             if (hipStreamCreateWithFlags(&ss, hipStreamNonBlocking) != hipSuccess ||
                 hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
                 hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+                // release what was made; a later call tries again
+                if (j)
+                    (void)hipEventDestroy(j);
+                if (f)
+                    (void)hipEventDestroy(f);
+                if (ss)
+                    (void)hipStreamDestroy(ss);
                 (void)hipGetLastError();
-                return;   // (handles that were created are kept unused)
+                return;
             }
             sl.ss = ss;
             sl.fork = f;
