@@ -597,29 +597,60 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
     }
 }
 
-// Next step's B rows in registers (one B row per thread: kGN = 256 threads).
+// Next step's B rows in registers. All variants: init() once per workgroup,
+// load(step) for the 32-deep step, store() of that step to the LDS B tile.
 template <typename W>
 struct BStage;
+// bf16 weights: four lanes per B row, 16 bytes each, so one wave-wide load
+// covers 16 rows x 64 contiguous bytes; thread t holds LDS rows t/4 + 64q
+// (q = 0..3), part t%4. Plain loads: the dense weights are reread by every
+// row tile, so they stay in L2.
 template <>
 struct BStage<BF16> {
+    const uint8_t *row[4];   // this thread's 16-byte column of its B rows (row 0 for rows past the end)
+    uint32_t ok;             // bit q: row q exists
     uint4 v[4];
-    __device__ __forceinline__ void load(const uint8_t *M, int rows, int cols, int n, int blk)
+    template <bool DUAL, int BM>
+    __device__ __forceinline__ void init(const GemmArgs &p, int e, int n0, int tid)
     {
+        ok = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            v[q] = n < rows ? ld_nt16(M + (static_cast<size_t>(n) * cols + blk * 32 + q * 8) * 2) : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+            const uint8_t *m;
+            const int bn = gemm_brow<DUAL, BM>(p, e, n0, (tid >> 2) + 64 * q, m);
+            ok |= (bn < p.N ? 1u : 0u) << q;
+            row[q] = m + (static_cast<size_t>(bn < p.N ? bn : 0) * p.Kd + (tid & 3) * 8) * 2;
+        }
     }
-    __device__ __forceinline__ void store(uint16_t *Bh, uint16_t *, int row) const
+    __device__ __forceinline__ void load(int blk)
+    {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(row[q] + blk * 64);
+            v[q] = ((ok >> q) & 1u) ? w : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *Bh, uint16_t *, int tid) const
     {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint4 *>(Bh + row * kLD + q * 8) = v[q];
+            *reinterpret_cast<uint4 *>(Bh + ((tid >> 2) + 64 * q) * kLD + (tid & 3) * 8) = v[q];
     }
 };
+// fp32 weights (split to bf16 hi/lo when stored): one B row per thread.
 template <>
 struct BStage<F32> {
+    const uint8_t *M;
+    int n, rows, cols;
     uint4 v[8];
-    __device__ __forceinline__ void load(const uint8_t *M, int rows, int cols, int n, int blk)
+    template <bool DUAL, int BM>
+    __device__ __forceinline__ void init(const GemmArgs &p, int e, int n0, int tid)
+    {
+        n = gemm_brow<DUAL, BM>(p, e, n0, tid, M);
+        rows = p.N;
+        cols = p.Kd;
+    }
+    __device__ __forceinline__ void load(int blk)
     {
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -660,8 +691,6 @@ __global__ void __launch_bounds__(256) k_ggemm(GemmArgs p)
         return;
     const int e = Ltile[0], r0 = Ltile[1], nrows = Ltile[2];
     const int n0 = blockIdx.x * (DUAL ? kGN / 2 : kGN);
-    const uint8_t *bmat;
-    const int bn = gemm_brow<DUAL, BM>(p, e, n0, tid, bmat);
     const bool a_loader = tid < BM * 4;
     const int arow = (tid >> 2) % BM, apart = tid & 3;
     const int asrc = Ltok[arow];
@@ -679,16 +708,17 @@ __global__ void __launch_bounds__(256) k_ggemm(GemmArgs p)
     const int nsteps = (static_cast<int>(blockIdx.z) + 1) * nsteps_all / ks - s_begin;
     uint4 rah = make_uint4(0, 0, 0, 0), ral = rah;
     BStage<W> rb;
+    rb.template init<DUAL, BM>(p, e, n0, tid);
+    // unconditional loads (rows without a source read row 0, then zero)
+    const bool a_live = a_loader && asrc >= 0;
+    const size_t a_base = (static_cast<size_t>(a_live ? asrc : 0) * p.Kd + apart * 8) / 8;
     auto load_step = [&](int s) {
         s += s_begin;
-        if (a_loader && asrc >= 0) {
-            const size_t idx = (static_cast<size_t>(asrc) * p.Kd + s * 32 + apart * 8) / 8;
-            rah = reinterpret_cast<const uint4 *>(p.ah)[idx];
-            ral = reinterpret_cast<const uint4 *>(p.al)[idx];
-        } else {
-            rah = ral = make_uint4(0, 0, 0, 0);
-        }
-        rb.load(bmat, p.N, p.Kd, bn, s);
+        const uint4 h = reinterpret_cast<const uint4 *>(p.ah)[a_base + s * 4];
+        const uint4 l = reinterpret_cast<const uint4 *>(p.al)[a_base + s * 4];
+        rah = a_live ? h : make_uint4(0, 0, 0, 0);
+        ral = a_live ? l : make_uint4(0, 0, 0, 0);
+        rb.load(s);
     };
     load_step(0);
     for (int s = 0; s < nsteps; ++s) {
