@@ -257,7 +257,7 @@ def rows_sweep(args):
         ms, _ = time_steps(wl, max(2, args.steps // 2), 1)
         per_call = ms / 1e3 / wl.ncalls
         # the library's choice for this layer (4-row launches fit its shapes)
-        out[str(R)] = {"path": "decode" if R == 1 else ("few-row" if R <= 13 else "prefill"),
+        out[str(R)] = {"path": "decode" if R == 1 else ("few-row" if R <= 12 else "prefill"),
                        "calls": wl.ncalls, "us_per_call": round(per_call * 1e6, 3),
                        "rows_per_s": round(R / per_call, 1)}
     return {"workload": "rows_sweep", "config": cfg.name, "rows": out}

@@ -138,7 +138,7 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T,
  *   nothing. Otherwise routing is computed and,
  *   for each of ids_out / wts_out / gate_out that is non-NULL, written out.
  * Path by T: T == 1 decode; 2 <= T <= 4 few-row (the selected experts'
- * union is read once for all rows); 5 <= T <= 13 few-row launches of three
+ * union is read once for all rows); 5 <= T <= 12 few-row launches of three
  * rows (a remainder of one joins the last launch as four) when the layer's
  * shapes allow 4-row launches; larger T the prefill path (rows grouped by
  * expert, grouped bf16 MFMA GEMMs). The environment variable MOE_FORCE_PATH

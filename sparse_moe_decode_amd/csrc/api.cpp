@@ -63,8 +63,8 @@ int max_rows(const moe_layer_desc *d)
 // Calls of up to this many rows run as few-row launches (see group_at) when
 // the layer allows groups of kMaxRows; larger calls take the grouped prefill
 // path. Measured on the 2-bit layer (us per call, few-row / prefill): 8 rows
-// 104 / 154, 12 rows 151 / 164, 14 rows 179 / 169, 16 rows 204 / 187.
-constexpr int kFewRowMaxT = 13;
+// 104 / 147, 12 rows 151 / 157, 13 rows 166 / 159, 16 rows 204 / 181.
+constexpr int kFewRowMaxT = 12;
 
 Path choose_path(const moe_layer_desc *d, int T)
 {
