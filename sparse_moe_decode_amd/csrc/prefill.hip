@@ -382,8 +382,11 @@ __global__ void __launch_bounds__(256) k_take_routing(const int32_t *ids_in, con
         gate[i] = gate_in[i];
 }
 
-// Per-expert tile offsets: tile_off[e] = sum_{e' < e} ceil(count[e'] / bm).
-__global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, int bm, int32_t *tile_off)
+// Per-expert tile offsets: tile_off[e] = sum_{e' < e} ceil(count[e'] / bm),
+// and the expert of every row tile (tile_e[tix], tix < tile_off[E]), so that
+// a GEMM workgroup finds its expert with one load.
+__global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, int bm, int32_t *tile_off,
+                                                int32_t *tile_e)
 {
     __shared__ int s[kMaxE];
     const int t = threadIdx.x;
@@ -404,6 +407,19 @@ __global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, in
         tile_off[t] = s[t] - v;
     if (t == 0)
         tile_off[E] = s[E - 1];
+    // expert of tile tix: the first e whose inclusive sum exceeds tix
+    const int total = s[E - 1];
+    for (int tix = t; tix < total; tix += blockDim.x) {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s[mid] > tix)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        tile_e[tix] = lo;
+    }
 }
 
 // ================================================================= GEMMs
@@ -441,6 +457,7 @@ struct GemmShape {
 struct GemmArgs {
     int routed, T, K, E;
     const int32_t *tile_off;   // [E+1] (routed)
+    const int32_t *tile_e;     // [tiles] expert of each row tile (routed)
     const int32_t *offsets;    // [E+1] (routed)
     const int32_t *perm;       // [T*K] sorted row -> pair index (routed)
     const float *wts;          // [T*K] route weights by pair index (routed)
@@ -478,17 +495,9 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs &p, int *tile, int *tok
         int e = -1, r0 = 0, nr = 0;
         if (p.routed) {
             if (tix < p.tile_off[p.E]) {
-                int lo = 0, hi = p.E;   // largest e with tile_off[e] <= tix
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (p.tile_off[mid] <= tix)
-                        lo = mid;
-                    else
-                        hi = mid;
-                }
-                e = lo;
-                r0 = p.offsets[lo] + (tix - p.tile_off[lo]) * BM;
-                nr = min(BM, p.offsets[lo + 1] - r0);
+                e = p.tile_e[tix];
+                r0 = p.offsets[e] + (tix - p.tile_off[e]) * BM;
+                nr = min(BM, p.offsets[e + 1] - r0);
             }
         } else if (tix * BM < p.T) {
             e = 0;
@@ -1151,7 +1160,7 @@ struct PrefillWs {
     float *kpart_sh;                 // split-K partial sums of the shared expert's GEMMs
     int32_t *ids;
     float *wts, *gate;
-    int32_t *counts, *offsets, *perm, *inv, *tile_off;
+    int32_t *counts, *offsets, *perm, *inv, *tile_off, *tile_e;
     uint16_t *hh, *hl, *shh, *shl;   // h of the routed pairs [T*K][I] and of the shared expert [T][Is], bf16 hi/lo
     float *xsum, *hsum;              // 32-element block sums of x [T][H/32] and of h [T*K][I/32]
     float *rout, *sout;
@@ -1183,6 +1192,7 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.perm = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.inv = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.tile_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (E + 1)));
+    w.tile_e = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * ((P + 31) / 32 + E)));   // tiles at the smallest bm
     w.hh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
     w.hl = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
     w.shh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * T * Is));
@@ -1237,6 +1247,7 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     g.K = K;
     g.E = E;
     g.tile_off = w.tile_off;
+    g.tile_e = w.tile_e;
     g.offsets = w.offsets;
     g.perm = w.perm;
     g.wts = w.wts;
@@ -1484,7 +1495,7 @@ static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const 
     if (rc != MOE_OK)
         return rc;
     const int bm = routed_bm(P, E);
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off);
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off, w.tile_e);
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32)
         return et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s, ss)
