@@ -363,6 +363,25 @@ def test_prefill_small(fmt, T):
     assert_parity(run_calls(G, x, T, force_path="prefill"), ref, f"prefill {fmt} T={T}")
 
 
+@pytest.mark.parametrize("T", [8192, 16384])
+def test_prefill_router_slices_large_T(T):
+    """Large chunks on a 16-expert layer: the router GEMM already fills the
+    chip with few K slices, so it runs with 2 (8192 rows) and 1 (16384 rows)
+    slices; every row is compared with the oracle."""
+    _say(f"case: prefill bf16 router slices T={T}")
+    rng = np.random.default_rng(2000 + T)
+    a = _random_arrays(rng, 256, 16, 4, 96, 64, rstd=0.05, estd=0.05)
+    a["router_bias"] = rng.standard_normal(16).astype(np.float32) * 0.5
+    x = rng.standard_normal((T, 256)).astype(np.float32)
+    b = dict(a)
+    for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+        b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
+    ref = _oracle_ref(L, x)
+    assert_parity(run_calls(G, x, T), ref, f"prefill router slices T={T}")
+
+
 def test_prefill_forced_on_small_calls():
     """MOE_FORCE_PATH=prefill runs the grouped path for 1..3 rows per call."""
     _say("case: prefill forced for small calls")
