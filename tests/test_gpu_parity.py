@@ -184,6 +184,32 @@ def test_bf16_and_q2_small_shapes():
     assert_parity(run_calls(Gq, x, 11, force_path="prefill"), ref, "q2 prefill")
 
 
+def test_path_boundaries():
+    """Calls at the edges of the library's path choice on a 2-bit layer:
+    5 and 12 rows run as few-row launches of three (remainders of two and
+    none), 13 rows as one prefill chunk; 13 rows forced through few-row
+    launches (a remainder of one joining the last launch as four) must agree
+    as well."""
+    _say("case: path boundaries (5, 12, 13 rows)")
+    import oracle
+    rng = np.random.default_rng(43)
+    a = _random_arrays(rng, 256, 32, 6, 128, 64, rstd=0.05, estd=0.05)
+    b = dict(a)
+    for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+        b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    q = dict(b)
+    for k in ("exp_gate", "exp_up", "exp_down"):
+        q[k] = [oracle.q2_quantize(m) for m in a[k]]
+    L = oracle_layer_from_arrays(q, router_t="bf16", expert_t="q2", shared_t="bf16")
+    G = gpu_layer_from_arrays(dict(b, exp_gate=a["exp_gate"], exp_up=a["exp_up"], exp_down=a["exp_down"]),
+                              router_t="bf16", expert_t="q2", shared_t="bf16")
+    x = rng.standard_normal((60, 256)).astype(np.float32)
+    ref = _oracle_ref(L, x)
+    for rows in (5, 12, 13):
+        assert_parity(run_calls(G, x, rows), ref, f"boundary rows={rows}")
+    assert_parity(run_calls(G, x, 13, force_path="fewrow"), ref, "boundary rows=13 few-row")
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "q2"])
 def test_wide_rows_and_large_pair_sets(fmt):
     """Rows wider than one chunk set per wave (H = 2112: the streamed gate/up
