@@ -17,18 +17,14 @@
  *   - All pointers are raw. "device" means memory of the current HIP device
  *     (hipMalloc or a framework allocator), "host" means ordinary CPU memory.
  *   - The caller owns every buffer; the library never allocates or frees
- *     device memory and keeps no device state between calls. Its global
- *     state is host-side and mutex-guarded: a cache of occupancy queries per
- *     kernel and device, and per device one side stream with two events,
- *     created by the first prefill call outside a stream capture and kept
- *     until the process ends.
- *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). GPU
- *     work is enqueued on it and the call returns without waiting. A prefill
- *     call (moe_forward with many rows) forks the shared expert's GEMMs onto
- *     the side stream after an event on `stream` and joins them back with a
- *     second event before its last kernel, so all of its work is still
- *     ordered after earlier work on `stream` and before later work; inside a
- *     stream capture this is a fork and join of the captured graph.
+ *     device memory and keeps no device state between calls. Its only
+ *     global state is a host-side, mutex-guarded memo of occupancy queries
+ *     (workgroups a kernel keeps resident per device), which does not change
+ *     results.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     GPU work of a call is enqueued on it, in order, and the call returns
+ *     without waiting. Calls on different streams with different workspaces
+ *     are independent.
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns a negative moe_status and enqueues nothing. Device-side faults
  *     surface at the caller's next synchronization.
@@ -116,7 +112,11 @@ const char *moe_strerror(int status);
 size_t moe_workspace_bytes(const moe_layer_desc *d, int32_t T);
 
 /*
- * Routing only (router logits, top-K, softmax weights, shared gate).
+ * Routing only (router logits, top-K, softmax weights, shared gate): the
+ * single routing step of "Research notes, October 2026", section 1 ("Metal"
+ * bullet: router, top-k and shared gate computed together), with the tie
+ * rule (lower expert id first) that settles the exact router tie reported on
+ * the "Red Lite dev18" page, section "Scope boundary".
  *   x     [T][H]  fp32 device, 16-byte aligned
  *   ids   [T][K]  int32 device (out), ordered by logit desc, id asc
  *   wts   [T][K]  fp32 device (out)
@@ -130,7 +130,12 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T,
               void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The whole layer for T rows.
+ * The whole layer for T rows (the Qwen3-Next MoE block of the "Architecture"
+ * page, section "Qwen3-Next shape"; the shared expert as one more slot of
+ * the expert pass and the weighted reduce of "Research notes, October 2026",
+ * sections 1 and 4; several rows reading each selected expert once: the
+ * same page, section 1, MTP "Verify" bullet; prefill chunks: the "DwarfStar
+ * Red Lite" guide, section "Chat defaults").
  *   x [T][H] fp32 device (in), y [T][H] fp32 device (out, overwritten).
  *   If ids_in != NULL, the routing ids_in [T][K], wts_in [T][K] and
  *   gate_in [T] (device) is used as given (wts_in/gate_in must then be
@@ -141,9 +146,10 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T,
  * union is read once for all rows); 5 <= T <= 12 few-row launches of three
  * rows (a remainder of one joins the last launch as four) when the layer's
  * shapes allow 4-row launches; larger T the prefill path (rows grouped by
- * expert, grouped bf16 MFMA GEMMs). The environment variable MOE_FORCE_PATH
- * (decode | fewrow | prefill) overrides the choice; decode/fewrow then run
- * in such groups (one launch when T fits one).
+ * expert, grouped bf16 MFMA GEMMs), in chunks of rows whose workspace stays
+ * below 1.5 GiB (consecutive chunks reuse the workspace). The environment
+ * variable MOE_FORCE_PATH (decode | fewrow | prefill) overrides the choice;
+ * decode/fewrow then run in such groups (one launch when T fits one).
  */
 int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y,
                 const int32_t *ids_in, const float *wts_in, const float *gate_in,
@@ -151,7 +157,9 @@ int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y,
                 void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Prefill grouping step on its own: a stable counting sort of the T*K
+ * Prefill grouping step on its own (rows grouped by expert before the
+ * batched prefill GEMMs; "DwarfStar Red Lite" guide, "Chat defaults"): a
+ * stable counting sort of the T*K
  * (row, slot) pairs of ids [T][K] (device int32, values in [0, E)) by expert.
  *   counts  [E]    int32 device (out): pairs per expert
  *   offsets [E+1]  int32 device (out): exclusive prefix sum of counts
@@ -167,7 +175,10 @@ int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E,
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
- * 2-bit block format (MOE_Q2B32). The logical content of a [rows][cols] fp32
+ * 2-bit block format (MOE_Q2B32): 32-weight blocks as in the 32-weight
+ * chunks of the quantized matvec kernels ("Research notes, October 2026",
+ * section 4, narrow-row row), with the code width, fp16 scale and fp16
+ * minimum fixed by the layer's 2-bit configuration. The logical content of a [rows][cols] fp32
  * matrix (cols % 32 == 0): each run of 32 consecutive weights of a row is a
  * block with 2-bit codes c (0..3), an fp16 scale s and an fp16 minimum m;
  * the weight is fp32(c * s + m).
@@ -188,13 +199,14 @@ int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E,
  * cols <= 0 or cols % 32 != 0. */
 size_t moe_q2_packed_bytes(int64_t rows, int64_t cols);
 
-/* Host-only packer: src [rows][cols] fp32 (host) -> dst (host, dst_bytes >=
+/* Host-only packer (the quantizer above, applied block by block): src [rows][cols] fp32 (host) -> dst (host, dst_bytes >=
  * moe_q2_packed_bytes). Returns MOE_ENONFINITE if an input is NaN/Inf or a
  * block's min or scale does not fit fp16, MOE_EWORKSPACE if dst is too small. */
 int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes);
 
 /* Device unpack of one packed matrix to fp32 [rows][cols] (device), bit-exact
- * with the format definition. packed: device, 16-byte aligned. */
+ * with the format definition (w = fp32(c * s + m) above). packed: device,
+ * 16-byte aligned. */
 int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream);
 
 #ifdef __cplusplus

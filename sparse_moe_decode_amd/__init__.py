@@ -128,15 +128,69 @@ def workspace_bytes(desc: LayerDesc, T: int) -> int:
     return int(lib().moe_workspace_bytes(C.byref(desc), T))
 
 
-def route(desc: LayerDesc, x, ids, wts, gate, ws, stream=None) -> None:
+def _want(t, name, dtype, shape):
+    """Host-side checks of a tensor handed to the C ABI as a raw pointer: its
+    dtype, shape and contiguity, then that it lives on the GPU."""
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: on {t.device}, expected a GPU tensor")
+
+
+def _check_ws(ws):
+    import torch
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous() or not ws.is_cuda:
+        raise ValueError("ws: expected a contiguous GPU tensor")
+
+
+def _check_rows(desc: LayerDesc, x, y=None, ids=None, wts=None, gate=None, **more):
+    import torch
+    if x is None or x.dim() != 2:
+        raise ValueError("x: expected a [T, hidden] tensor")
     T = x.shape[0]
+    H, K = desc.hidden, desc.top_k
+    _want(x, "x", torch.float32, (T, H))
+    _want(y, "y", torch.float32, (T, H))
+    _want(ids, "ids", torch.int32, (T, K))
+    _want(wts, "wts", torch.float32, (T, K))
+    _want(gate, "gate", torch.float32, (T,))
+    for name, t in more.items():
+        kind = name.split("_")[0]
+        _want(t, name, torch.int32 if kind == "ids" else torch.float32, (T,) if kind == "gate" else (T, K))
+    _on_gpu(x=x, y=y, ids=ids, wts=wts, gate=gate, **more)
+    return T
+
+
+def route(desc: LayerDesc, x, ids, wts, gate, ws, stream=None) -> None:
+    T = _check_rows(desc, x, ids=ids, wts=wts, gate=gate)
+    for name, t in (("ids", ids), ("wts", wts), ("gate", gate)):
+        if t is None:
+            raise ValueError(f"{name}: required")
+    _check_ws(ws)
     _check(lib().moe_route(C.byref(desc), _ptr(x), T, _ptr(ids), _ptr(wts), _ptr(gate), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
 
 
 def forward(desc: LayerDesc, x, y, ws, ids_in=None, wts_in=None, gate_in=None, ids_out=None, wts_out=None,
             gate_out=None, stream=None) -> None:
-    T = x.shape[0]
+    T = _check_rows(desc, x, y, ids_in=ids_in, wts_in=wts_in, gate_in=gate_in, ids_out=ids_out,
+                    wts_out=wts_out, gate_out=gate_out)
+    if y is None:
+        raise ValueError("y: required")
+    _check_ws(ws)
     _check(lib().moe_forward(C.byref(desc), _ptr(x), T, _ptr(y), _ptr(ids_in), _ptr(wts_in), _ptr(gate_in),
                              _ptr(ids_out), _ptr(wts_out), _ptr(gate_out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
@@ -147,12 +201,27 @@ def sort_workspace_bytes(T: int, K: int, E: int) -> int:
 
 
 def sort_by_expert(ids, E: int, counts, offsets, perm, ws, stream=None) -> None:
+    import torch
+    if ids is None or ids.dim() != 2:
+        raise ValueError("ids: expected a [T, K] tensor")
     T, K = ids.shape
+    _want(ids, "ids", torch.int32, (T, K))
+    _want(counts, "counts", torch.int32, (E,))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(perm, "perm", torch.int32, (T * K,))
+    _on_gpu(ids=ids, counts=counts, offsets=offsets, perm=perm)
+    _check_ws(ws)
     _check(lib().moe_sort_by_expert(_ptr(ids), T, K, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_sort_by_expert")
 
 
 def q2_unpack(packed, rows: int, cols: int, dst, stream=None) -> None:
+    import torch
+    _want(dst, "dst", torch.float32, (rows, cols))
+    _on_gpu(dst=dst)
+    if packed.numel() * packed.element_size() < q2_packed_bytes(rows, cols) or not packed.is_contiguous() \
+            or not packed.is_cuda:
+        raise ValueError("packed: expected a contiguous GPU buffer of moe_q2_packed_bytes(rows, cols) bytes")
     _check(lib().moe_q2_unpack(_ptr(packed), rows, cols, _ptr(dst), _stream(stream)), "moe_q2_unpack")
 
 

@@ -6,7 +6,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 #include "internal.h"
 #include "moe.h"
 
@@ -113,13 +113,43 @@ int group_at(const moe_layer_desc *d, Path p, int T, int t)
     return rem < g ? rem : g;
 }
 
+// Rows per prefill chunk. The prefill kernels address their workspace
+// buffers with 32-bit offsets (buffer descriptors and int indices), so one
+// chunk's workspace stays below 1.5 GiB; a longer call runs as consecutive
+// chunks on the same workspace. MOE_PREFILL_CHUNK (rows) lowers the chunk
+// (to test the chunk loop on small calls).
+int prefill_chunk_rows(const moe_layer_desc *d)
+{
+    constexpr size_t kMaxChunkWs = static_cast<size_t>(3) << 29;
+    int lo = 1, hi = 1 << 22;   // largest T in [lo, hi) whose workspace fits
+    while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (moe::prefill_ws_bytes(d, mid) <= kMaxChunkWs)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const char *f = std::getenv("MOE_PREFILL_CHUNK");
+    if (f && *f) {
+        const long v = std::strtol(f, nullptr, 10);
+        if (v >= 1 && v < lo)
+            lo = static_cast<int>(v);
+    }
+    return lo;
+}
+
 size_t ws_bytes_for(const moe_layer_desc *d, int T)
 {
     if (T <= 0)
         return 256;
     const Path p = choose_path(d, T);
-    if (p == kPrefill)
-        return moe::prefill_ws_bytes(d, T);
+    if (p == kPrefill) {
+        const int c = prefill_chunk_rows(d);
+        if (T <= c)
+            return moe::prefill_ws_bytes(d, T);
+        const size_t full = moe::prefill_ws_bytes(d, c), rest = T % c ? moe::prefill_ws_bytes(d, T % c) : 0;
+        return full > rest ? full : rest;
+    }
     return static_cast<size_t>(moe::decode_ws_size(d, group_rows(d, p, T)));
 }
 
@@ -170,9 +200,18 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T, int32_t *ids, 
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Path path = choose_path(d, T);
-    if (path == kPrefill)
-        return moe::launch_prefill_route(d, x, T, ids, wts, gate, ws, s);
     const int H = d->hidden, K = d->top_k;
+    if (path == kPrefill) {
+        const int c = prefill_chunk_rows(d);
+        for (int t = 0; t < T; t += c) {
+            const int r = T - t < c ? T - t : c;
+            const size_t ok = static_cast<size_t>(t) * K;
+            rc = moe::launch_prefill_route(d, x + static_cast<size_t>(t) * H, r, ids + ok, wts + ok, gate + t, ws, s);
+            if (rc != MOE_OK)
+                return rc;
+        }
+        return MOE_OK;
+    }
     for (int t = 0, r = 0; t < T; t += r) {
         r = group_at(d, path, T, t);
         rc = moe::launch_decode_route(d, x + static_cast<size_t>(t) * H, r, ids + static_cast<size_t>(t) * K,
@@ -209,13 +248,12 @@ int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y, co
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Path path = choose_path(d, T);
-    if (path == kPrefill)
-        return moe::launch_prefill_forward(d, x, T, y, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, ws, s);
     const int H = d->hidden, K = d->top_k;
+    const int chunk = path == kPrefill ? prefill_chunk_rows(d) : 0;
     for (int t = 0, r = 0; t < T; t += r) {
-        r = group_at(d, path, T, t);
+        r = path == kPrefill ? (T - t < chunk ? T - t : chunk) : group_at(d, path, T, t);
         const size_t ok = static_cast<size_t>(t) * K;
-        rc = moe::launch_decode_forward(d, x + static_cast<size_t>(t) * H, r, y + static_cast<size_t>(t) * H,
+        rc = (path == kPrefill ? moe::launch_prefill_forward : moe::launch_decode_forward)(d, x + static_cast<size_t>(t) * H, r, y + static_cast<size_t>(t) * H,
                                         ids_in ? ids_in + ok : nullptr, ids_in ? wts_in + ok : nullptr,
                                         ids_in ? gate_in + t : nullptr, ids_out ? ids_out + ok : nullptr,
                                         wts_out ? wts_out + ok : nullptr, gate_out ? gate_out + t : nullptr, ws, s);

@@ -29,9 +29,9 @@
 #include <type_traits>
 #include <vector>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 #include "internal.h"
-#include "routing.cuh"
+#include "routing.hpp"
 
 namespace moe {
 

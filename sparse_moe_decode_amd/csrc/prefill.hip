@@ -18,8 +18,8 @@
 //   k_ggemm           per (expert row tile, 256-column block): h times the
 //                     expert's down rows -> one output row per (row, slot)
 //   k_combine         y[t] = sum_k out[(t, k)] + g_t * shared(t)
-// The shared expert uses the same GEMM kernels over all rows, on a side
-// stream (SideStream) beside the routing and the routed GEMMs.
+// The shared expert uses the same GEMM kernels over all rows. Everything runs
+// on the caller's stream, in order.
 //
 // MFMA precision: activations enter as bf16 hi+lo pairs; 2-bit weights as
 // the exact bf16 values 1 + c/4 of their codes with 4 x the block scale
@@ -30,11 +30,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <mutex>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 #include "internal.h"
-#include "routing.cuh"
+#include "routing.hpp"
 
 namespace moe {
 
@@ -1240,10 +1239,9 @@ static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s, in
     }
 }
 
-// Routed GEMMs on stream s; the shared expert's GEMMs on stream ss (s itself,
-// or a side stream that waits for the x split).
+// Routed and shared GEMMs on stream s, in order.
 template <typename ET, typename ST>
-static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm, hipStream_t s, hipStream_t ss)
+static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm, hipStream_t s)
 {
     const int H = d->hidden, E = d->n_experts, K = d->top_k, I = d->inter, Is = d->shared_inter;
     const int64_t P = static_cast<int64_t>(T) * K;
@@ -1288,10 +1286,10 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sg.hsum = nullptr;
     sg.kpart = w.kpart_sh;
     const int gks = shared_gu_splits(d, T);
-    launch_ggemm<ST, true>(sg, 64, sh_tiles, ss, gks);
+    launch_ggemm<ST, true>(sg, 64, sh_tiles, s, gks);
     if (gks > 1) {
         const int64_t n = static_cast<int64_t>(T) * Is;
-        hipLaunchKernelGGL(k_dual_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, ss, w.kpart_sh, gks, T,
+        hipLaunchKernelGGL(k_dual_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart_sh, gks, T,
                            Is, w.shh, w.shl);
     }
     // routed down: A = h of the pairs (sorted order)
@@ -1322,10 +1320,10 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     sd.out = w.sout;
     sd.kpart = w.kpart_sh;
     const int dks = shared_dn_splits(d, T);
-    launch_ggemm<ST, false>(sd, 64, sh_tiles, ss, dks);
+    launch_ggemm<ST, false>(sd, 64, sh_tiles, s, dks);
     if (dks > 1) {
         const int64_t n = static_cast<int64_t>(T) * H;
-        hipLaunchKernelGGL(k_single_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, ss, w.kpart_sh, dks,
+        hipLaunchKernelGGL(k_single_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w.kpart_sh, dks,
                            T, H, w.sout);
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
@@ -1398,80 +1396,6 @@ static void split_x(const moe_layer_desc *d, const float *x, int T, const Prefil
         hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
 }
 
-// A side stream for the shared expert's GEMMs, which need only the x split
-// and so run beside the routing, sorting and routed GEMMs. One per device,
-// created on first use (not while the caller's stream is being captured),
-// with a fork and a join event; a mutex per device keeps each call's
-// record / wait sequence whole when calls come from several host threads.
-// Without it (creation failed, or first use inside a capture) the shared
-// GEMMs run on the caller's stream.
-class SideStream {
-public:
-    explicit SideStream(hipStream_t s) : s_(s)
-    {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-            (void)hipGetLastError();
-            return;
-        }
-        Slot &sl = slots()[dev];
-        lock_ = std::unique_lock<std::mutex>(sl.mu);
-        if (!sl.ss) {
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-                (void)hipGetLastError();
-                return;
-            }
-            hipStream_t ss = nullptr;
-            hipEvent_t f = nullptr, j = nullptr;
-            if (hipStreamCreateWithFlags(&ss, hipStreamNonBlocking) != hipSuccess ||
-                hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-                hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-                // release what was made; a later call tries again
-                if (j)
-                    (void)hipEventDestroy(j);
-                if (f)
-                    (void)hipEventDestroy(f);
-                if (ss)
-                    (void)hipStreamDestroy(ss);
-                (void)hipGetLastError();
-                return;
-            }
-            sl.ss = ss;
-            sl.fork = f;
-            sl.join = j;
-        }
-        if (hipEventRecord(sl.fork, s) != hipSuccess || hipStreamWaitEvent(sl.ss, sl.fork, 0) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        slot_ = &sl;
-    }
-    ~SideStream()
-    {
-        if (slot_ && (hipEventRecord(slot_->join, slot_->ss) != hipSuccess ||
-                      hipStreamWaitEvent(s_, slot_->join, 0) != hipSuccess))
-            (void)hipGetLastError();
-    }
-    hipStream_t stream() const { return slot_ ? slot_->ss : s_; }
-
-private:
-    static constexpr int kMaxDevices = 64;
-    struct Slot {
-        std::mutex mu;
-        hipStream_t ss = nullptr;
-        hipEvent_t fork = nullptr, join = nullptr;
-    };
-    static Slot *slots()
-    {
-        static Slot table[kMaxDevices];
-        return table;
-    }
-    hipStream_t s_;
-    Slot *slot_ = nullptr;
-    std::unique_lock<std::mutex> lock_;
-};
-
 int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t *ids, float *wts, float *gate,
                          void *ws, hipStream_t s)
 {
@@ -1481,10 +1405,10 @@ int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t
 }
 
 // Everything between the x split and the combine: the routing (computed or
-// given), the sort, the tiles and the GEMMs (the shared expert's on ss).
+// given), the sort, the tiles and the GEMMs.
 static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, const int32_t *ids_in,
                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
-                          float *gate_out, hipStream_t s, hipStream_t ss)
+                          float *gate_out, hipStream_t s)
 {
     const int E = d->n_experts, K = d->top_k;
     const int64_t P = static_cast<int64_t>(T) * K;
@@ -1505,12 +1429,12 @@ static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const 
     hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off, w.tile_e);
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32)
-        return et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s, ss)
-                             : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s, ss)
-                                               : run_gemms<Q2, F32>(d, T, w, bm, s, ss));
-    return et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s, ss)
-                         : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s, ss)
-                                           : run_gemms<Q2, BF16>(d, T, w, bm, s, ss));
+        return et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s)
+                             : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s)
+                                               : run_gemms<Q2, F32>(d, T, w, bm, s));
+    return et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s)
+                         : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s)
+                                           : run_gemms<Q2, BF16>(d, T, w, bm, s));
 }
 
 int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float *y, const int32_t *ids_in,
@@ -1520,11 +1444,7 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
     const int H = d->hidden, K = d->top_k;
     const PrefillWs w = prefill_carve(ws, d, T, true);
     split_x(d, x, T, w, ids_in == nullptr, s);
-    int rc;
-    {
-        const SideStream side(s);
-        rc = prefill_middle(d, x, T, w, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, s, side.stream());
-    }   // the side stream's work joins s here
+    const int rc = prefill_middle(d, x, T, w, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, s);
     if (rc != MOE_OK)
         return rc;
     const int64_t n4 = static_cast<int64_t>(T) * H / 4;

@@ -4,7 +4,7 @@
 // add rounds once, so the result equals the format definition bit for bit.
 #include <hip/hip_runtime.h>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 #include "internal.h"
 
 namespace moe {

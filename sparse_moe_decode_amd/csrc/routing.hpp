@@ -7,7 +7,7 @@
 
 #include <cfloat>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 
 namespace moe {
 

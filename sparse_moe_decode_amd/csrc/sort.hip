@@ -12,7 +12,7 @@
 // unique. Optionally also the inverse permutation inv[pair] = sorted position.
 #include <hip/hip_runtime.h>
 
-#include "device_common.cuh"
+#include "device_common.hpp"
 #include "internal.h"
 
 namespace moe {

@@ -93,6 +93,52 @@ def test_call_validation():
     assert moe.lib().moe_workspace_bytes(C.byref(d), 2048) >= need
 
 
+def test_prefill_chunks_keep_workspace_bounded(monkeypatch):
+    """Long prefill calls run as chunks whose workspace stays below 1.5 GiB
+    (the prefill kernels address it with 32-bit offsets): the workspace of a
+    call of any length is that of its largest chunk, also at the largest
+    shapes the ABI accepts."""
+    limit = 3 << 29
+    for kw in (dict(), dict(hidden=8192, inter=4096, shared_inter=4096, top_k=16, n_experts=1024,
+                           expert_t=moe.MOE_Q2B32)):
+        d = _fake_desc(**kw)
+        big = moe.lib().moe_workspace_bytes(C.byref(d), 2 ** 31 - 1)
+        assert 0 < big <= limit
+        assert moe.lib().moe_workspace_bytes(C.byref(d), 10 ** 6) <= big
+    d = _fake_desc()
+    monkeypatch.setenv("MOE_PREFILL_CHUNK", "100")
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 1000) == moe.lib().moe_workspace_bytes(C.byref(d), 100)
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 250) == moe.lib().moe_workspace_bytes(C.byref(d), 100)
+    monkeypatch.delenv("MOE_PREFILL_CHUNK")
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 1000) > moe.lib().moe_workspace_bytes(C.byref(d), 100)
+
+
+def test_binding_rejects_bad_tensors():
+    """The Python binding checks dtype, shape, contiguity and device before
+    handing raw pointers to the library."""
+    torch = pytest.importorskip("torch")
+    d = _fake_desc(hidden=64, n_experts=8, top_k=2, inter=32, shared_inter=32)
+    x = torch.zeros((3, 64), dtype=torch.float32)
+    y = torch.zeros((3, 64), dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        moe.forward(d, x.double(), y, ws)
+    with pytest.raises(ValueError):
+        moe.forward(d, x[:, :32], y, ws)                      # hidden mismatch
+    with pytest.raises(ValueError):
+        moe.forward(d, x, y[:2], ws)                          # row count mismatch
+    with pytest.raises(ValueError):
+        moe.forward(d, torch.zeros((64, 3)).t(), y, ws)       # strided
+    with pytest.raises(TypeError):
+        moe.forward(d, x, y, ws, ids_out=torch.zeros((3, 2), dtype=torch.int64))
+    with pytest.raises(ValueError):
+        moe.forward(d, x, y, ws, ids_out=torch.zeros((3, 3), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        moe.forward(d, x, y, ws)                              # host tensors
+    with pytest.raises(ValueError):
+        moe.route(d, x, torch.zeros((3, 2), dtype=torch.int32), torch.zeros((3, 2)), None, ws)
+
+
 def test_sort_and_unpack_validation():
     L = moe.lib()
     assert L.moe_sort_by_expert(0x1000, 4, 0, 8, 0x2000, 0x3000, 0x4000, 0x5000, 1 << 20, None) == moe.MOE_EINVAL

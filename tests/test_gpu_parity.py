@@ -311,13 +311,11 @@ def test_given_routing_entry():
 
 # --------------------------------------------------------- graph capture
 
-@pytest.mark.parametrize("rows", [1, 3, 300])   # decode, few-row, prefill (side stream)
+@pytest.mark.parametrize("rows", [1, 3, 300])   # decode, few-row, prefill
 def test_graph_replay_matches_eager(rows):
     """Calls captured into a HIP graph (as bench.py runs them) give the eager
     results bit for bit on every replay, with other eager work on the same
-    layer and synchronizations between the replays. The prefill call forks
-    the shared expert's GEMMs onto the library's side stream inside the
-    capture."""
+    layer and synchronizations between the replays."""
     _say(f"case: graph replay rows={rows}")
     import torch
     import sparse_moe_decode_amd as moe
@@ -354,6 +352,75 @@ def test_graph_replay_matches_eager(rows):
         np.testing.assert_array_equal(y_g.cpu().numpy().view(np.uint32), y_eager.cpu().numpy().view(np.uint32))
         run(other, y_o, ids_o)   # eager work between the replays
         torch.cuda.synchronize()
+
+
+def test_two_streams_two_workspaces():
+    """Calls on two streams with two workspaces are independent: prefill and
+    decode calls interleaved on two streams (no ordering between them) both
+    match the oracle."""
+    _say("case: two streams, two workspaces (prefill and decode interleaved)")
+    import sparse_moe_decode_amd as moe
+    rng = np.random.default_rng(303)
+    a = _random_arrays(rng, 256, 32, 4, 96, 64, rstd=0.05)
+    a["router_bias"] = rng.standard_normal(32).astype(np.float32) * 0.5
+    G = gpu_layer_from_arrays(a)
+    L = oracle_layer_from_arrays(a)
+    xs = [rng.standard_normal((300, 256)).astype(np.float32) for _ in range(2)]
+    refs = [_oracle_ref(L, x) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for i in range(2):
+        T = 300
+        outs.append(dict(x=torch.from_numpy(xs[i]).cuda(), y=torch.empty((T, 256), device="cuda"),
+                         yd=torch.empty((T, 256), device="cuda"),
+                         ids=torch.empty((T, 4), dtype=torch.int32, device="cuda"),
+                         wts=torch.empty((T, 4), device="cuda"), gate=torch.empty((T,), device="cuda"),
+                         ws=G.workspace(300), wsd=G.workspace(1)))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in range(2):
+            o = outs[i]
+            moe.forward(G.desc, o["x"], o["y"], o["ws"], ids_out=o["ids"], wts_out=o["wts"], gate_out=o["gate"],
+                        stream=streams[i])
+        for t in range(0, 40):   # decode calls on both streams, alternating
+            for i in range(2):
+                o = outs[i]
+                moe.forward(G.desc, o["x"][t:t + 1], o["yd"][t:t + 1], o["wsd"], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        o = outs[i]
+        got = (o["ids"].cpu().numpy(), o["wts"].cpu().numpy(), o["gate"].cpu().numpy(), o["y"].cpu().numpy())
+        assert_parity(got, refs[i], f"stream {i} prefill")
+        yd = o["yd"].cpu().numpy()[:40]
+        assert tolerance_ok(yd, refs[i][3][:40]).all(), f"stream {i} decode"
+
+
+def test_prefill_in_chunks():
+    """A prefill call longer than the chunk runs as consecutive chunks on one
+    workspace (MOE_PREFILL_CHUNK lowers the chunk here): 600 rows as 256,
+    256 and 88, against the oracle, for moe_forward and moe_route."""
+    _say("case: prefill in chunks of 256 rows (600 rows)")
+    rng = np.random.default_rng(606)
+    a = _random_arrays(rng, 256, 32, 4, 96, 64, rstd=0.05)
+    a["router_bias"] = rng.standard_normal(32).astype(np.float32) * 0.5
+    G = gpu_layer_from_arrays(a)
+    L = oracle_layer_from_arrays(a)
+    x = rng.standard_normal((600, 256)).astype(np.float32)
+    ref = _oracle_ref(L, x)
+    old = os.environ.get("MOE_PREFILL_CHUNK")
+    os.environ["MOE_PREFILL_CHUNK"] = "256"
+    try:
+        assert G.workspace(600).numel() < G.workspace(300).numel() + 16
+        assert_parity(run_calls(G, x, 600), ref, "prefill chunks")
+        ids, wts, gate = G.route(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy(), ref[0])
+        assert tolerance_ok(wts.cpu().numpy(), ref[1]).all()
+    finally:
+        if old is None:
+            os.environ.pop("MOE_PREFILL_CHUNK", None)
+        else:
+            os.environ["MOE_PREFILL_CHUNK"] = old
 
 
 # ------------------------------------------------------------- prefill
