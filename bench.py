@@ -7,9 +7,12 @@ expert with a sigmoid gate, 1000 seeded tokens, one token per call, calls
 back to back on one stream. A step is one pass of the 1000-token stream
 through the layer. Dense weights (router, gate vector, shared expert) rotate
 over 48 layer instances so they are re-read from HBM as in a 48-layer model;
-routed experts (3.2 GB) are shared by the instances. The calls are captured
-once into a HIP graph and replayed; the timed region is K replays bracketed
-by device synchronizations and HIP events on the replay stream.
+the bf16 routed experts (3.2 GB, far beyond the 256 MB last-level cache) are
+shared by the instances, while the 2-bit lines give every instance its own
+copy of the routed stacks (48 x 604 MB). The calls are captured once into a
+HIP graph and replayed; the timed region is K replays bracketed by device
+synchronizations and HIP events on the replay stream (one event per step:
+the median step is reported beside the mean).
 
 Prints one JSON line. `roofline` covers the decode layer kernel(s):
 algorithmic bytes per call (selected experts, shared expert, router, gate
@@ -77,9 +80,13 @@ class Workload:
         self.stacks = mi.expert_stacks(cfg) if cfg.expert_t != "q2" else None
         base = gpu_layer_from_config(cfg, self.dense0, self.stacks)
         self.layers = [base]
+        # 2-bit stacks (604 MB) would partly stay in the 256 MB last-level
+        # cache across calls: each instance gets its own copy
+        self.distinct_experts = cfg.expert_t == "q2" and rotate > 1
         for i in range(1, rotate):
             d = mi.dense_weights(mi.layer_instance(cfg, i))
-            self.layers.append(base.with_dense(**d))
+            L = base.with_dense(**d)
+            self.layers.append(L.with_expert_copies() if self.distinct_experts else L)
         T = rows_per_call * ncalls
         self.x_host = mi.activations(cfg, T=T, instance=x_instance)
         self.x = torch.from_numpy(self.x_host).cuda()
@@ -117,31 +124,66 @@ class Workload:
         return np.array([len(np.unique(r)) for r in ids], np.float64)
 
 
-def time_steps(wl, steps: int, warmup: int):
+def time_steps(wl, steps: int, warmup: int, per_step: list | None = None):
+    """Mean ms per step over `steps` graph replays (events on the replay
+    stream); `per_step`, if given, receives each step's ms."""
     import torch
     for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         wl.step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps, wall
 
 
-def traffic_for(kernel_key: str, cfg_name: str):
-    """HBM bytes per call from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+def call_latency(wl, n: int = 200):
+    """Latency of one call (the first layer instance, one row group), from a
+    graph of that single call replayed n times, each replay between two
+    events; a long sleep kernel first lets the host queue every replay ahead
+    of the GPU so that the intervals hold no host gaps. Returns microseconds
+    (p50, p90, min)."""
+    import torch
+    import sparse_moe_decode_amd as moe
+    R, L = wl.R, wl.layers[0]
+    args = dict(ids_out=wl.ids[:R], wts_out=wl.wts[:R], gate_out=wl.gate[:R])
+    moe.forward(L.desc, wl.x[:R], wl.y[:R], wl.ws, **args)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(L.desc, wl.x[:R], wl.y[:R], wl.ws, **args)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for i in range(n):
+        ev[2 * i].record(stream)
+        g.replay()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.sort([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n)])
+    return round(float(np.percentile(us, 50)), 3), round(float(np.percentile(us, 90)), 3), round(float(us[0]), 3)
+
+
+def traffic_for(workload: str):
+    """HBM bytes per call from committed rocprofv3 counter runs of this
+    workload, if they were taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(f"{kernel_key}:{cfg_name}")
+        rec = json.load(f).get(workload)
     if not rec:
         return None
     if rec.get("source_sha") != source_sha():
@@ -156,27 +198,36 @@ def source_sha() -> str:
 
 # ---------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl, seconds: float):
-    """The CPU oracle, as it stands, on the workload's token stream (cycled)
-    with all available host cores (OpenMP over tokens), for about `seconds`."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
+def _oracle_rate(L, x_host, threads: int, seconds: float):
+    """Tokens/s of the oracle on the token stream x_host (cycled) with the
+    given OpenMP thread count, for about `seconds`."""
     import oracle
+    oracle.set_threads(threads)
+    threads = oracle.max_threads()
+    done, chunk, n_tok = 0, 4 * threads, x_host.shape[0]
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        s0 = done % n_tok
+        n = min(chunk, n_tok - s0)
+        L.forward(x_host[s0:s0 + n])
+        done += n
+    dt = time.perf_counter() - t0
+    return done, dt, threads
+
+
+def cpu_baseline(wl, seconds: float, single_seconds: float):
+    """The CPU oracle, as it stands, on the workload's token stream (cycled):
+    with all available host cores (OpenMP over tokens) for about `seconds`,
+    and on one thread for about `single_seconds`."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _layers import oracle_layer_from_config
     cfg = wl.cfg
     L = oracle_layer_from_config(cfg, dense=wl.dense0, stacks=wl.stacks)
     cores = len(os.sched_getaffinity(0))
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
-    oracle.set_threads(cores)
-    threads = oracle.max_threads()
-    done, chunk, n_tok = 0, 4 * threads, wl.x_host.shape[0]
-    t0 = time.perf_counter()
-    # the workload's token stream, cycled until `seconds` have passed
-    while time.perf_counter() - t0 < seconds:
-        s0 = done % n_tok
-        n = min(chunk, n_tok - s0)
-        L.forward(wl.x_host[s0:s0 + n])
-        done += n
-    dt = time.perf_counter() - t0
+    n_tok = wl.x_host.shape[0]
+    done, dt, threads = _oracle_rate(L, wl.x_host, cores, seconds)
+    done1, dt1, _ = _oracle_rate(L, wl.x_host, 1, single_seconds)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -189,15 +240,17 @@ def cpu_baseline(wl, seconds: float):
     return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} tokens: the {n_tok}-token {cfg.name} stream (layer instance 0) cycled "
                       f"{done / n_tok:.1f} times, {dt:.1f} s, double-precision oracle, OpenMP over tokens; "
-                      f"CPU: {cpu}"}
+                      f"CPU: {cpu}",
+            "single_thread": {"value": round(done1 / dt1, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"the first {done1} tokens of the same stream, {dt1:.1f} s, one thread"}}
 
 
 # ------------------------------------------------------------------ main
 
-def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0):
+def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0, per_step=None):
     wl = Workload(cfg, rows, ncalls, rotate, x_instance)
     wl.capture()
-    ms, wall = time_steps(wl, steps, warmup)
+    ms, wall = time_steps(wl, steps, warmup, per_step)
     return wl, ms, wall
 
 
@@ -218,18 +271,28 @@ def run_extra(args, keys):
         # one prefill call is about a millisecond: time more of them, after a
         # longer warm-up, so that clock ramp-up does not show in the figure
         steps, warm = (max(2, args.steps // 2), 1) if rows < 2048 else (max(20, args.steps), 5)
-        w2, m2, _ = measure(c, rows, ncalls, args.rotate if rows < 2048 else 1,
-                            steps, warm, x_instance=rows if idx == 3 else 0)
+        per = []
+        rot = args.rotate if rows < 2048 else 1
+        w2, m2, _ = measure(c, rows, ncalls, rot, steps, warm, x_instance=rows if idx == 3 else 0, per_step=per)
         u = w2.union_sizes()
         per_call = m2 / 1e3 / ncalls
-        rec = {"ms_per_step": round(m2, 4), "calls": ncalls, "rows_per_call": rows,
+        rec = {"ms_per_step": round(m2, 4), "median_ms_per_step": round(float(np.median(per)), 4),
+               "calls": ncalls, "rows_per_call": rows, "layer_instances": rot,
+               "distinct_expert_stacks": rot if w2.distinct_experts else 1,
                "rows_per_s": round(rows * ncalls / (m2 / 1e3), 1), "us_per_call": round(per_call * 1e6, 3)}
         if rows < 2048:
             b = float(np.mean([call_bytes(c, rows, n) for n in u]))
+            tr = traffic_for(key)
             rec.update({"bytes_per_call": round(b), "mean_expert_union": round(float(u.mean()), 3),
                         "GBps": round(b / per_call / 1e9, 1),
-                        "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4)})
+                        "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic_bytes_per_call": tr,
+                        "traffic_over_algorithmic": None if tr is None else round(tr / b, 4)})
+            p50, p90, mn = call_latency(w2)
+            rec.update({"hot_call_latency_us": {"p50": p50, "p90": p90, "min": mn}})
         else:
+            tr = traffic_for(key)
+            rec.update({"traffic_bytes_per_call": tr})
             flops = 2.0 * rows * (cfg.K * 3 * cfg.H * cfg.I + 3 * cfg.H * cfg.Is + cfg.E * cfg.H)
             rec.update({"useful_GFLOP": round(flops / 1e9, 2),
                         "TFLOPs": round(flops / per_call / 1e12, 2),
@@ -269,7 +332,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rotate", type=int, default=48, help="layer instances for the dense weights")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle on all host cores")
+    ap.add_argument("--cpu-single-seconds", type=float, default=8.0, help="oracle on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
     ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2"],
@@ -301,7 +365,8 @@ def main():
 
     cfg = mi.CONFIGS[1]
     print(f"[bench] building {cfg.name} workload, {args.rotate} dense-weight instances", file=sys.stderr, flush=True)
-    wl, ms, wall = measure(cfg, 1, cfg.T, args.rotate, args.steps, args.warmup)
+    per_step = []
+    wl, ms, wall = measure(cfg, 1, cfg.T, args.rotate, args.steps, args.warmup, per_step=per_step)
     tokens = cfg.T
     tok_s = tokens / (ms / 1e3)
     per_call_s = ms / 1e3 / tokens
@@ -310,7 +375,13 @@ def main():
     print(f"[bench] {cfg.name}: {ms:.3f} ms/step, {tok_s:.0f} tok/s, {achieved:.0f} GB/s", file=sys.stderr,
           flush=True)
 
-    extra = {}
+    p50, p90, mn = call_latency(wl)
+    extra = {"decode_bf16_timing": {
+        "median_ms_per_step": round(float(np.median(per_step)), 4),
+        "min_ms_per_step": round(float(np.min(per_step)), 4), "max_ms_per_step": round(float(np.max(per_step)), 4),
+        "hot_call_latency_us": {"p50": p50, "p90": p90, "min": mn,
+                                "how": "one call captured alone and replayed 200 times (its weights may stay "
+                                       "in the last-level cache between replays)"}}}
     if args.rotate != 1:
         wl1, ms1, _ = measure(cfg, 1, 200, 1, args.steps, args.warmup)
         extra["decode_bf16_single_instance"] = {
@@ -322,7 +393,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_single_seconds)
     del wl
     torch.cuda.empty_cache()
 
@@ -349,7 +420,7 @@ def main():
                    "dense_weight_instances": args.rotate, "timing": "HIP graph replay of 1000 calls"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("decode", cfg.name),
+                     "traffic": traffic_for(cfg.name),
                      "bytes_per_call": bytes_call, "us_per_call": round(per_call_s * 1e6, 3)},
         "cpu_baseline": cpu,
         "extra": extra,

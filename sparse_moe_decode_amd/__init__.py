@@ -292,6 +292,20 @@ class Layer:
         other.desc = d
         return other
 
+    def with_expert_copies(self) -> "Layer":
+        """The same layer with its routed expert stacks copied to new device
+        memory (identical bytes at other addresses), so that layers rotated in
+        a benchmark do not share cached expert lines."""
+        other = object.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+        other.exp_gate, other.exp_up, other.exp_down = (t.clone() for t in (self.exp_gate, self.exp_up,
+                                                                            self.exp_down))
+        d = LayerDesc()
+        C.memmove(C.byref(d), C.byref(self.desc), C.sizeof(LayerDesc))
+        d.exp_gate, d.exp_up, d.exp_down = _ptr(other.exp_gate), _ptr(other.exp_up), _ptr(other.exp_down)
+        other.desc = d
+        return other
+
     def _pack_stack(self, source, mat, rows, cols):
         import torch
         from concurrent.futures import ThreadPoolExecutor
