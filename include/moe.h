@@ -157,6 +157,25 @@ int moe_forward(const moe_layer_desc *d, const float *x, int32_t T, float *y,
                 void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The library keeps one scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (a static device array, held until the
+ * process ends) and runs moe_forward on it; this call itself allocates
+ * nothing. Arguments and results are those of moe_forward. Calls whose
+ * workspace (moe_workspace_bytes(d, T)) exceeds the scratch return
+ * MOE_EWORKSPACE and enqueue nothing: every decode and few-row call of any
+ * supported shape fits (at most 0.35 MiB), prefill calls only while their
+ * workspace does (about 20 rows at hidden 2048, 512 experts, top-10). All calls on one GPU share its scratch array: calls
+ * that overlap on one GPU (two streams, two host threads) race and must be
+ * ordered by the caller. The scratch needs no initialization.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_forward_noalloc(const moe_layer_desc *d, const float *x, int32_t T, float *y,
+                        const int32_t *ids_in, const float *wts_in, const float *gate_in,
+                        int32_t *ids_out, float *wts_out, float *gate_out, void *stream);
+
+/*
  * Prefill grouping step on its own (rows grouped by expert before the
  * batched prefill GEMMs; "DwarfStar Red Lite" guide, "Chat defaults"): a
  * stable counting sort of the T*K

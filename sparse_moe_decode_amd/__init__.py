@@ -21,7 +21,7 @@ MOE_F32, MOE_BF16, MOE_Q2B32 = 0, 1, 2
 WTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "q2": MOE_Q2B32}
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_forward",
-           "moe_sort_workspace_bytes", "moe_sort_by_expert", "moe_q2_packed_bytes", "moe_q2_pack",
+           "moe_forward_noalloc", "moe_sort_workspace_bytes", "moe_sort_by_expert", "moe_q2_packed_bytes", "moe_q2_pack",
            "moe_q2_unpack")
 
 
@@ -64,6 +64,8 @@ def lib():
             L.moe_route.restype = C.c_int
             L.moe_forward.argtypes = [C.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             L.moe_forward.restype = C.c_int
+            L.moe_forward_noalloc.argtypes = [C.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.moe_forward_noalloc.restype = C.c_int
             L.moe_sort_workspace_bytes.argtypes = [i32, i32, i32]
             L.moe_sort_workspace_bytes.restype = sz
             L.moe_sort_by_expert.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -194,6 +196,22 @@ def forward(desc: LayerDesc, x, y, ws, ids_in=None, wts_in=None, gate_in=None, i
     _check(lib().moe_forward(C.byref(desc), _ptr(x), T, _ptr(y), _ptr(ids_in), _ptr(wts_in), _ptr(gate_in),
                              _ptr(ids_out), _ptr(wts_out), _ptr(gate_out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20    # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def forward_noalloc(desc: LayerDesc, x, y, ids_in=None, wts_in=None, gate_in=None, ids_out=None, wts_out=None,
+                    gate_out=None, stream=None) -> None:
+    """moe_forward_noalloc: the layer on the library's own per-GPU scratch
+    (no workspace argument, nothing allocated by the call)."""
+    T = _check_rows(desc, x, y, ids_in=ids_in, wts_in=wts_in, gate_in=gate_in, ids_out=ids_out,
+                    wts_out=wts_out, gate_out=gate_out)
+    if y is None:
+        raise ValueError("y: required")
+    _check(lib().moe_forward_noalloc(C.byref(desc), _ptr(x), T, _ptr(y), _ptr(ids_in), _ptr(wts_in), _ptr(gate_in),
+                                     _ptr(ids_out), _ptr(wts_out), _ptr(gate_out), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def sort_workspace_bytes(T: int, K: int, E: int) -> int:
