@@ -55,6 +55,7 @@ class Desc(C.Structure):
         ("router_w", C.c_void_p), ("router_bias", C.c_void_p), ("gate_vec", C.c_void_p),
         ("exp_gate", C.c_void_p), ("exp_up", C.c_void_p), ("exp_down", C.c_void_p),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+        ("bias_mode", C.c_int32), ("residual", C.c_int32), ("norm_w", C.c_void_p), ("norm_eps", C.c_double),
     ]
 
 
@@ -78,6 +79,8 @@ def lib():
             L.oracle_layer.argtypes = [C.POINTER(Desc), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p, C.c_void_p]
             L.oracle_layer.restype = C.c_int
+            L.oracle_rmsnorm.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_double, C.c_void_p]
+            L.oracle_rmsnorm.restype = None
             L.oracle_max_threads.restype = C.c_int
             L.oracle_set_threads.argtypes = [C.c_int]
             _lib = L
@@ -129,19 +132,37 @@ def q2_dequantize(q: Q2) -> np.ndarray:
     return out
 
 
+# ----------------------------------------------------------------- norm
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """u = fp32(x / sqrt(mean(x^2) + eps) * gamma), row by row (oracle.c,
+    oracle_rmsnorm)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows = x.reshape(-1, x.shape[-1])
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.zeros_like(rows)
+    for r in range(rows.shape[0]):
+        lib().oracle_rmsnorm(rows[r].ctypes.data, rows.shape[1], g.ctypes.data, float(eps), out[r].ctypes.data)
+    return out.reshape(x.shape)
+
+
 # ---------------------------------------------------------------- layer
 
 class Layer:
     """Weights of one layer as the oracle reads them.
 
     router_w [E][H] and gate_vec [H] (f32 values or bf16 bits), optional
-    router_bias [E] fp32, per-expert matrices (a list of E arrays, or of
+    router_bias [E] fp32 (bias_mode 0: in the selection and the weights; 1:
+    in the selection only), per-expert matrices (a list of E arrays, or of
     ``Q2`` objects for 2-bit experts; entries may be None for experts that
-    are never selected), and the shared expert (f32 values or bf16 bits).
+    are never selected), the shared expert (f32 values or bf16 bits), and
+    optionally the pre-MoE RMS norm (norm_w [H] fp32, norm_eps) and the
+    residual (y = x + MoE(u)).
     """
 
     def __init__(self, *, H, E, K, I, Is, router_t, expert_t, shared_t, router_w, gate_vec,
-                 router_bias, exp_gate, exp_up, exp_down, sh_gate, sh_up, sh_down, renormalize=1):
+                 router_bias, exp_gate, exp_up, exp_down, sh_gate, sh_up, sh_down, renormalize=1,
+                 bias_mode=0, norm_w=None, norm_eps=1e-6, residual=0):
         self.H, self.E, self.K, self.I, self.Is = H, E, K, I, Is
         self._keep = []
 
@@ -159,6 +180,9 @@ class Layer:
             router_bias = np.ascontiguousarray(router_bias, dtype=np.float32)
             self._keep.append(router_bias)
         sh = [arr(m, shared_t) for m in (sh_gate, sh_up, sh_down)]
+        if norm_w is not None:
+            norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+            self._keep.append(norm_w)
 
         def table(mats):
             t = (C.c_void_p * E)()
@@ -178,7 +202,8 @@ class Layer:
         self.desc = Desc(H, E, K, I, Is, renormalize, WTYPE[router_t], WTYPE[expert_t], WTYPE[shared_t],
                          _ptr(router_w), _ptr(router_bias), _ptr(gate_vec),
                          C.addressof(tg), C.addressof(tu), C.addressof(td),
-                         _ptr(sh[0]), _ptr(sh[1]), _ptr(sh[2]))
+                         _ptr(sh[0]), _ptr(sh[1]), _ptr(sh[2]), int(bias_mode), int(residual), _ptr(norm_w),
+                         float(norm_eps))
 
     def route(self, x: np.ndarray):
         x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, self.H)

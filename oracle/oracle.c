@@ -22,6 +22,18 @@
  *     "Red Lite dev18" page, section "Scope boundary", reports an exact router
  *     tie that two implementations broke differently; this oracle fixes the
  *     rule (lower id first) so the result is unique.
+ *   - a per-expert router bias b_e: either added to the logits for both the
+ *     selection and the softmax weights (bias_mode 0), or used for the
+ *     selection only, the weights coming from the unbiased logits
+ *     (bias_mode 1: the opt-in cache-aware routing z + lambda * Delta *
+ *     cached of "Research notes, October 2026", section 4, where the bias
+ *     steers which experts are chosen);
+ *   - optionally (multi-layer stacks) the layer's input x is first
+ *     RMS-normalized and scaled, u = x / sqrt(mean(x^2) + eps) * gamma (the
+ *     RMS_NORM+SCALE that precedes the MoE block, fused there per the MoE
+ *     fusions row of the same page, section 4), u stored as fp32 like every
+ *     activation of the layer, and the output carries the residual,
+ *     y = x + MoE(u).
  *
  * Weight widening is exact: fp32 and bf16 values convert to double without
  * rounding; the 2-bit block format is decoded to fp32 first (its own
@@ -62,6 +74,10 @@ typedef struct {
     const void *sh_gate;         /* [Is][H], shared_t */
     const void *sh_up;           /* [Is][H] */
     const void *sh_down;         /* [H][Is] */
+    int32_t bias_mode;           /* 0: bias in selection and weights; 1: selection only */
+    int32_t residual;            /* 1: y = x + MoE(u) */
+    const float *norm_w;         /* [H] gamma, or NULL: u = x (no norm) */
+    double norm_eps;
 } oracle_desc;
 
 /* ---------------------------------------------------------------- fp16 */
@@ -222,7 +238,8 @@ static double dot(const double *a, const double *b, int64_t n)
 /* ------------------------------------------------------------- routing */
 
 typedef struct {
-    double l;
+    double l;   /* selection logit (with the bias) */
+    double w;   /* weight logit (with the bias in bias_mode 0, without it in bias_mode 1) */
     int32_t e;
 } scored;
 
@@ -235,7 +252,7 @@ static int by_logit_then_id(const void *pa, const void *pb)
     return (a->e > b->e) - (a->e < b->e);
 }
 
-/* Route one token. logits[E] receives l_e (including the bias). */
+/* Route one token. logits[E] receives the selection logits l_e + b_e. */
 static void route_one(const oracle_desc *d, const double *x, double *logits,
                       int32_t *ids, double *wts, double *gate, double *rowbuf, scored *sc)
 {
@@ -243,31 +260,60 @@ static void route_one(const oracle_desc *d, const double *x, double *logits,
     for (int64_t e = 0; e < E; ++e) {
         row_to_double(d->router_w, d->router_t, e, H, rowbuf);
         double l = dot(rowbuf, x, H);
-        if (d->router_bias)
-            l += (double)d->router_bias[e];
-        logits[e] = l;
-        sc[e].l = l;
+        double b = d->router_bias ? (double)d->router_bias[e] : 0.0;
+        logits[e] = l + b;
+        sc[e].l = l + b;
+        sc[e].w = d->bias_mode == 1 ? l : l + b;
         sc[e].e = (int32_t)e;
     }
     /* Brute force: a full sort of all experts by the selection order. */
     qsort(sc, (size_t)E, sizeof(scored), by_logit_then_id);
     for (int64_t k = 0; k < K; ++k)
         ids[k] = sc[k].e;
-    /* Softmax over the experts; m is the largest logit, which is sc[0]. */
-    double m = sc[0].l;
+    /* Softmax of the weight logits over the selected experts (renormalized)
+       or over all E, taken at the selected ones; m is the largest weight
+       logit of the set summed over. */
+    const int64_t n = d->renormalize ? K : E;
+    double m = sc[0].w;
+    for (int64_t i = 1; i < n; ++i)
+        if (sc[i].w > m)
+            m = sc[i].w;
     double denom = 0.0;
-    if (d->renormalize) {
-        for (int64_t k = 0; k < K; ++k)
-            denom += exp(sc[k].l - m);
-    } else {
-        for (int64_t e = 0; e < E; ++e)
-            denom += exp(sc[e].l - m);
-    }
+    for (int64_t i = 0; i < n; ++i)
+        denom += exp(sc[i].w - m);
     for (int64_t k = 0; k < K; ++k)
-        wts[k] = exp(sc[k].l - m) / denom;
+        wts[k] = exp(sc[k].w - m) / denom;
     row_to_double(d->gate_vec, d->router_t, 0, H, rowbuf);
     double z = dot(rowbuf, x, H);
     *gate = 1.0 / (1.0 + exp(-z));
+}
+
+/*
+ * RMS norm and scale of one row: u_h = fp32(x_h * r * gamma_h) with
+ * r = 1 / sqrt(sum_h x_h^2 / H + eps), everything in double until u is
+ * stored as fp32 (the layer's activation format).
+ */
+void oracle_rmsnorm(const float *x, int64_t H, const float *gamma, double eps, float *u)
+{
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h)
+        ss += (double)x[h] * (double)x[h];
+    const double r = 1.0 / sqrt(ss / (double)H + eps);
+    for (int64_t h = 0; h < H; ++h)
+        u[h] = (float)((double)x[h] * r * (double)gamma[h]);
+}
+
+/* The layer input of row t as double: x, or its RMS norm when the layer has one. */
+static void input_row(const oracle_desc *d, const float *x, int64_t t, float *ubuf, double *xd)
+{
+    const int64_t H = d->hidden;
+    const float *xr = x + t * H;
+    if (d->norm_w) {
+        oracle_rmsnorm(xr, H, d->norm_w, d->norm_eps, ubuf);
+        xr = ubuf;
+    }
+    for (int64_t h = 0; h < H; ++h)
+        xd[h] = (double)xr[h];
 }
 
 /* --------------------------------------------------------- expert FFN */
@@ -304,6 +350,12 @@ static int check_desc(const oracle_desc *d)
         return -1;
     if (d->expert_t == OR_Q2 && (d->hidden % 32 || d->inter % 32))
         return -1;
+    if (d->bias_mode != 0 && d->bias_mode != 1)
+        return -1;
+    if (d->residual != 0 && d->residual != 1)
+        return -1;
+    if (d->norm_w && !(d->norm_eps >= 0.0))
+        return -1;
     return 0;
 }
 
@@ -323,14 +375,14 @@ int oracle_route(const oracle_desc *d, const float *x, int64_t T,
         double *rowbuf = malloc(sizeof(double) * H);
         double *lg = malloc(sizeof(double) * E);
         scored *sc = malloc(sizeof(scored) * E);
-        if (!xd || !rowbuf || !lg || !sc) {
+        float *ubuf = malloc(sizeof(float) * H);
+        if (!xd || !rowbuf || !lg || !sc || !ubuf) {
 #pragma omp atomic write
             rc = -2;
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int64_t t = 0; t < T; ++t) {
-                for (int64_t h = 0; h < H; ++h)
-                    xd[h] = (double)x[t * H + h];
+                input_row(d, x, t, ubuf, xd);
                 route_one(d, xd, lg, ids + t * K, wts + t * K, gate + t, rowbuf, sc);
                 if (logits)
                     memcpy(logits + t * E, lg, sizeof(double) * E);
@@ -340,12 +392,14 @@ int oracle_route(const oracle_desc *d, const float *x, int64_t T,
         free(rowbuf);
         free(lg);
         free(sc);
+        free(ubuf);
     }
     return rc;
 }
 
 /*
- * Whole layer for T tokens (each token independently):
+ * Whole layer for T tokens (each token independently; with a norm, on the
+ * normalized input; with the residual, x is added to the output):
  *   ids[T][K] int32, wts[T][K] double, gate[T] double,
  *   y[T][H] float (the double result rounded once), y64[T][H] double or NULL.
  * Tokens are spread over OpenMP threads (set by the caller); every token is
@@ -371,14 +425,14 @@ int oracle_layer(const oracle_desc *d, const float *x, int64_t T,
         double *h = malloc(sizeof(double) * (nmax > 0 ? nmax : 1));
         double *dv = malloc(sizeof(double) * H);
         double *acc = malloc(sizeof(double) * H);
-        if (!xd || !rowbuf || !lg || !sc || !h || !dv || !acc) {
+        float *ubuf = malloc(sizeof(float) * H);
+        if (!xd || !rowbuf || !lg || !sc || !h || !dv || !acc || !ubuf) {
 #pragma omp atomic write
             rc = -2;
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int64_t t = 0; t < T; ++t) {
-                for (int64_t j = 0; j < H; ++j)
-                    xd[j] = (double)x[t * H + j];
+                input_row(d, x, t, ubuf, xd);
                 int32_t *tid = ids + t * K;
                 double *tw = wts + t * K;
                 route_one(d, xd, lg, tid, tw, gate + t, rowbuf, sc);
@@ -399,6 +453,9 @@ int oracle_layer(const oracle_desc *d, const float *x, int64_t T,
                 swiglu_ffn(d->sh_gate, d->sh_up, d->sh_down, d->shared_t, H, Is, xd, dv, rowbuf, h);
                 for (int64_t j = 0; j < H; ++j)
                     acc[j] += gate[t] * dv[j];
+                if (d->residual)   /* the residual stream: the un-normalized input */
+                    for (int64_t j = 0; j < H; ++j)
+                        acc[j] += (double)x[t * H + j];
                 for (int64_t j = 0; j < H; ++j) {
                     y[t * H + j] = (float)acc[j];
                     if (y64)
@@ -413,6 +470,7 @@ int oracle_layer(const oracle_desc *d, const float *x, int64_t T,
         free(h);
         free(dv);
         free(acc);
+        free(ubuf);
     }
     return rc;
 }

@@ -62,21 +62,37 @@ def load_hand_fixture(name="hand_layer_f32.json"):
         su[i, h] = v
     for j, i, v in g["sh_down"]:
         sd[j, i] = v
-    exp = g["expected"]
-    y = np.zeros((H,), np.float64)
-    for j, expr in exp["y_nonzero"].items():
-        y[int(j)] = eval_closed_form(expr)
-    expected = dict(ids=np.array(exp["ids"], np.int32),
-                    wts=np.array([eval_closed_form(s) for s in exp["wts"]]),
+    def expected_of(exp):
+        y = np.zeros((H,), np.float64)
+        for j, expr in exp["y_nonzero"].items():
+            y[int(j)] = eval_closed_form(expr)
+        return dict(ids=np.array(exp["ids"], np.int32), wts=np.array([eval_closed_form(s) for s in exp["wts"]]),
                     gate=eval_closed_form(exp["gate"]), y=y)
-    arrays = dict(H=H, E=E, K=g["K"], I=I, Is=Is, x=x, router_w=rw, gate_vec=gv, router_bias=None,
-                  exp_gate=eg, exp_up=eu, exp_down=ed, sh_gate=sg, sh_up=su, sh_down=sd)
+
+    expected = expected_of(g["expected"])
+    for k in g:   # further expectations of the same layer under other settings
+        if k.startswith("expected_"):
+            expected[k[len("expected_"):]] = expected_of(g[k])
+    bias = None
+    if "router_bias" in g:
+        bias = np.zeros((E,), np.float32)
+        for e, v in g["router_bias"]:
+            bias[e] = v
+    norm_w = None
+    if "norm_w" in g:
+        norm_w = np.ones((H,), np.float32)   # unlisted entries of gamma are 1
+        for h, v in g["norm_w"]:
+            norm_w[h] = v
+    arrays = dict(H=H, E=E, K=g["K"], I=I, Is=Is, x=x, router_w=rw, gate_vec=gv, router_bias=bias,
+                  exp_gate=eg, exp_up=eu, exp_down=ed, sh_gate=sg, sh_up=su, sh_down=sd,
+                  bias_mode=g.get("bias_mode", 0), norm_w=norm_w, norm_eps=g.get("norm_eps", 1e-6),
+                  residual=g.get("residual", 0))
     return arrays, expected
 
 
 def oracle_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_t="f32", renormalize=1):
     """Oracle layer from dense arrays (f32 values or bf16 bits; experts may be
-    a list of ``oracle.Q2``)."""
+    a list of ``oracle.Q2``); optional bias_mode, norm_w / norm_eps, residual."""
     import oracle
     E = a["E"]
     return oracle.Layer(H=a["H"], E=E, K=a["K"], I=a["I"], Is=a["Is"], router_t=router_t,
@@ -86,7 +102,8 @@ def oracle_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_
                         exp_up=[a["exp_up"][e] for e in range(E)],
                         exp_down=[a["exp_down"][e] for e in range(E)],
                         sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"],
-                        renormalize=renormalize)
+                        renormalize=renormalize, bias_mode=a.get("bias_mode", 0), norm_w=a.get("norm_w"),
+                        norm_eps=a.get("norm_eps", 1e-6), residual=a.get("residual", 0))
 
 
 def oracle_layer_from_config(cfg: mi.LayerConfig, dense=None, experts=None, stacks=None):

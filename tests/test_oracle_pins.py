@@ -428,3 +428,108 @@ def test_q2_layer_equals_dequantized_fp32_layer():
     rf = oracle_layer_from_arrays(fa).forward(x)
     for u, v in zip(rq, rf):
         np.testing.assert_array_equal(u, v)
+
+
+# ------------------------------------------- selection-only router bias
+
+def test_hand_fixture_bias_selection_only():
+    """hand_bias_select_only.json: a bias that ties two experts at the top;
+    bias_mode 1 weighs them by their unbiased logits, bias_mode 0 by the
+    biased (equal) ones."""
+    a, exp = load_hand_fixture("hand_bias_select_only.json")
+    for mode, e in ((1, exp), (0, exp["bias_mode_0"])):
+        L = oracle_layer_from_arrays(dict(a, bias_mode=mode))
+        ids, wts, gate, y, y64 = L.forward(a["x"])
+        np.testing.assert_array_equal(ids[0], e["ids"])
+        np.testing.assert_allclose(wts[0], e["wts"], rtol=0, atol=1e-15)
+        assert abs(gate[0] - e["gate"]) < 1e-15
+        np.testing.assert_allclose(y64[0], e["y"], rtol=1e-14, atol=1e-15)
+
+
+def test_bias_selection_only_invariants():
+    """bias 0: both modes equal the unbiased layer; a bias equal for every
+    expert: the same selection and (mode 1) the same weights as no bias; any
+    bias: both modes select the same experts, and mode 1's weights are the
+    softmax of the unbiased logits of that selection."""
+    rng = np.random.default_rng(77)
+    a = _random_arrays(rng, 96, 40, 6, 32, 32, rstd=0.1)
+    x = rng.standard_normal((12, 96)).astype(np.float32)
+    plain = oracle_layer_from_arrays(a).forward(x)
+    for mode in (0, 1):
+        r = oracle_layer_from_arrays(dict(a, router_bias=np.zeros(40, np.float32), bias_mode=mode)).forward(x)
+        for u, v in zip(plain, r):
+            np.testing.assert_array_equal(u, v)
+    const = oracle_layer_from_arrays(dict(a, router_bias=np.full(40, 0.75, np.float32), bias_mode=1)).forward(x)
+    np.testing.assert_array_equal(const[0], plain[0])
+    np.testing.assert_allclose(const[1], plain[1], rtol=0, atol=1e-15)
+    b = rng.standard_normal(40).astype(np.float32)
+    m0 = oracle_layer_from_arrays(dict(a, router_bias=b, bias_mode=0))
+    m1 = oracle_layer_from_arrays(dict(a, router_bias=b, bias_mode=1))
+    i0, w0, _, _ = m0.route(x)
+    i1, w1, _, sel = m1.route(x)
+    np.testing.assert_array_equal(i0, i1)
+    assert not np.array_equal(i1, plain[0])                         # the bias changed some selections
+    unb = sel - b.astype(np.float64)[None, :]                       # unbiased logits of every expert
+    for t in range(x.shape[0]):
+        v = unb[t, i1[t]]
+        ref = np.exp(v - v.max()) / np.exp(v - v.max()).sum()
+        np.testing.assert_allclose(w1[t], ref, rtol=1e-12, atol=1e-15)
+        v0 = sel[t, i0[t]]
+        np.testing.assert_allclose(w0[t], np.exp(v0 - v0.max()) / np.exp(v0 - v0.max()).sum(), rtol=1e-12)
+
+
+# ------------------------------------------------ RMS norm and residual
+
+def test_hand_fixture_norm_and_residual():
+    """hand_norm_residual.json: mean(x^2) = 4 and eps = 12 make r = 1/4
+    exactly; a missing sqrt, mean or eps changes every value."""
+    a, exp = load_hand_fixture("hand_norm_residual.json")
+    u = oracle.rmsnorm(a["x"], a["norm_w"], a["norm_eps"])
+    ref_u = np.zeros(32, np.float32)
+    ref_u[:8] = 1.0
+    ref_u[0], ref_u[1] = 0.25, 0.5
+    np.testing.assert_array_equal(u[0], ref_u)
+    L = oracle_layer_from_arrays(a)
+    ids, wts, gate, y, y64 = L.forward(a["x"])
+    np.testing.assert_array_equal(ids[0], exp["ids"])
+    np.testing.assert_allclose(wts[0], exp["wts"], rtol=0, atol=1e-15)
+    assert abs(gate[0] - exp["gate"]) < 1e-15
+    np.testing.assert_allclose(y64[0], exp["y"], rtol=1e-14, atol=1e-15)
+
+
+def test_rmsnorm_properties():
+    """Scaling x by a power of two leaves u unchanged (eps = 0); with gamma = 1
+    and eps = 0 the mean square of u is 1; eps enters under the root (a row
+    with mean square m and eps gives u = x / sqrt(m + eps)); an all-zero row
+    with eps > 0 gives zeros."""
+    rng = np.random.default_rng(8)
+    H = 256
+    x = rng.standard_normal((5, H)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    u = oracle.rmsnorm(x, g, 0.0)
+    np.testing.assert_array_equal(oracle.rmsnorm(x * np.float32(8.0), g, 0.0), u)
+    one = oracle.rmsnorm(x, np.ones(H, np.float32), 0.0).astype(np.float64)
+    np.testing.assert_allclose((one ** 2).mean(axis=1), 1.0, rtol=1e-6)
+    xc = np.full((1, H), 3.0, np.float32)                      # mean square 9, eps 7: r = 1/4
+    np.testing.assert_array_equal(oracle.rmsnorm(xc, np.ones(H, np.float32), 7.0), np.full((1, H), 0.75, np.float32))
+    np.testing.assert_array_equal(oracle.rmsnorm(np.zeros((1, H), np.float32), g, 1e-6), np.zeros((1, H), np.float32))
+
+
+def test_norm_of_unit_rows_and_residual():
+    """gamma = 1, eps = 0 and rows of +-1 (mean square 1): the norm is the
+    identity, so the layer with norm and residual equals x plus the plain
+    layer, to the rounding of the final sum; zero down matrices leave y = x
+    exactly."""
+    rng = np.random.default_rng(9)
+    H = 128
+    a = _random_arrays(rng, H, 24, 4, 64, 32)
+    x = np.where(rng.random((6, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    plain = oracle_layer_from_arrays(a).forward(x)
+    nr = oracle_layer_from_arrays(dict(a, norm_w=np.ones(H, np.float32), norm_eps=0.0, residual=1)).forward(x)
+    np.testing.assert_array_equal(nr[0], plain[0])
+    np.testing.assert_array_equal(nr[1], plain[1])
+    np.testing.assert_allclose(nr[4], plain[4] + x.astype(np.float64), rtol=0, atol=1e-13)
+    z = dict(a, exp_down=np.zeros_like(a["exp_down"]), sh_down=np.zeros_like(a["sh_down"]),
+             norm_w=rng.uniform(0.5, 2.0, H).astype(np.float32), residual=1)
+    xr = rng.standard_normal((6, H)).astype(np.float32)
+    np.testing.assert_array_equal(oracle_layer_from_arrays(z).forward(xr)[3], xr)
