@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1u
+#define MOE_ABI_VERSION 2u
 
 typedef enum {
     MOE_OK = 0,
@@ -52,6 +52,12 @@ typedef enum {
     MOE_EHIP = -5,          /* a HIP launch or runtime call failed */
     MOE_ENONFINITE = -6     /* packer: NaN/Inf input, or a block out of fp16 range */
 } moe_status;
+
+/* How router_bias enters the routing. */
+typedef enum {
+    MOE_BIAS_SELECT_AND_WEIGH = 0,  /* l_e + b_e for the selection and the softmax weights */
+    MOE_BIAS_SELECT_ONLY = 1        /* l_e + b_e for the selection; weights from the unbiased l_e */
+} moe_bias_mode;
 
 /* Weight storage formats. */
 typedef enum {
@@ -67,8 +73,8 @@ typedef enum {
  *
  * All weight pointers are device pointers, 16-byte aligned, row-major:
  *   router_w       [E][H]   router_t (MOE_F32 or MOE_BF16)
- *   router_bias    [E]      fp32, or NULL for no bias (added to the logits
- *                           before selection and softmax)
+ *   router_bias    [E]      fp32, or NULL for no bias; bias_mode says whether
+ *                           it enters the softmax weights too (see below)
  *   shared_gate_w  [H]      router_t (the vector w_g)
  *   exp_gate       E stacked [I][H] matrices, expert_t
  *   exp_up         E stacked [I][H] matrices, expert_t
@@ -84,17 +90,39 @@ typedef enum {
  *
  * renormalize: 1 = softmax over the K selected logits (the Qwen3-Next case),
  * 0 = the full softmax over all E, taken at the K selected experts.
+ *
+ * bias_mode (with router_bias): MOE_BIAS_SELECT_AND_WEIGH adds b_e to the
+ * logits for the selection and the weights (a skewed router);
+ * MOE_BIAS_SELECT_ONLY adds it for the selection only and weighs the chosen
+ * experts by their unbiased logits: the opt-in cache-aware routing
+ * z + lambda * Delta * cached of "Research notes, October 2026", section 4,
+ * with router_bias[e] = lambda * Delta * cached_e (cached_e = 1 for experts
+ * resident in the caller's expert cache, else 0).
+ *
+ * Multi-layer stacks ("Architecture" page, "Qwen3-Next shape": 48 MoE layers,
+ * each preceded by an RMS norm; RMS_NORM+SCALE and the tail fused into the
+ * MoE step, "Research notes, October 2026", section 4, MoE-fusions row):
+ *   norm_w    [H] fp32 gamma (device), or NULL: the layer's input u is x.
+ *             Otherwise, per row, r = 1 / sqrt(sum_h x_h^2 / H + eps) in
+ *             double and u_h = fp32(x_h * r * gamma_h); routing and experts
+ *             read u.
+ *   norm_eps  eps of that norm (fp32, >= 0).
+ *   residual  1: y = x + MoE(u) (x un-normalized); 0: y = MoE(u).
  */
 typedef struct moe_layer_desc {
     int32_t hidden, n_experts, top_k, inter, shared_inter;
     int32_t renormalize;
     int32_t router_t, expert_t, shared_t;
-    int32_t reserved;                  /* must be 0 */
+    int32_t bias_mode;                 /* moe_bias_mode */
     const void *router_w;
     const float *router_bias;
     const void *shared_gate_w;
     const void *exp_gate, *exp_up, *exp_down;
     const void *sh_gate, *sh_up, *sh_down;
+    const float *norm_w;               /* pre-MoE RMS norm gamma [H], or NULL */
+    float norm_eps;
+    int32_t residual;                  /* 0 or 1 */
+    int64_t reserved;                  /* must be 0 */
 } moe_layer_desc;
 
 /* MOE_ABI_VERSION of the loaded library. */

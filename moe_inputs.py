@@ -13,7 +13,7 @@ and chat prompts; seeded normal draws of the same shapes stand in for them.
 Seeding: one NumPy PCG64 stream per tensor, keyed by
 ``[20261203 + 100*config, stream, expert, matrix]``. Streams: 0 router,
 1 shared-gate vector, 2 routed experts, 3 shared expert, 4 activations x,
-5 router bias. Every expert matrix has its own stream, so any single expert
+5 router bias, 6 the pre-MoE norm's gamma (multi-layer stacks). Every expert matrix has its own stream, so any single expert
 can be regenerated without drawing the others.
 """
 from __future__ import annotations
@@ -32,6 +32,7 @@ STREAM_EXPERTS = 2
 STREAM_SHARED = 3
 STREAM_X = 4
 STREAM_BIAS = 5
+STREAM_NORM = 6
 
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
@@ -187,6 +188,14 @@ def dense_weights(cfg: LayerConfig) -> dict:
     out["sh_up"] = _store(_normal(_rng(cfg, STREAM_SHARED, 1), (cfg.Is, cfg.H), cfg.expert_std), cfg.shared_t)
     out["sh_down"] = _store(_normal(_rng(cfg, STREAM_SHARED, 2), (cfg.H, cfg.Is), cfg.expert_std), cfg.shared_t)
     return out
+
+
+def norm_weights(cfg: LayerConfig, layer: int = 0) -> np.ndarray:
+    """gamma[H] of a layer's pre-MoE RMS norm: 1 + N(0, 0.1) in fp32 (a
+    trained norm scale near one)."""
+    g = _normal(_rng(cfg, STREAM_NORM, layer), (cfg.H,), 0.1)
+    g += np.float32(1.0)
+    return g
 
 
 def activations(cfg: LayerConfig, T: int | None = None, instance: int = 0) -> np.ndarray:

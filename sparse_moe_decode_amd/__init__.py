@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EALIGN, MOE_EHIP, MOE_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
 MOE_F32, MOE_BF16, MOE_Q2B32 = 0, 1, 2
+MOE_BIAS_SELECT_AND_WEIGH, MOE_BIAS_SELECT_ONLY = 0, 1
 WTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "q2": MOE_Q2B32}
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_forward",
@@ -35,10 +36,11 @@ class LayerDesc(C.Structure):
     _fields_ = [
         ("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("inter", C.c_int32),
         ("shared_inter", C.c_int32), ("renormalize", C.c_int32), ("router_t", C.c_int32),
-        ("expert_t", C.c_int32), ("shared_t", C.c_int32), ("reserved", C.c_int32),
+        ("expert_t", C.c_int32), ("shared_t", C.c_int32), ("bias_mode", C.c_int32),
         ("router_w", C.c_void_p), ("router_bias", C.c_void_p), ("shared_gate_w", C.c_void_p),
         ("exp_gate", C.c_void_p), ("exp_up", C.c_void_p), ("exp_down", C.c_void_p),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+        ("norm_w", C.c_void_p), ("norm_eps", C.c_float), ("residual", C.c_int32), ("reserved", C.c_int64),
     ]
 
 
@@ -254,7 +256,7 @@ class Layer:
 
     def __init__(self, *, H, E, K, I, Is, router_t, expert_t, shared_t, router_w, gate_vec, router_bias,
                  sh_gate, sh_up, sh_down, exp_gate=None, exp_up=None, exp_down=None, expert_source=None,
-                 renormalize=1, device="cuda"):
+                 renormalize=1, bias_mode=0, norm_w=None, norm_eps=1e-6, residual=0, device="cuda"):
         import torch
         self.H, self.E, self.K, self.I, self.Is = H, E, K, I, Is
         self.router_t, self.expert_t, self.shared_t = router_t, expert_t, shared_t
@@ -273,6 +275,7 @@ class Layer:
         self.router_w = up(router_w, router_t)
         self.gate_vec = up(gate_vec, router_t)
         self.router_bias = up(None if router_bias is None else np.asarray(router_bias, np.float32))
+        self.norm_w = up(None if norm_w is None else np.asarray(norm_w, np.float32))
         self.sh_gate, self.sh_up, self.sh_down = up(sh_gate), up(sh_up), up(sh_down)
         if expert_t == "q2":
             # expert_source(e, mat) -> fp32 [rows][cols]; mat 0 gate, 1 up, 2 down
@@ -281,14 +284,16 @@ class Layer:
             self.exp_down = self._pack_stack(expert_source, 2, H, I)
         else:
             self.exp_gate, self.exp_up, self.exp_down = up(exp_gate), up(exp_up), up(exp_down)
-        self.desc = LayerDesc(H, E, K, I, Is, renormalize, WTYPE[router_t], WTYPE[expert_t], WTYPE[shared_t], 0,
-                              _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.gate_vec),
+        self.desc = LayerDesc(H, E, K, I, Is, renormalize, WTYPE[router_t], WTYPE[expert_t], WTYPE[shared_t],
+                              int(bias_mode), _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.gate_vec),
                               _ptr(self.exp_gate), _ptr(self.exp_up), _ptr(self.exp_down),
-                              _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down))
+                              _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down), _ptr(self.norm_w),
+                              float(norm_eps), int(residual), 0)
 
-    def with_dense(self, *, router_w, gate_vec, router_bias, sh_gate, sh_up, sh_down) -> "Layer":
+    def with_dense(self, *, router_w, gate_vec, router_bias, sh_gate, sh_up, sh_down, norm_w=None) -> "Layer":
         """Another layer of the same shape that shares this layer's routed
-        experts but has its own router, gate vector and shared expert."""
+        experts but has its own router, gate vector, shared expert (and norm
+        gamma, when this layer has a norm)."""
         import torch
         other = object.__new__(Layer)
         other.__dict__.update(self.__dict__)
@@ -302,10 +307,13 @@ class Layer:
         other.router_w, other.gate_vec = up(router_w), up(gate_vec)
         other.router_bias = up(None if router_bias is None else np.asarray(router_bias, np.float32))
         other.sh_gate, other.sh_up, other.sh_down = up(sh_gate), up(sh_up), up(sh_down)
+        if norm_w is not None:
+            other.norm_w = up(np.asarray(norm_w, np.float32))
         d = LayerDesc()
         C.memmove(C.byref(d), C.byref(self.desc), C.sizeof(LayerDesc))
         d.router_w, d.shared_gate_w = _ptr(other.router_w), _ptr(other.gate_vec)
         d.router_bias = _ptr(other.router_bias)
+        d.norm_w = _ptr(other.norm_w)
         d.sh_gate, d.sh_up, d.sh_down = _ptr(other.sh_gate), _ptr(other.sh_up), _ptr(other.sh_down)
         other.desc = d
         return other

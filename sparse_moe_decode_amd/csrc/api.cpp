@@ -22,6 +22,12 @@ int validate_desc(const moe_layer_desc *d)
         return MOE_EINVAL;
     if (d->reserved != 0)
         return MOE_EINVAL;
+    if (d->bias_mode != MOE_BIAS_SELECT_AND_WEIGH && d->bias_mode != MOE_BIAS_SELECT_ONLY)
+        return MOE_EINVAL;
+    if (d->residual != 0 && d->residual != 1)
+        return MOE_EINVAL;
+    if (d->norm_w && !(d->norm_eps >= 0.0f && d->norm_eps <= 3.0e38f))
+        return MOE_EINVAL;
     if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->inter <= 0 || d->shared_inter <= 0)
         return MOE_EINVAL;
     if (d->hidden % 32 || d->inter % 32 || d->shared_inter % 32)
@@ -45,6 +51,8 @@ int validate_desc(const moe_layer_desc *d)
             return MOE_EALIGN;
     }
     if (d->router_bias && (reinterpret_cast<uintptr_t>(d->router_bias) & 3u))
+        return MOE_EALIGN;
+    if (d->norm_w && !aligned16(d->norm_w))
         return MOE_EALIGN;
     return MOE_OK;
 }

@@ -136,6 +136,7 @@ struct RouteArgs {
     int32_t *ids_out;          // optional outputs
     float *wts_out, *gate_out;
     SlotTable *slots;          // published for the expert kernels (or null)
+    const float *wbias;        // the router bias when it enters the selection only (weights without it), or null
 };
 
 constexpr int kRouteThreads = 256;   // threads of every workgroup that routes
@@ -226,20 +227,20 @@ __device__ __forceinline__ void route_block1(const RouteArgs &a, double *lg, Rou
                 rl.cand_p[0][lane] = p;
             }
             if (!rank_packed(C, K, a.renorm, E, lg, z, false, 0, rl, lane, [&](uint64_t) { return val; },
-                             &rl.slots)) {
+                             &rl.slots, a.wbias)) {
                 if (lane < C) {
                     rl.cand[0][lane] = static_cast<int>(~static_cast<uint32_t>(p));
                     rl.cand_v[0][lane] = val;
                 }
                 rank_exact(C, K, 0, rl, lane);
-                wave_weights(lg, E, K, a.renorm, z, 0, rl, lane, false);
+                wave_weights(lg, E, K, a.renorm, z, 0, rl, lane, false, a.wbias);
                 if (lane < K) {
                     rl.slots.expert[lane + 1] = rl.sel_e[0][lane];
                     rl.slots.w[lane + 1][0] = rl.sel_w[0][lane];
                 }
             }
         } else {
-            wave_route(lg, E, K, a.renorm, z, 0, rl, lane);
+            wave_route(lg, E, K, a.renorm, z, 0, rl, lane, a.wbias);
             build_slots<1>(rl, K, lane);
         }
     } else if (wave == 1 && C <= kWave) {
@@ -311,7 +312,7 @@ __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, Rout
             }
         __syncthreads();
         if (wave < R) {
-            wave_route(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane);
+            wave_route(lg + wave * lgs, a.E, a.K, a.renorm, a.zlogit[wave], wave, rl, lane, a.wbias);
         }
     }
     __syncthreads();
@@ -368,6 +369,8 @@ __global__ void __launch_bounds__(kRouteThreads) k_route(RouteArgs a)
 
 struct GateUpArgs {
     const float *x;            // [R][H]
+    const float *norm_w;       // RMS norm gamma [H], or null
+    float norm_eps;
     int H, I, Is, Imax;
     const uint8_t *eg, *eu;    // routed gate/up stacks
     size_t estride;            // bytes per routed [I][H] matrix
@@ -555,9 +558,10 @@ __device__ __forceinline__ void dot_rows(Q2, const RowChunks<Q2> &r, int base, i
     }
 }
 
-// x of all rows into LDS, plus per-32 block sums when W is the 2-bit format.
+// x of all rows into LDS (with the layer's RMS norm applied when gamma is
+// given), plus per-32 block sums when W is the 2-bit format.
 template <int R, typename W>
-__device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float *xsum)
+__device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float *xsum, const float *gamma, float eps)
 {
     // 2-bit weights: chunk c of block b of a row at slot x_chunk_slot(b, c)
     const int n4 = H >> 2;
@@ -569,7 +573,14 @@ __device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float 
         }
         reinterpret_cast<float4 *>(xs)[d] = reinterpret_cast<const float4 *>(x)[i];
     }
-    __syncthreads();
+    if (gamma) {
+        if (W::kChunk == 32)
+            rms_norm_rows<R>(xs, H, gamma, eps, SlotsQ2{});
+        else
+            rms_norm_rows<R>(xs, H, gamma, eps, SlotsInOrder{});
+    } else {
+        __syncthreads();
+    }
     if (W::kChunk == 32) {
         for (int i = threadIdx.x; i < R * (H >> 5); i += blockDim.x) {
             float s = 0.0f;
@@ -668,14 +679,14 @@ __device__ __forceinline__ void gateup_one(const GateUpArgs &p, const MatRef &G,
         RowChunks<W> r;
         if (ch < n)
             load_rows(W{}, G, U, ch, 0, lane, nck, r);
-        stage_x<R, W>(p.x, p.H, xs, xsum);
+        stage_x<R, W>(p.x, p.H, xs, xsum, p.norm_w, p.norm_eps);
         if (ch < n) {
             dot_rows<R>(W{}, r, 0, lane, nck, xs, p.H, xsum, a, c);
             finish_channel<R>(p, pair, ch, a, c, wq, lane);
         }
         return;
     }
-    stage_x<R, W>(p.x, p.H, xs, xsum);
+    stage_x<R, W>(p.x, p.H, xs, xsum, p.norm_w, p.norm_eps);
     if (ch < n)
         gateup_wide<R, W>(p, G, U, pair, ch, wq, xs, xsum);
 }
@@ -727,7 +738,7 @@ __global__ void __launch_bounds__(kGuWaves * kWave,
     const int nck = p.H / ET::kChunk;
     if (nck > kWave * GuChunks<ET>::value) {
         // wide rows: each item streams its rows in steps
-        stage_x<R, ET>(p.x, p.H, xs, xsum);
+        stage_x<R, ET>(p.x, p.H, xs, xsum, p.norm_w, p.norm_eps);
         for (int it = b; it < nitems; it += stride) {
             int slot, ch;
             MatRef G, U;
@@ -754,7 +765,7 @@ __global__ void __launch_bounds__(kGuWaves * kWave,
             if (ch < p.I)
                 load_rows(ET{}, G, U, ch, 0, lane, nck, r);
             if (first)
-                stage_x<R, ET>(p.x, p.H, xs, xsum);
+                stage_x<R, ET>(p.x, p.H, xs, xsum, p.norm_w, p.norm_eps);
             if (ch < p.I)
                 routed_channel<R, ET>(p, r, rl.slots, slot, ch, xs, xsum, lane);
         };
@@ -770,7 +781,7 @@ __global__ void __launch_bounds__(kGuWaves * kWave,
         RowChunks<ET> cur, nxt;
         if (ch < p.I)
             load_rows(ET{}, G, U, ch, 0, lane, nck, cur);
-        stage_x<R, ET>(p.x, p.H, xs, xsum);
+        stage_x<R, ET>(p.x, p.H, xs, xsum, p.norm_w, p.norm_eps);
         while (true) {
             const int nx = it + stride;
             int nslot = 0, nch = 0;
@@ -796,6 +807,8 @@ __global__ void __launch_bounds__(kGuWaves * kWave,
 
 struct LogitArgs {
     const float *x;          // [R][H]
+    const float *norm_w;     // RMS norm gamma [H], or null
+    float norm_eps;
     int H, E;
     const uint8_t *router_w; // [E][H]
     const float *bias;       // [E] or null
@@ -828,7 +841,10 @@ __global__ void __launch_bounds__(256) k_logits(LogitArgs a)
     }
     for (int i = tid; i < R * a.H / 4; i += blockDim.x)
         reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(a.x)[i];
-    __syncthreads();
+    if (a.norm_w)
+        rms_norm_rows<R>(xs, a.H, a.norm_w, a.norm_eps, SlotsInOrder{});
+    else
+        __syncthreads();
     if (!live)
         return;
     double acc[R];
@@ -863,6 +879,7 @@ __global__ void __launch_bounds__(256) k_logits(LogitArgs a)
 
 struct DownArgs {
     float *y;                  // [R][H]
+    const float *xres;         // [R][H] the layer input added to y (residual), or null
     int H, I, Is, Imax;
     const uint8_t *ed;         // routed down stack
     size_t estride;            // bytes per routed [H][I] matrix
@@ -1185,7 +1202,7 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     for (int q = 0; q < R; ++q) {
         const float v = wave_sum(acc[q]) + gate[q] * wave_sum(sh[q]);
         if (lane == 0)
-            p.y[q * p.H + j] = v;
+            p.y[q * p.H + j] = p.xres ? p.xres[q * p.H + j] + v : v;
     }
 }
 
@@ -1215,6 +1232,8 @@ static GateUpArgs gateup_args(const moe_layer_desc *d, const float *x, const Dec
 {
     GateUpArgs g;
     g.x = x;
+    g.norm_w = d->norm_w;
+    g.norm_eps = d->norm_eps;
     g.H = d->hidden;
     g.I = d->inter;
     g.Is = d->shared_inter;
@@ -1270,6 +1289,8 @@ static int launch_logits_t(const moe_layer_desc *d, const float *x, int R, const
 {
     LogitArgs a;
     a.x = x;
+    a.norm_w = d->norm_w;
+    a.norm_eps = d->norm_eps;
     a.H = d->hidden;
     a.E = d->n_experts;
     a.router_w = static_cast<const uint8_t *>(d->router_w);
@@ -1308,6 +1329,7 @@ static RouteArgs route_args(const moe_layer_desc *d, const RoutingIO &io, const 
     a.wts_out = io.wts_out;
     a.gate_out = io.gate_out;
     a.slots = slots ? w.slots : nullptr;
+    a.wbias = d->bias_mode == MOE_BIAS_SELECT_ONLY ? d->router_bias : nullptr;
     return a;
 }
 
@@ -1362,6 +1384,7 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     }
     DownArgs dn;
     dn.y = y;
+    dn.xres = d->residual ? x : nullptr;
     dn.H = H;
     dn.I = I;
     dn.Is = Is;

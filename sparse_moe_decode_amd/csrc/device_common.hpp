@@ -220,6 +220,67 @@ __device__ __forceinline__ double wave_sum(double v)
     return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
+// Pre-MoE RMS norm of R rows of H fp32 values staged in LDS (row q at
+// xs + q * H), in place: u_h = fp32(x_h * r * gamma_h) with
+// r = 1 / sqrt(sum_h x_h^2 / H + eps); the sum of squares is in double (each
+// square is exact there; only the order of the additions differs from a
+// sequential sum), r and the products too, u rounded once. The float4 at
+// slot i of a row holds the values of float4 logical(i) (the 2-bit chunk
+// order of x). Every thread of the workgroup (at most 16 waves) calls it; it
+// begins and ends with a workgroup barrier.
+template <int R, typename Map>
+__device__ __forceinline__ void rms_norm_rows(float *xs, int H, const float *gamma, float eps, Map logical)
+{
+    __shared__ double part[R][16];
+    __shared__ double rr[R];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nw = blockDim.x / kWave;
+    const int n4 = H >> 2;
+    float4 *x4 = reinterpret_cast<float4 *>(xs);
+    __syncthreads();
+    for (int q = 0; q < R; ++q) {
+        double ss = 0.0;
+        for (int i = tid; i < n4; i += blockDim.x) {
+            const float4 v = x4[q * n4 + i];
+            ss += static_cast<double>(v.x) * v.x + static_cast<double>(v.y) * v.y + static_cast<double>(v.z) * v.z +
+                  static_cast<double>(v.w) * v.w;
+        }
+        ss = wave_sum(ss);
+        if (lane == 0)
+            part[q][wave] = ss;
+    }
+    __syncthreads();
+    if (tid < R) {
+        double t = 0.0;
+        for (int w = 0; w < nw; ++w)
+            t += part[tid][w];
+        rr[tid] = 1.0 / sqrt(t / H + static_cast<double>(eps));
+    }
+    __syncthreads();
+    const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+    for (int i = tid; i < n4; i += blockDim.x) {
+        const float4 g = g4[logical(i)];
+        for (int q = 0; q < R; ++q) {
+            const double r = rr[q];
+            float4 v = x4[q * n4 + i];
+            v.x = static_cast<float>(static_cast<double>(v.x) * r * static_cast<double>(g.x));
+            v.y = static_cast<float>(static_cast<double>(v.y) * r * static_cast<double>(g.y));
+            v.z = static_cast<float>(static_cast<double>(v.z) * r * static_cast<double>(g.z));
+            v.w = static_cast<float>(static_cast<double>(v.w) * r * static_cast<double>(g.w));
+            x4[q * n4 + i] = v;
+        }
+    }
+    __syncthreads();
+}
+
+// The float4 slot maps of rms_norm_rows: rows in order, or the 2-bit chunk
+// order (chunk c of 32-value block b at c ^ (b & 7), an involution).
+struct SlotsInOrder {
+    __device__ int operator()(int i) const { return i; }
+};
+struct SlotsQ2 {
+    __device__ int operator()(int i) const { return (i & ~7) | ((i & 7) ^ ((i >> 3) & 7)); }
+};
+
 __device__ __forceinline__ float silu_mul(float a, float c)
 {
     return a / (1.0f + __expf(-a)) * c;

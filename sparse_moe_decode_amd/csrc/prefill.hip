@@ -17,7 +17,10 @@
 //                     times the route weight -> h (bf16 hi/lo, sorted rows)
 //   k_ggemm           per (expert row tile, 256-column block): h times the
 //                     expert's down rows -> one output row per (row, slot)
-//   k_combine         y[t] = sum_k out[(t, k)] + g_t * shared(t)
+//   k_rmsnorm         (layers with a pre-MoE norm) u = RMS norm of x, the
+//                     input of everything above
+//   k_combine         y[t] = sum_k out[(t, k)] + g_t * shared(t) (+ x[t] with
+//                     the residual)
 // The shared expert uses the same GEMM kernels over all rows. Everything runs
 // on the caller's stream, in order.
 //
@@ -213,8 +216,8 @@ constexpr int kMaxRouterSplits = 8;   // K slices of the router GEMM, summed by 
 template <typename RT, int PL>
 __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
     const float *x, const float *lap, int ks, const float *wn, const uint8_t *router_w, const uint8_t *gate_w,
-    const float *bias, int T, int H, int E, int K, int renorm, double cH, int32_t *ids, float *wts, float *gate,
-    int32_t *ids_out, float *wts_out, float *gate_out)
+    const float *bias, const float *wbias, int T, int H, int E, int K, int renorm, double cH, int32_t *ids,
+    float *wts, float *gate, int32_t *ids_out, float *wts_out, float *gate_out)
 {
     extern __shared__ __align__(16) float xs[];   // [H] x row, then [E] exact logits (all-E path)
     __shared__ RouteLds rl;
@@ -344,9 +347,9 @@ __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
         return;
     if (C >= 0) {
         rank_exact(C, K, 0, rl, lane);
-        wave_weights(nullptr, E, K, renorm, zsh, 0, rl, lane);
+        wave_weights(nullptr, E, K, renorm, zsh, 0, rl, lane, true, wbias);
     } else {
-        wave_route(lg, E, K, renorm, zsh, 0, rl, lane);
+        wave_route(lg, E, K, renorm, zsh, 0, rl, lane, wbias);
     }
     __builtin_amdgcn_wave_barrier();
     if (lane < K) {
@@ -1086,7 +1089,8 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
 
 // y[t] = sum_k out[inv[t*K + k]] + g_t * shared[t]   (float4 per thread)
 __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const float *shared_out,
-                                                 const int32_t *inv, const float *gate, int T, int K, int H, float *y)
+                                                 const int32_t *inv, const float *gate, int T, int K, int H,
+                                                 const float *xres, float *y)
 {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int h4 = H / 4;
@@ -1104,7 +1108,27 @@ __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const 
         acc.z += v.z;
         acc.w += v.w;
     }
+    if (xres) {
+        const float4 xv = reinterpret_cast<const float4 *>(xres + static_cast<size_t>(t) * H)[c];
+        acc.x = xv.x + acc.x;
+        acc.y = xv.y + acc.y;
+        acc.z = xv.z + acc.z;
+        acc.w = xv.w + acc.w;
+    }
     reinterpret_cast<float4 *>(y + static_cast<size_t>(t) * H)[c] = acc;
+}
+
+// The layer's pre-MoE RMS norm, one row per workgroup: u = fp32(x r gamma)
+// (rms_norm_rows).
+__global__ void __launch_bounds__(256) k_rmsnorm(const float *x, int H, const float *gamma, float eps, float *u)
+{
+    extern __shared__ __align__(16) float row[];
+    const size_t off = static_cast<size_t>(blockIdx.x) * H;
+    for (int i = threadIdx.x; i < H / 4; i += blockDim.x)
+        reinterpret_cast<float4 *>(row)[i] = reinterpret_cast<const float4 *>(x + off)[i];
+    rms_norm_rows<1>(row, H, gamma, eps, SlotsInOrder{});
+    for (int i = threadIdx.x; i < H / 4; i += blockDim.x)
+        reinterpret_cast<float4 *>(u + off)[i] = reinterpret_cast<const float4 *>(row)[i];
 }
 
 // ============================================================ workspace
@@ -1170,6 +1194,7 @@ struct PrefillWs {
     uint16_t *hh, *hl, *shh, *shl;   // h of the routed pairs [T*K][I] and of the shared expert [T][Is], bf16 hi/lo
     float *xsum, *hsum;              // 32-element block sums of x [T][H/32] and of h [T*K][I/32]
     float *rout, *sout;
+    float *u;                        // the normalized input [T][H] (layers with a norm)
 };
 
 static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool carve)
@@ -1209,6 +1234,7 @@ static PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.sout = reinterpret_cast<float *>(take(sizeof(float) * T * H));
     w.kpart = reinterpret_cast<float *>(take(router_kpart_bytes(d, T)));
     w.kpart_sh = reinterpret_cast<float *>(take(shared_kpart_bytes(d, T)));
+    w.u = reinterpret_cast<float *>(take(d->norm_w ? sizeof(float) * T * H : 0));
     w.sort_bytes = off;   // total, when not carving
     return w;
 }
@@ -1359,15 +1385,16 @@ static void prefill_route_t(const moe_layer_desc *d, const float *x, int T, cons
     const float *lap = ks > 1 ? w.kpart : w.lap;
     const double cH = 1.01 * (3.0 * std::ldexp(1.0, -16) + (3.0 * H + 64.0) * std::ldexp(1.0, -23));
     const size_t lds = sizeof(float) * ((H + 3) & ~3) + sizeof(double) * E;
+    const float *wb = d->bias_mode == MOE_BIAS_SELECT_ONLY ? d->router_bias : nullptr;
     if (E <= 8 * kWave)
         hipLaunchKernelGGL((k_select_approx<RT, 8>), dim3(T), dim3(kSelWaves * kWave), lds, s, x, lap, ks, w.wn,
                            static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
+                           d->router_bias, wb, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
                            gate_out);
     else
         hipLaunchKernelGGL((k_select_approx<RT, kMaxE / kWave>), dim3(T), dim3(kSelWaves * kWave), lds, s, x, lap, ks, w.wn,
                            static_cast<const uint8_t *>(d->router_w), static_cast<const uint8_t *>(d->shared_gate_w),
-                           d->router_bias, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
+                           d->router_bias, wb, T, H, E, K, d->renormalize, cH, w.ids, w.wts, w.gate, ids_out, wts_out,
                            gate_out);
 }
 
@@ -1396,12 +1423,23 @@ static void split_x(const moe_layer_desc *d, const float *x, int T, const Prefil
         hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
 }
 
+// The layer's input: x, or its RMS norm (k_rmsnorm into the workspace).
+static const float *layer_input(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, hipStream_t s)
+{
+    if (!d->norm_w)
+        return x;
+    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), sizeof(float) * d->hidden, s, x, d->hidden, d->norm_w,
+                       d->norm_eps, w.u);
+    return w.u;
+}
+
 int launch_prefill_route(const moe_layer_desc *d, const float *x, int T, int32_t *ids, float *wts, float *gate,
                          void *ws, hipStream_t s)
 {
     const PrefillWs w = prefill_carve(ws, d, T, true);
-    split_x(d, x, T, w, true, s);
-    return prefill_route(d, x, T, w, ids, wts, gate, s);
+    const float *u = layer_input(d, x, T, w, s);
+    split_x(d, u, T, w, true, s);
+    return prefill_route(d, u, T, w, ids, wts, gate, s);
 }
 
 // Everything between the x split and the combine: the routing (computed or
@@ -1443,13 +1481,14 @@ int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float
 {
     const int H = d->hidden, K = d->top_k;
     const PrefillWs w = prefill_carve(ws, d, T, true);
-    split_x(d, x, T, w, ids_in == nullptr, s);
-    const int rc = prefill_middle(d, x, T, w, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, s);
+    const float *u = layer_input(d, x, T, w, s);
+    split_x(d, u, T, w, ids_in == nullptr, s);
+    const int rc = prefill_middle(d, u, T, w, ids_in, wts_in, gate_in, ids_out, wts_out, gate_out, s);
     if (rc != MOE_OK)
         return rc;
     const int64_t n4 = static_cast<int64_t>(T) * H / 4;
     hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s, w.rout, w.sout,
-                       w.inv, w.gate, T, K, H, y);
+                       w.inv, w.gate, T, K, H, d->residual ? x : nullptr, y);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -113,21 +113,28 @@ __device__ __forceinline__ void rank_exact(int C, int K, int q, RouteLds &rl, in
     __builtin_amdgcn_wave_barrier();
 }
 
+// Weight logit of expert e from its selection logit l: l itself, or l - b_e
+// when the router bias enters the selection only (wb = the bias, else null).
+__device__ __forceinline__ double weight_logit(double l, int e, const float *wb)
+{
+    return wb ? l - static_cast<double>(wb[e]) : l;
+}
+
 // Route weights of row q by the wave that selected it, in selection order:
-// w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the selection
-// (renormalized) or over all E logits; the gate sigmoid(z_q) = 1/(1+exp(-z_q)).
-// The differences l_k - l_0 (<= 0) are taken in fp64 and rounded once; the
-// exponentials, sums and quotients are fp32 (the outputs are fp32). Lane k < K
-// evaluates exp(l_k - l_0), lane K evaluates exp(-z), in one pass; sums are
-// wave reductions in a fixed order.
+// w_k = exp(v_k - v_0) / sum_j exp(v_j - v_0) over the selection
+// (renormalized) or over all E, with v the weight logits (weight_logit); the
+// gate sigmoid(z_q) = 1/(1+exp(-z_q)). The differences v_k - v_0 are taken
+// in fp64 and rounded once; the exponentials, sums and quotients are fp32
+// (the outputs are fp32). Lane k < K evaluates exp(v_k - v_0), lane K
+// evaluates exp(-z), in one pass; sums are wave reductions in a fixed order.
 __device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
-                                             int lane, bool gate = true)
+                                             int lane, bool gate = true, const float *wb = nullptr)
 {
     __builtin_amdgcn_wave_barrier();
-    const double l0 = rl.sel_l[q][0];
+    const double l0 = weight_logit(rl.sel_l[q][0], rl.sel_e[q][0], wb);
     float arg = 0.0f;
     if (lane < K)
-        arg = static_cast<float>(rl.sel_l[q][lane] - l0);
+        arg = static_cast<float>(weight_logit(rl.sel_l[q][lane], rl.sel_e[q][lane], wb) - l0);
     else if (lane == K)
         arg = static_cast<float>(-z);
     const float v = expf(arg);
@@ -137,7 +144,7 @@ __device__ __forceinline__ void wave_weights(const double *lg, int E, int K, int
     } else {
         float s = 0.0f;
         for (int e = lane; e < E; e += kWave)
-            s += expf(static_cast<float>(lg[e] - l0));
+            s += expf(static_cast<float>(weight_logit(lg[e], e, wb) - l0));
         denom = wave_sum(s);
     }
     const float r = (lane < K ? v : 1.0f) / (lane < K ? denom : 1.0f + v);
@@ -187,7 +194,8 @@ __device__ __forceinline__ uint32_t kth_of_32(const uint32_t *gm, int K, int lan
 // written and the candidates need exact fp64 ranking.
 template <typename ValueOf>
 __device__ __forceinline__ bool rank_packed(int C, int K, int renorm, int E, const double *lg, double z, bool gate,
-                                            int q, RouteLds &rl, int lane, ValueOf value, SlotTable *st)
+                                            int q, RouteLds &rl, int lane, ValueOf value, SlotTable *st,
+                                            const float *wb)
 {
     // padding 0 is below every candidate and shares no key with one; up to
     // 16 candidates (the usual case) are read in one unrolled batch
@@ -221,21 +229,22 @@ __device__ __forceinline__ bool rank_packed(int C, int K, int renorm, int E, con
         return false;
     const int e = static_cast<int>(~static_cast<uint32_t>(p));
     const double val = live ? value(p) : 0.0;
-    // l_0: the value of the candidate ranked first
+    const double wv = live ? weight_logit(val, e, wb) : 0.0;
+    // v_0: the weight logit of the candidate ranked first
     const int r0 = __builtin_ctzll(__ballot(live && rank == 0));
-    const long long vb = __double_as_longlong(val);
+    const long long vb = __double_as_longlong(wv);
     const int lo = __builtin_amdgcn_readlane(static_cast<int>(vb & 0xffffffff), r0);
     const int hi = __builtin_amdgcn_readlane(static_cast<int>(vb >> 32), r0);
     const double l0 = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
     const bool sel = live && rank < K;
-    const float ex = sel ? expf(static_cast<float>(val - l0)) : 0.0f;
+    const float ex = sel ? expf(static_cast<float>(wv - l0)) : 0.0f;
     float denom;
     if (renorm) {
         denom = wave_sum(ex);
     } else {
         float sum = 0.0f;
         for (int e2 = lane; e2 < E; e2 += kWave)
-            sum += expf(static_cast<float>(lg[e2] - l0));
+            sum += expf(static_cast<float>(weight_logit(lg[e2], e2, wb) - l0));
         denom = wave_sum(sum);
     }
     if (sel) {
@@ -273,7 +282,7 @@ __device__ __forceinline__ bool rank_packed(int C, int K, int renorm, int E, con
 //     path.
 template <int PL>
 __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, int renorm, double z, int q,
-                                              RouteLds &rl, int lane)
+                                              RouteLds &rl, int lane, const float *wb)
 {
     uint32_t key[PL];
     uint32_t mk = 0;   // 0 is below every key of a non-NaN value
@@ -321,7 +330,7 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
     if (C <= kWave) {
         // 3. rank by packed key
         if (rank_packed(C, K, renorm, E, lg, z, true, q, rl, lane,
-                        [&](uint64_t p) { return lg[~static_cast<uint32_t>(p)]; }, nullptr))
+                        [&](uint64_t p) { return lg[~static_cast<uint32_t>(p)]; }, nullptr, wb))
             return;
         // a key shared near the boundary: exact fp64 ranking
         if (lane < C)
@@ -347,17 +356,18 @@ __device__ __forceinline__ void wave_route_pl(const double *lg, int E, int K, in
         }
         __builtin_amdgcn_wave_barrier();
     }
-    wave_weights(lg, E, K, renorm, z, q, rl, lane);
+    wave_weights(lg, E, K, renorm, z, q, rl, lane, true, wb);
 }
 
-// Routing of row q by one wave (see wave_route_pl).
+// Routing of row q by one wave (see wave_route_pl); wb: the router bias when
+// it enters the selection only (the weights then use the unbiased logits).
 __device__ __forceinline__ void wave_route(const double *lg, int E, int K, int renorm, double z, int q, RouteLds &rl,
-                                           int lane)
+                                           int lane, const float *wb)
 {
     if (E <= 8 * kWave)
-        wave_route_pl<8>(lg, E, K, renorm, z, q, rl, lane);
+        wave_route_pl<8>(lg, E, K, renorm, z, q, rl, lane, wb);
     else
-        wave_route_pl<kMaxE / kWave>(lg, E, K, renorm, z, q, rl, lane);
+        wave_route_pl<kMaxE / kWave>(lg, E, K, renorm, z, q, rl, lane, wb);
 }
 
 }  // namespace moe

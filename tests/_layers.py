@@ -103,7 +103,7 @@ def oracle_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_
                         exp_down=[a["exp_down"][e] for e in range(E)],
                         sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"],
                         renormalize=renormalize, bias_mode=a.get("bias_mode", 0), norm_w=a.get("norm_w"),
-                        norm_eps=a.get("norm_eps", 1e-6), residual=a.get("residual", 0))
+                        norm_eps=float(np.float32(a.get("norm_eps", 1e-6))), residual=a.get("residual", 0))
 
 
 def oracle_layer_from_config(cfg: mi.LayerConfig, dense=None, experts=None, stacks=None):
@@ -164,7 +164,9 @@ def gpu_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_t="
     import sparse_moe_decode_amd as moe
     kw = dict(H=a["H"], E=a["E"], K=a["K"], I=a["I"], Is=a["Is"], router_t=router_t, expert_t=expert_t,
               shared_t=shared_t, router_w=a["router_w"], gate_vec=a["gate_vec"], router_bias=a.get("router_bias"),
-              sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"], renormalize=renormalize)
+              sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"], renormalize=renormalize,
+              bias_mode=a.get("bias_mode", 0), norm_w=a.get("norm_w"), norm_eps=float(np.float32(a.get("norm_eps", 1e-6))),
+              residual=a.get("residual", 0))
     if expert_t == "q2":
         src = {0: a["exp_gate"], 1: a["exp_up"], 2: a["exp_down"]}
         return moe.Layer(**kw, expert_source=lambda e, m: np.asarray(src[m][e], np.float32))

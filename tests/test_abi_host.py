@@ -30,7 +30,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_strerror():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert moe.strerror(code) and moe.strerror(code) != "unknown status"
     assert moe.strerror(-99) == "unknown status"
@@ -62,6 +62,10 @@ def _fwd(desc, x=0x20000, T=1, y=0x30000, ws=0x40000, ws_bytes=1 << 30, ids_in=N
     (dict(router_t=moe.MOE_Q2B32), moe.MOE_EINVAL),
     (dict(shared_t=7), moe.MOE_EINVAL),
     (dict(reserved=1), moe.MOE_EINVAL),
+    (dict(bias_mode=2), moe.MOE_EINVAL),
+    (dict(residual=2), moe.MOE_EINVAL),
+    (dict(norm_w=0x10000, norm_eps=-1.0), moe.MOE_EINVAL),
+    (dict(norm_w=0x10004), moe.MOE_EALIGN),
     (dict(router_w=None), moe.MOE_EINVAL),
     (dict(exp_down=None), moe.MOE_EINVAL),
     (dict(exp_up=0x10008), moe.MOE_EALIGN),

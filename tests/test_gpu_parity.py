@@ -260,12 +260,16 @@ def test_maximum_sizes():
         _say(f"rows={rows}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
 
 
-def test_cache_aware_routing_bias():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_cache_aware_routing_bias(mode):
     """The opt-in cache-aware routing variant: logits z + lambda * Delta *
     cached_e (Research notes page, section 4, the cache-aware routing row),
-    given to the layer as its per-expert router bias. Parity with the oracle,
-    and the bias moves selections toward the cached experts."""
-    _say("case: cache-aware routing bias")
+    given as the per-expert router bias with MOE_BIAS_SELECT_ONLY (the bias
+    picks the experts, the weights come from the unbiased logits), and the
+    same bias in the selection and the weights (mode 0). Parity with the
+    oracle's variant on decode, few-row and prefill calls; the bias moves
+    selections toward the cached experts; both modes select the same experts."""
+    _say(f"case: cache-aware routing bias, bias_mode {mode}")
     rng = np.random.default_rng(2412)
     a = _random_arrays(rng, 256, 64, 6, 64, 64, rstd=0.1)
     cached = (rng.random(64) < 0.25).astype(np.float32)
@@ -273,16 +277,71 @@ def test_cache_aware_routing_bias():
     base = _oracle_ref(oracle_layer_from_arrays(a), x)
     hits0 = cached[base[0]].sum()
     for lam_delta in (0.25, 1.0):
-        b = dict(a, router_bias=(lam_delta * cached).astype(np.float32))
+        b = dict(a, router_bias=(lam_delta * cached).astype(np.float32), bias_mode=mode)
         L = oracle_layer_from_arrays(b)
         G = gpu_layer_from_arrays(b)
         ref = _oracle_ref(L, x)
+        other = _oracle_ref(oracle_layer_from_arrays(dict(b, bias_mode=1 - mode)), x)
+        np.testing.assert_array_equal(ref[0], other[0])
         for rows in (1, 3, 24):
-            assert_parity(run_calls(G, x, rows), ref, f"cache bias {lam_delta} rows={rows}")
+            assert_parity(run_calls(G, x, rows), ref, f"cache bias {lam_delta} mode {mode} rows={rows}")
+        assert_parity(run_calls(G, x, 24, force_path="prefill"), ref, f"cache bias {lam_delta} mode {mode} prefill")
         hits = cached[ref[0]].sum()
         assert hits >= hits0, (lam_delta, hits, hits0)
         hits0 = hits
     assert hits0 > cached[base[0]].sum()
+
+
+@pytest.mark.parametrize("name", ["hand_bias_select_only.json", "hand_norm_residual.json"])
+def test_hand_fixtures_bias_norm_residual(name):
+    """The hand-derived fixtures of the selection-only bias and of the norm
+    with the residual, on the decode and the prefill path."""
+    _say(f"case: hand fixture {name}")
+    a, exp = load_hand_fixture(name)
+    G = gpu_layer_from_arrays(a)
+    for path in (None, "prefill"):
+        ids, wts, gate, y = run_calls(G, a["x"], 1, force_path=path)
+        np.testing.assert_array_equal(ids[0], exp["ids"])
+        assert tolerance_ok(wts[0], exp["wts"]).all()
+        assert tolerance_ok(gate[0], exp["gate"]).all()
+        assert tolerance_ok(y[0], exp["y"]).all(), (path, y[0][:8], exp["y"][:8])
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2"])
+def test_norm_and_residual_layers(fmt):
+    """Layers with the pre-MoE RMS norm (random gamma) and the residual, with
+    a selection-only bias, on decode, few-row (3 and 12 rows) and prefill
+    calls, against the oracle."""
+    _say(f"case: norm + residual layer, {fmt} experts")
+    import oracle
+    rng = np.random.default_rng(4242)
+    H, E, K, I, Is = 256, 48, 6, 96, 64
+    a = _random_arrays(rng, H, E, K, I, Is, rstd=0.05, estd=0.05)
+    a.update(norm_w=rng.uniform(0.5, 1.5, H).astype(np.float32), norm_eps=1e-6, residual=1,
+             router_bias=(0.5 * (rng.random(E) < 0.3)).astype(np.float32), bias_mode=1)
+    x = (rng.standard_normal((37, H)) * 3.0).astype(np.float32)
+    rt = st = "f32" if fmt == "f32" else "bf16"
+    b = dict(a)
+    if fmt != "f32":
+        for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
+            b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+    if fmt == "q2":
+        src = {k: mi.bf16_bits_to_f32(b[k]).reshape(a[k].shape) for k in ("exp_gate", "exp_up", "exp_down")}
+        qo = dict(b)
+        for k in src:
+            qo[k] = [oracle.q2_quantize(m) for m in src[k]]
+        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t="q2", shared_t=st)
+        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t="q2", shared_t=st)
+    else:
+        L = oracle_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
+        G = gpu_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
+    ref = _oracle_ref(L, x)
+    for rows in (1, 3, 12):
+        assert_parity(run_calls(G, x, rows), ref, f"norm {fmt} rows={rows}")
+    assert_parity(run_calls(G, x, 37), ref, f"norm {fmt} prefill")
+    ids, wts, gate = G.route(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref[0])
 
 
 def test_given_routing_entry():
@@ -677,3 +736,68 @@ def test_determinism(decode_q2):
     b = run_calls(G, x, 1)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+# ------------------------------------------------ 48-layer decode stack
+
+def _rotated(mats, off, E):
+    """Expert e of a rotated stack is expert (e + off) % E of the base stack."""
+    return [mats[(e + off) % E] for e in range(E)]
+
+
+def test_stack_48_layers(decode_bf16):
+    """48 MoE layers in a row (the model's MoE layers, Architecture page,
+    "Qwen3-Next shape"): each with its own router, gate vector, shared
+    expert and pre-MoE norm gamma, the RMS norm and the residual, its routed
+    experts a rotation of one bf16 stack (layer l's expert e is base expert
+    (e + 97 l) mod 512, through a doubled stack on the GPU). Three tokens one
+    per call, three in one few-row call and sixteen in one prefill call run
+    through all 48 layers; at every layer the output is compared with the
+    oracle given the same layer input (ids identical, the rest within the
+    tolerance)."""
+    cfg, dense, stacks, G0 = decode_bf16
+    import sparse_moe_decode_amd as moe
+    E, L_layers = cfg.E, 48
+    _say(f"case: 48-layer stack, {cfg.name} shapes")
+    dbl = [torch.cat([t, t]) for t in (G0.exp_gate, G0.exp_up, G0.exp_down)]
+    strides = [t.shape[1] * t.shape[2] * 2 for t in (G0.exp_gate, G0.exp_up, G0.exp_down)]
+    offs = [(97 * l) % E for l in range(L_layers)]
+    layers, dense_l, gam = [], [], []
+    for l in range(L_layers):
+        d = dense if l == 0 else mi.dense_weights(mi.layer_instance(cfg, l))
+        g = mi.norm_weights(cfg, l)
+        Gl = moe.Layer(H=cfg.H, E=E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t, expert_t=cfg.expert_t,
+                       shared_t=cfg.shared_t, router_w=d["router_w"], gate_vec=d["gate_vec"], router_bias=None,
+                       sh_gate=d["sh_gate"], sh_up=d["sh_up"], sh_down=d["sh_down"], exp_gate=np.zeros((1, 8, 8), np.uint16),
+                       exp_up=np.zeros((1, 8, 8), np.uint16), exp_down=np.zeros((1, 8, 8), np.uint16), norm_w=g,
+                       norm_eps=1e-6, residual=1)
+        Gl.desc.exp_gate, Gl.desc.exp_up, Gl.desc.exp_down = (t.data_ptr() + offs[l] * st for t, st in zip(dbl, strides))
+        layers.append(Gl)
+        dense_l.append(d)
+        gam.append(g)
+    import oracle
+
+    def oracle_layer(l, need):
+        d = dense_l[l]
+        mats = [_rotated(m, offs[l], E) for m in stacks]
+        keep = set(int(e) for e in need)
+        pick = [[m[e] if e in keep else None for e in range(E)] for m in mats]
+        return oracle.Layer(H=cfg.H, E=E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t, expert_t=cfg.expert_t,
+                            shared_t=cfg.shared_t, router_w=d["router_w"], gate_vec=d["gate_vec"], router_bias=None,
+                            exp_gate=pick[0], exp_up=pick[1], exp_down=pick[2], sh_gate=d["sh_gate"],
+                            sh_up=d["sh_up"], sh_down=d["sh_down"], norm_w=gam[l], norm_eps=float(np.float32(1e-6)),
+                            residual=1)
+
+    x0 = mi.activations(cfg, T=22, instance=48)
+    for what, rows, T in (("decode", 1, 3), ("few-row", 3, 3), ("prefill", 16, 16)):
+        x = x0[:T].copy()
+        worst = 0.0
+        for l in range(L_layers):
+            got = run_calls(layers[l], x, rows)
+            Lo = oracle_layer(l, np.unique(got[0]))
+            ref = _oracle_ref(Lo, x)
+            err = assert_parity(got, ref, f"stack {what} layer {l}")
+            worst = max(worst, err[1])
+            x = got[3]
+        assert np.isfinite(x).all()
+        _say(f"stack {what}: 48 layers, worst error / tolerance {worst:.3g}")
