@@ -303,6 +303,78 @@ def run_extra(args, keys):
     return extra
 
 
+class StackWorkload:
+    """A 48-layer stack of 2-bit MoE layers as in the model (one per decoder
+    layer): every layer with its own router, gate vector, shared expert,
+    pre-MoE norm gamma and routed-expert copy, the RMS norm and the residual
+    fused into the layer. Each token passes through all 48 layers, one call
+    per layer (its input is the previous layer's output); the calls of all
+    tokens are captured in one graph."""
+
+    def __init__(self, cfg, tokens: int, n_layers: int = 48):
+        import torch
+        import sparse_moe_decode_amd as moe
+        self.cfg, self.T, self.NL = cfg, tokens, n_layers
+        d0 = mi.dense_weights(cfg)
+        base = moe.Layer(H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t, expert_t=cfg.expert_t,
+                         shared_t=cfg.shared_t, router_w=d0["router_w"], gate_vec=d0["gate_vec"],
+                         router_bias=d0["router_bias"], sh_gate=d0["sh_gate"], sh_up=d0["sh_up"],
+                         sh_down=d0["sh_down"], expert_source=lambda e, m: mi.expert_matrix_f32(cfg, e, m),
+                         norm_w=mi.norm_weights(cfg, 0), norm_eps=1e-6, residual=1)
+        self.layers = [base]
+        for l in range(1, n_layers):
+            d = mi.dense_weights(mi.layer_instance(cfg, l))
+            self.layers.append(base.with_dense(**d, norm_w=mi.norm_weights(cfg, l)).with_expert_copies())
+        x = mi.activations(cfg, T=tokens, instance=777)
+        self.buf = [torch.from_numpy(x).cuda()] + [torch.empty((tokens, cfg.H), device="cuda")
+                                                   for _ in range(n_layers)]
+        self.ws = base.workspace(1)
+        self.graph = None
+
+    def run_calls(self):
+        import sparse_moe_decode_amd as moe
+        for t in range(self.T):
+            for l, L in enumerate(self.layers):
+                moe.forward(L.desc, self.buf[l][t:t + 1], self.buf[l + 1][t:t + 1], self.ws)
+
+    def capture(self):
+        import torch
+        self.run_calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_calls()
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def step(self):
+        self.graph.replay()
+
+
+def run_stack(args):
+    """Per-token decode through a 48-layer 2-bit stack (stack_q2_48)."""
+    import torch
+    cfg = mi.CONFIGS[2]
+    print("[bench] stack_q2_48", file=sys.stderr, flush=True)
+    tokens = 64
+    wl = StackWorkload(cfg, tokens)
+    wl.capture()
+    per = []
+    ms, _ = time_steps(wl, max(2, args.steps // 2), 1, per)
+    calls = tokens * wl.NL
+    per_call = ms / 1e3 / calls
+    # algorithmic bytes of one layer call: as a decode call, plus gamma and the residual's x read
+    b = call_bytes(cfg, 1, cfg.K) + cfg.H * 4 * 2
+    rec = {"ms_per_step": round(ms, 4), "median_ms_per_step": round(float(np.median(per)), 4), "tokens": tokens,
+           "layers": wl.NL, "distinct_expert_stacks": wl.NL, "tokens_per_s": round(tokens / (ms / 1e3), 1),
+           "ms_per_token": round(ms / tokens, 4), "us_per_layer_call": round(per_call * 1e6, 3),
+           "bytes_per_layer_call": round(b), "GBps": round(b / per_call / 1e9, 1),
+           "hbm_frac": round(b / per_call / 1e9 / HBM_PEAK_GBS, 4), "traffic_bytes_per_call": traffic_for("stack_q2_48")}
+    del wl
+    torch.cuda.empty_cache()
+    return {"stack_q2_48": rec}
+
+
 def rows_sweep(args):
     """Throughput of calls of R rows on the 2-bit layer: one decode row, the
     few-row path up to 4 rows, the grouped prefill path above (the crossover
@@ -336,7 +408,7 @@ def main():
     ap.add_argument("--cpu-single-seconds", type=float, default=8.0, help="oracle on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
-    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2"],
+    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2", "stack_q2_48"],
                     help="run just this one of the other workloads (for profiling); prints its record")
     ap.add_argument("--rows-sweep", action="store_true",
                     help="rows per call from 1 to 2048 on the 2-bit layer (decode, few-row, prefill paths); "
@@ -359,7 +431,7 @@ def main():
         print(json.dumps(rows_sweep(args)), flush=True)
         return
     if args.only:
-        extra = run_extra(args, [args.only])
+        extra = run_stack(args) if args.only == "stack_q2_48" else run_extra(args, [args.only])
         print(json.dumps({"workload": args.only, **extra[args.only]}), flush=True)
         return
 
@@ -399,6 +471,7 @@ def main():
 
     if not args.no_extra:
         extra.update(run_extra(args, None))
+        extra.update(run_stack(args))
 
     line = {
         "metric": "MoE-layer decode tokens/s and % of HBM roofline (expert bytes read/s)",
