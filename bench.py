@@ -255,6 +255,7 @@ def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0, per_step=Non
 
 
 EXTRA_WORKLOADS = [("decode_q2", 2, 1, 1000), ("fewrow_q2_R2", 3, 2, 500), ("fewrow_q2_R3", 3, 3, 333),
+                   ("fewrow_q2_R8", 3, 8, 125),
                    ("prefill_q2", 4, 2048, 1)]
 
 
@@ -384,7 +385,7 @@ def rows_sweep(args):
     print("[bench] rows sweep", file=sys.stderr, flush=True)
     wl = Workload(cfg, 1, total, 1)
     out = {}
-    for R in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64, 256, 2048):
+    for R in (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 13, 16, 24, 32, 64, 256, 2048):
         wl.R = R
         wl.ncalls = max(1, min(total // R, 256))
         wl.ws = wl.layers[0].workspace(R)
@@ -408,7 +409,8 @@ def main():
     ap.add_argument("--cpu-single-seconds", type=float, default=8.0, help="oracle on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
-    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "prefill_q2", "stack_q2_48"],
+    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "fewrow_q2_R8", "prefill_q2",
+                                       "stack_q2_48"],
                     help="run just this one of the other workloads (for profiling); prints its record")
     ap.add_argument("--rows-sweep", action="store_true",
                     help="rows per call from 1 to 2048 on the 2-bit layer (decode, few-row, prefill paths); "

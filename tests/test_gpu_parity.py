@@ -64,7 +64,7 @@ def test_hand_fixture():
     assert tolerance_ok(y[0], exp["y"]).all(), (y[0][:4], exp["y"][:4])
 
 
-@pytest.mark.parametrize("rows", [1, 2, 3, 4])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_tiny_fp32_workload(rows):
     _say(f"case: tiny fp32 workload, {rows} rows per call")
     cfg = mi.CONFIGS[0]
@@ -149,7 +149,7 @@ def test_edge_shapes(case):
     L = oracle_layer_from_arrays(a, renormalize=renorm)
     G = gpu_layer_from_arrays(a, renormalize=renorm)
     ref = _oracle_ref(L, x)
-    for rows in (1, 3, 4, T):   # decode, few-row, few-row, T rows in one call
+    for rows in (1, 3, 4, 6, 8, T):   # decode, few-row launches of 3 and 4 rows, calls of 6, 8 and 9 rows
         assert_parity(run_calls(G, x, rows), ref, f"{case} rows={rows}")
     assert_parity(run_calls(G, x, T, force_path="prefill"), ref, f"{case} prefill")
 
@@ -186,10 +186,10 @@ def test_bf16_and_q2_small_shapes():
 
 def test_path_boundaries():
     """Calls at the edges of the library's path choice on a 2-bit layer:
-    5 and 12 rows run as few-row launches of three (remainders of two and
-    none), 13 rows as one prefill chunk; 13 rows forced through few-row
-    launches (a remainder of one joining the last launch as four) must agree
-    as well."""
+    5, 8 and 12 rows run as few-row launches of three (remainders of two,
+    two and none), 13 rows as one prefill chunk; 13 rows forced through
+    few-row launches (a remainder of one joining the last launch as four)
+    must agree as well."""
     _say("case: path boundaries (5, 12, 13 rows)")
     import oracle
     rng = np.random.default_rng(43)
@@ -205,7 +205,7 @@ def test_path_boundaries():
                               router_t="bf16", expert_t="q2", shared_t="bf16")
     x = rng.standard_normal((60, 256)).astype(np.float32)
     ref = _oracle_ref(L, x)
-    for rows in (5, 12, 13):
+    for rows in (5, 8, 12, 13):
         assert_parity(run_calls(G, x, rows), ref, f"boundary rows={rows}")
     assert_parity(run_calls(G, x, 13, force_path="fewrow"), ref, "boundary rows=13 few-row")
 
@@ -213,15 +213,16 @@ def test_path_boundaries():
 @pytest.mark.parametrize("fmt", ["bf16", "q2"])
 def test_wide_rows_and_large_pair_sets(fmt):
     """Rows wider than one chunk set per wave (H = 2112: the streamed gate/up
-    path) and, at four rows with K = 16, more (slot, row) pairs than the
-    down pass stages in LDS (h' read from L2)."""
+    path) and, at four rows with K = 16, more (slot, row) pairs than the down
+    pass stages in LDS (h' read from L2); eight rows as launches of three,
+    three and two."""
     _say(f"case: wide rows {fmt} H=2112 E=16 K=16 I=544 Is=96")
     rng = np.random.default_rng(77)
     a = _random_arrays(rng, 2112, 16, 16, 544, 96, rstd=0.05, estd=0.03)
     b = dict(a)
     for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
         b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
-    x = rng.standard_normal((4, 2112)).astype(np.float32)
+    x = rng.standard_normal((8, 2112)).astype(np.float32)
     if fmt == "bf16":
         L = oracle_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
         G = gpu_layer_from_arrays(b, router_t="bf16", expert_t="bf16", shared_t="bf16")
@@ -235,7 +236,7 @@ def test_wide_rows_and_large_pair_sets(fmt):
         G = gpu_layer_from_arrays(dict(b, **{k: np.stack(v) for k, v in ef.items()}),
                                   router_t="bf16", expert_t="q2", shared_t="bf16")
     ref = _oracle_ref(L, x)
-    for rows in (1, 4):
+    for rows in (1, 4, 8):
         assert_parity(run_calls(G, x, rows), ref, f"wide {fmt} rows={rows}")
 
 
@@ -691,13 +692,13 @@ def test_decode_q2_full(decode_q2):
     _say(f"{cfg.name}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
 
 
-@pytest.mark.parametrize("R", [2, 3])
+@pytest.mark.parametrize("R", [2, 3, 5, 8])
 def test_fewrow_q2_full(R):
     cfg = mi.CONFIGS[3].with_(rows_per_call=R)
     _say(f"case: {cfg.name} R={R}")
     dense = mi.dense_weights(cfg)
     G = gpu_layer_from_config(cfg, dense)
-    calls = 500 if R == 2 else 333
+    calls = {2: 500, 3: 333, 5: 100, 8: 125}[R]
     x = mi.activations(cfg, T=calls * R, instance=R)
     got = run_calls(G, x, R)
     Lr = oracle_layer_from_config(cfg, dense=dense, experts=[])
