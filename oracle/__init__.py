@@ -27,8 +27,9 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-OR_F32, OR_BF16, OR_Q2 = 0, 1, 2
-WTYPE = {"f32": OR_F32, "bf16": OR_BF16, "q2": OR_Q2}
+OR_F32, OR_BF16, OR_Q2, OR_Q3, OR_Q4 = 0, 1, 2, 3, 4
+WTYPE = {"f32": OR_F32, "bf16": OR_BF16, "q2": OR_Q2, "q3": OR_Q3, "q4": OR_Q4}
+BITS = {"q2": 2, "q3": 3, "q4": 4}
 
 
 def build(force: bool = True) -> str:
@@ -73,6 +74,12 @@ def lib():
             L.oracle_q2_quantize.restype = C.c_int
             L.oracle_q2_dequantize.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p]
             L.oracle_q2_dequantize.restype = None
+            L.oracle_qb_quantize.argtypes = [C.c_int, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]
+            L.oracle_qb_quantize.restype = C.c_int
+            L.oracle_qb_dequantize.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                                               C.c_void_p]
+            L.oracle_qb_dequantize.restype = None
             L.oracle_route.argtypes = [C.POINTER(Desc), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p]
             L.oracle_route.restype = C.c_int
@@ -101,35 +108,45 @@ def float_to_half(f: float) -> int:
     return int(lib().oracle_float_to_half(float(np.float32(f))))
 
 
-# --------------------------------------------------------- 2-bit blocks
+# -------------------------------------------------------- b-bit blocks
 
 class Q2:
-    """Logical 2-bit block form of one matrix (codes, fp16 scale and min bits)."""
+    """Logical b-bit block form of one matrix (codes [rows][cols*b/8], fp16
+    scale and min bits [rows][cols/32]); b = 2 unless given."""
 
-    def __init__(self, codes, scale, minv, rows, cols):
+    def __init__(self, codes, scale, minv, rows, cols, bits=2):
         self.codes, self.scale, self.minv = codes, scale, minv
-        self.rows, self.cols = rows, cols
+        self.rows, self.cols, self.bits = rows, cols, bits
         self.struct = Q2Matrix(codes.ctypes.data, scale.ctypes.data, minv.ctypes.data)
 
 
-def q2_quantize(w: np.ndarray) -> Q2:
+def qb_quantize(w: np.ndarray, bits: int) -> Q2:
+    """The b-bit quantizer (oracle.c, oracle_qb_quantize)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
-    codes = np.zeros((rows, cols // 4), np.uint8)
+    codes = np.zeros((rows, cols * bits // 8), np.uint8)
     scale = np.zeros((rows, cols // 32), np.uint16)
     minv = np.zeros((rows, cols // 32), np.uint16)
-    rc = lib().oracle_q2_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, scale.ctypes.data,
+    rc = lib().oracle_qb_quantize(bits, w.ctypes.data, rows, cols, codes.ctypes.data, scale.ctypes.data,
                                   minv.ctypes.data)
     if rc != 0:
         raise ValueError("oracle quantizer rejected the input (non-finite or out of fp16 range)")
-    return Q2(codes, scale, minv, rows, cols)
+    return Q2(codes, scale, minv, rows, cols, bits)
+
+
+def qb_dequantize(q: Q2) -> np.ndarray:
+    out = np.zeros((q.rows, q.cols), np.float32)
+    lib().oracle_qb_dequantize(q.bits, q.codes.ctypes.data, q.scale.ctypes.data, q.minv.ctypes.data,
+                               q.rows, q.cols, out.ctypes.data)
+    return out
+
+
+def q2_quantize(w: np.ndarray) -> Q2:
+    return qb_quantize(w, 2)
 
 
 def q2_dequantize(q: Q2) -> np.ndarray:
-    out = np.zeros((q.rows, q.cols), np.float32)
-    lib().oracle_q2_dequantize(q.codes.ctypes.data, q.scale.ctypes.data, q.minv.ctypes.data,
-                               q.rows, q.cols, out.ctypes.data)
-    return out
+    return qb_dequantize(q)
 
 
 # ----------------------------------------------------------------- norm

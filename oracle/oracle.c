@@ -39,12 +39,17 @@
  * rounding; the 2-bit block format is decoded to fp32 first (its own
  * definition) and then widened.
  *
- * 2-bit block format (logical form used only inside this oracle):
+ * b-bit block formats, b = 2, 3, 4 (logical form used only inside this
+ * oracle; the 3- and 4-bit variants are the higher-precision expert files of
+ * the same model, "DwarfStar Red Lite" guide, IQ3_XXS, with the weight type a
+ * function constant of the kernels, "Research notes, October 2026", section
+ * 1, "Metal"):
  *   32 consecutive weights of a row (along the reduction dimension) form a
- *   block with 8 bytes of codes (weight j at bits 2*(j%4).. of byte j/4,
- *   least significant first), an fp16 scale and an fp16 minimum;
- *   w = fp32(code * scale + min). The quantizer below is written from that
- *   definition with IEEE binary32 arithmetic, round-to-nearest-even.
+ *   block with 4b bytes of codes (weight j at bits b*j .. b*j+b-1 of the
+ *   block's bytes read as one little-endian integer), an fp16 scale and an
+ *   fp16 minimum; w = fp32(code * scale + min), code in 0 .. 2^b - 1. The
+ *   quantizer below is written from that definition with IEEE binary32
+ *   arithmetic, round-to-nearest-even.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math).
  */
@@ -54,13 +59,13 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_Q2 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_Q2 = 2, OR_Q3 = 3, OR_Q4 = 4 };
 
 typedef struct {
-    const uint8_t *codes;   /* [rows][cols/4] */
+    const uint8_t *codes;   /* [rows][cols*b/8] */
     const uint16_t *scale;  /* [rows][cols/32] fp16 bit patterns */
     const uint16_t *minv;   /* [rows][cols/32] fp16 bit patterns */
-} oracle_q2_matrix;
+} oracle_q2_matrix;         /* a b-bit matrix; b from the layer's expert type */
 
 typedef struct {
     int32_t hidden, n_experts, top_k, inter, shared_inter, renormalize;
@@ -68,7 +73,7 @@ typedef struct {
     const void *router_w;        /* [E][H], router_t */
     const float *router_bias;    /* [E] or NULL */
     const void *gate_vec;        /* [H], router_t */
-    const void *const *exp_gate; /* E entries: [I][H] (f32/bf16) or oracle_q2_matrix* */
+    const void *const *exp_gate; /* E entries: [I][H] (f32/bf16) or oracle_q2_matrix* (b-bit) */
     const void *const *exp_up;   /* E entries: [I][H] */
     const void *const *exp_down; /* E entries: [H][I] */
     const void *sh_gate;         /* [Is][H], shared_t */
@@ -126,17 +131,38 @@ uint16_t oracle_float_to_half(float f)
     return sign | (uint16_t)(((E + 15) << 10) | (int)m);
 }
 
-/* ------------------------------------------------------- 2-bit blocks */
+/* ------------------------------------------------------ b-bit blocks */
+
+/* Code j of a block (4b bytes, weight j at bits b*j..b*j+b-1). */
+static int block_code(const uint8_t *cb, int bits, int j)
+{
+    int c = 0;
+    for (int i = 0; i < bits; ++i) {
+        const int bit = bits * j + i;
+        c |= ((cb[bit / 8] >> (bit % 8)) & 1) << i;
+    }
+    return c;
+}
+
+static void set_block_code(uint8_t *cb, int bits, int j, int c)
+{
+    for (int i = 0; i < bits; ++i) {
+        const int bit = bits * j + i;
+        cb[bit / 8] |= (uint8_t)(((c >> i) & 1) << (bit % 8));
+    }
+}
 
 /* Quantize one row-major fp32 matrix [rows][cols] (cols % 32 == 0) into the
- * logical block form. Returns 0, or -1 if a value is not finite or a block's
- * min or scale does not fit fp16. */
-int oracle_q2_quantize(const float *src, int64_t rows, int64_t cols,
+ * logical b-bit block form (bits 2, 3 or 4). Returns 0, or -1 if a value is
+ * not finite or a block's min or scale does not fit fp16. */
+int oracle_qb_quantize(int bits, const float *src, int64_t rows, int64_t cols,
                        uint8_t *codes, uint16_t *scale, uint16_t *minv)
 {
-    if (cols % 32 != 0)
+    if (cols % 32 != 0 || bits < 2 || bits > 4)
         return -1;
-    int64_t nb = cols / 32;
+    const int top = (1 << bits) - 1;
+    const float levels = (float)top;
+    const int64_t nb = cols / 32, cbytes = 4 * bits;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
             const float *w = src + r * cols + b * 32;
@@ -150,22 +176,22 @@ int oracle_q2_quantize(const float *src, int64_t rows, int64_t cols,
             uint16_t mh = oracle_float_to_half(lo);
             float mf = oracle_half_to_float(mh);
             float range = hi - mf;                   /* binary32 subtract */
-            float step = range / 3.0f;               /* binary32 divide */
+            float step = range / levels;             /* binary32 divide */
             uint16_t sh = oracle_float_to_half(step);
             float sf = oracle_half_to_float(sh);
             if (!isfinite(mf) || !isfinite(sf))
                 return -1;
-            uint8_t *cb = codes + r * (cols / 4) + b * 8;
-            memset(cb, 0, 8);
+            uint8_t *cb = codes + r * (cols / 32) * cbytes + b * cbytes;
+            memset(cb, 0, (size_t)cbytes);
             for (int j = 0; j < 32; ++j) {
                 int c = 0;
                 if (sf != 0.0f) {
                     float diff = w[j] - mf;
                     float q = diff / sf;
                     float n = nearbyintf(q);
-                    c = n < 0.0f ? 0 : (n > 3.0f ? 3 : (int)n);
+                    c = n < 0.0f ? 0 : (n > levels ? top : (int)n);
                 }
-                cb[j / 4] |= (uint8_t)(c << (2 * (j % 4)));
+                set_block_code(cb, bits, j, c);
             }
             scale[r * nb + b] = sh;
             minv[r * nb + b] = mh;
@@ -175,22 +201,35 @@ int oracle_q2_quantize(const float *src, int64_t rows, int64_t cols,
 }
 
 /* Decode the logical block form back to fp32: w = code * scale + min. */
-void oracle_q2_dequantize(const uint8_t *codes, const uint16_t *scale, const uint16_t *minv,
+void oracle_qb_dequantize(int bits, const uint8_t *codes, const uint16_t *scale, const uint16_t *minv,
                           int64_t rows, int64_t cols, float *dst)
 {
-    int64_t nb = cols / 32;
+    const int64_t nb = cols / 32, cbytes = 4 * bits;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
             float sf = oracle_half_to_float(scale[r * nb + b]);
             float mf = oracle_half_to_float(minv[r * nb + b]);
-            const uint8_t *cb = codes + r * (cols / 4) + b * 8;
+            const uint8_t *cb = codes + r * nb * cbytes + b * cbytes;
             for (int j = 0; j < 32; ++j) {
-                int c = (cb[j / 4] >> (2 * (j % 4))) & 3;
-                float prod = (float)c * sf;          /* exact: <= 13 significant bits */
+                int c = block_code(cb, bits, j);
+                float prod = (float)c * sf;          /* exact: <= 15 significant bits */
                 dst[r * cols + b * 32 + j] = prod + mf;  /* one rounding */
             }
         }
     }
+}
+
+/* The 2-bit instances. */
+int oracle_q2_quantize(const float *src, int64_t rows, int64_t cols,
+                       uint8_t *codes, uint16_t *scale, uint16_t *minv)
+{
+    return oracle_qb_quantize(2, src, rows, cols, codes, scale, minv);
+}
+
+void oracle_q2_dequantize(const uint8_t *codes, const uint16_t *scale, const uint16_t *minv,
+                          int64_t rows, int64_t cols, float *dst)
+{
+    oracle_qb_dequantize(2, codes, scale, minv, rows, cols, dst);
 }
 
 /* ------------------------------------------------------------ widening */
@@ -215,10 +254,11 @@ static void row_to_double(const void *m, int32_t t, int64_t r, int64_t cols, dou
         for (int64_t c = 0; c < cols; ++c)
             out[c] = bf16_to_double(p[c]);
     } else {
+        const int bits = t == OR_Q2 ? 2 : (t == OR_Q3 ? 3 : 4);
         const oracle_q2_matrix *q = (const oracle_q2_matrix *)m;
         float tmp[32];
         for (int64_t b = 0; b < cols / 32; ++b) {
-            oracle_q2_dequantize(q->codes + r * (cols / 4) + b * 8,
+            oracle_qb_dequantize(bits, q->codes + r * (cols / 32) * 4 * bits + b * 4 * bits,
                                  q->scale + r * (cols / 32) + b,
                                  q->minv + r * (cols / 32) + b, 1, 32, tmp);
             for (int j = 0; j < 32; ++j)
@@ -346,9 +386,9 @@ static int check_desc(const oracle_desc *d)
         return -1;
     if (d->shared_t != OR_F32 && d->shared_t != OR_BF16)
         return -1;
-    if (d->expert_t < OR_F32 || d->expert_t > OR_Q2)
+    if (d->expert_t < OR_F32 || d->expert_t > OR_Q4)
         return -1;
-    if (d->expert_t == OR_Q2 && (d->hidden % 32 || d->inter % 32))
+    if (d->expert_t >= OR_Q2 && (d->hidden % 32 || d->inter % 32))
         return -1;
     if (d->bias_mode != 0 && d->bias_mode != 1)
         return -1;

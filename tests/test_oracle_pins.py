@@ -5,7 +5,9 @@ brute-force property, an invariant of the definition or an IEEE/NumPy library
 routine, chosen so that a plausible slip (dropped term, wrong sign, transposed
 operand, wrong tie rule, missing renormalization) fails at least one test.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -533,3 +535,83 @@ def test_norm_of_unit_rows_and_residual():
              norm_w=rng.uniform(0.5, 2.0, H).astype(np.float32), residual=1)
     xr = rng.standard_normal((6, H)).astype(np.float32)
     np.testing.assert_array_equal(oracle_layer_from_arrays(z).forward(xr)[3], xr)
+
+
+# ------------------------------------------------------ b-bit quantizer
+
+def _quant_cases():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_quant_blocks.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _quant_cases(), ids=lambda c: c["name"])
+def test_hand_fixture_quant_blocks(case):
+    """hand_quant_blocks.json: ties to even, a block whose fp16 min lies above
+    its maximum (negative step), and the 3- and 4-bit bit layouts."""
+    w = np.array(case["w"], np.float32).reshape(1, 32)
+    q = oracle.qb_quantize(w, case["bits"])
+    assert list(q.codes[0]) == case["codes"]
+    assert int(q.scale[0, 0]) == case["scale"] and int(q.minv[0, 0]) == case["min"]
+    np.testing.assert_array_equal(oracle.qb_dequantize(q)[0], np.array(case["decoded"], np.float32))
+
+
+def _unpack_codes(q):
+    """Codes of a b-bit matrix read bit by bit (weight j of a block at bits b*j..)."""
+    bits = q.bits
+    nb = q.cols // 32
+    raw = q.codes.reshape(q.rows, nb, 4 * bits)
+    allbits = np.unpackbits(raw, axis=-1, bitorder="little").reshape(q.rows, nb, 32, bits)
+    return (allbits * (1 << np.arange(bits))).sum(axis=-1).reshape(q.rows, q.cols)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_qb_exact_round_trip_dyadic_blocks(bits):
+    rng = np.random.default_rng(40 + bits)
+    rows, cols, top = 16, 256, (1 << bits) - 1
+    codes = rng.integers(0, top + 1, (rows, cols))
+    codes[:, ::32] = 0
+    codes[:, 1::32] = top                               # every block spans the full code range
+    s = 2.0 ** rng.integers(-12, -3, (rows, cols // 32))
+    m = rng.integers(-64, 64, (rows, cols // 32)) * 2.0 ** -10
+    w = (codes * np.repeat(s, 32, axis=1) + np.repeat(m, 32, axis=1)).astype(np.float32)
+    q = oracle.qb_quantize(w, bits)
+    assert q.codes.shape == (rows, cols * bits // 8)
+    np.testing.assert_array_equal(oracle.qb_dequantize(q), w)
+    np.testing.assert_array_equal(_unpack_codes(q), codes)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_qb_error_bound_random_blocks(bits):
+    """Each decoded weight lies within half a step of its input, plus the
+    min's fp16 rounding and the step's; more bits give a smaller error."""
+    rng = np.random.default_rng(50 + bits)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    q = oracle.qb_quantize(w, bits)
+    wq = oracle.qb_dequantize(q).astype(np.float64)
+    top = (1 << bits) - 1
+    sf = np.repeat(q.scale.view(np.float16).astype(np.float64), 32, axis=1)
+    mf = np.repeat(q.minv.view(np.float16).astype(np.float64), 32, axis=1)
+    lo = np.repeat(w.reshape(64, 16, 32).min(axis=2).astype(np.float64), 32, axis=1)
+    bound = 0.5 * np.abs(sf) + np.abs(lo - mf) + top * 0.001 * np.abs(sf) + 1e-9
+    assert np.all(np.abs(w - wq) <= bound)
+    c = _unpack_codes(q)
+    assert c.min() == 0 and c.max() == top
+    e_lo = np.abs(w - oracle.qb_dequantize(oracle.qb_quantize(w, bits - 1))).mean()
+    assert np.abs(w - wq).mean() < 0.75 * e_lo
+
+
+@pytest.mark.parametrize("wt", ["q3", "q4"])
+def test_qb_layer_equals_dequantized_fp32_layer(wt):
+    """A b-bit layer is the fp32 layer holding the dequantized weights."""
+    bits = oracle.BITS[wt]
+    rng = np.random.default_rng(60 + bits)
+    a = _random_arrays(rng, 64, 6, 2, 32, 32)
+    qa, fa = dict(a), dict(a)
+    for k in ("exp_gate", "exp_up", "exp_down"):
+        qa[k] = [oracle.qb_quantize(m, bits) for m in a[k]]
+        fa[k] = np.stack([oracle.qb_dequantize(q) for q in qa[k]])
+    x = rng.standard_normal((3, 64)).astype(np.float32)
+    rq = oracle_layer_from_arrays(qa, expert_t=wt).forward(x)
+    rf = oracle_layer_from_arrays(fa).forward(x)
+    for u, v in zip(rq, rf):
+        np.testing.assert_array_equal(u, v)
