@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2u
+#define MOE_ABI_VERSION 3u
 
 typedef enum {
     MOE_OK = 0,
@@ -63,7 +63,9 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,            /* IEEE binary32 */
     MOE_BF16 = 1,           /* bfloat16 bit patterns (uint16) */
-    MOE_Q2B32 = 2           /* 2-bit block format, see moe_q2_pack (routed experts only) */
+    MOE_Q2B32 = 2,          /* 2-bit block format, see moe_qb_pack (routed experts only) */
+    MOE_Q3B32 = 3,          /* 3-bit block format, see moe_qb_pack (routed experts only) */
+    MOE_Q4B32 = 4           /* 4-bit block format, see moe_qb_pack (routed experts only) */
 } moe_wtype;
 
 /*
@@ -82,9 +84,10 @@ typedef enum {
  *   sh_gate        [Is][H]  shared_t (MOE_F32 or MOE_BF16)
  *   sh_up          [Is][H]  shared_t
  *   sh_down        [H][Is]  shared_t
- * For MOE_Q2B32 experts each stacked matrix is one moe_q2_pack() result and
- * occupies moe_q2_packed_bytes(rows, cols) bytes; expert e starts at
- * e * moe_q2_packed_bytes(rows, cols). The expert dimension is outermost and
+ * For the b-bit block formats (MOE_Q2B32, MOE_Q3B32, MOE_Q4B32: b = 2, 3, 4)
+ * each stacked matrix is one moe_qb_pack(b, ...) result and occupies
+ * moe_qb_packed_bytes(b, rows, cols) bytes; expert e starts at
+ * e * moe_qb_packed_bytes(b, rows, cols). The expert dimension is outermost and
  * every expert is one contiguous byte range (the merged routed tensors of the
  * "Red Lite v0.3 streaming development" page, section "Implemented in dev1").
  *
@@ -222,38 +225,50 @@ int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E,
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
- * 2-bit block format (MOE_Q2B32): 32-weight blocks as in the 32-weight
- * chunks of the quantized matvec kernels ("Research notes, October 2026",
- * section 4, narrow-row row), with the code width, fp16 scale and fp16
- * minimum fixed by the layer's 2-bit configuration. The logical content of a [rows][cols] fp32
- * matrix (cols % 32 == 0): each run of 32 consecutive weights of a row is a
- * block with 2-bit codes c (0..3), an fp16 scale s and an fp16 minimum m;
- * the weight is fp32(c * s + m).
+ * b-bit block formats (b = 2: MOE_Q2B32, 3: MOE_Q3B32, 4: MOE_Q4B32). The
+ * 32-weight block is that of the quantized matvec kernels' 32-weight chunks
+ * ("Research notes, October 2026", section 4, narrow-row row); the 2-bit
+ * width, fp16 scale and fp16 minimum are the layer's 2-bit configuration,
+ * and the 3- and 4-bit widths stand for the higher-precision expert files
+ * of the same model ("DwarfStar Red Lite" guide, the IQ3_XXS file; the
+ * weight type a constant of the kernels, "Research notes", section 1).
+ * Logical content of a [rows][cols] fp32 matrix (cols % 32 == 0): each run
+ * of 32 consecutive weights of a row is a block with b-bit codes c
+ * (0 .. 2^b - 1), an fp16 scale s and an fp16 minimum m; the weight is
+ * fp32(c * s + m).
  * Quantizer (IEEE binary32, round to nearest even, no fused operations):
  *   lo, hi = min, max of the block;  m = fp16(lo);
- *   s = fp16((hi - float(m)) / 3);
- *   c = 0 if float(s) == 0, else clamp(nearbyint((w - float(m)) / float(s)), 0, 3).
- * Physical layout written by moe_q2_pack (little-endian):
- *   bytes [0, rows*cols/4)                 codes; weight j of block b of row r
- *                                          is at byte r*cols/4 + b*8 + j/4,
- *                                          bits 2*(j%4) .. 2*(j%4)+1
- *   bytes [rows*cols/4, rows*cols*3/8)     per block, row-major: uint16 scale
- *                                          bits then uint16 min bits
- *   then zero padding up to moe_q2_packed_bytes(rows, cols).
+ *   s = fp16((hi - float(m)) / (2^b - 1));
+ *   c = 0 if float(s) == 0, else clamp(nearbyint((w - float(m)) / float(s)), 0, 2^b - 1).
+ * Physical layout written by moe_qb_pack (little-endian), nb = cols / 32:
+ *   bytes [0, rows*cols*b/8)               codes: block b' of row r holds 4b
+ *                                          bytes at (r*nb + b')*4b, read as
+ *                                          one little-endian integer with
+ *                                          weight j at bits b*j .. b*j+b-1
+ *   bytes [rows*cols*b/8, rows*cols*(b+1)/8)  per block, row-major: uint16
+ *                                          scale bits then uint16 min bits
+ *   then zero padding up to moe_qb_packed_bytes(b, rows, cols).
  */
 
-/* Bytes of one packed matrix (a multiple of 256), or 0 if rows <= 0 or
- * cols <= 0 or cols % 32 != 0. */
-size_t moe_q2_packed_bytes(int64_t rows, int64_t cols);
+/* Bytes of one packed matrix (a multiple of 256), or 0 if bits is not 2, 3
+ * or 4, rows <= 0, cols <= 0 or cols % 32 != 0. */
+size_t moe_qb_packed_bytes(int32_t bits, int64_t rows, int64_t cols);
 
-/* Host-only packer (the quantizer above, applied block by block): src [rows][cols] fp32 (host) -> dst (host, dst_bytes >=
- * moe_q2_packed_bytes). Returns MOE_ENONFINITE if an input is NaN/Inf or a
- * block's min or scale does not fit fp16, MOE_EWORKSPACE if dst is too small. */
-int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes);
+/* Host-only packer (the quantizer above, applied block by block): src
+ * [rows][cols] fp32 (host) -> dst (host, dst_bytes >= moe_qb_packed_bytes).
+ * Returns MOE_EINVAL for a bits, shape or pointer outside the above,
+ * MOE_ENONFINITE if an input is NaN/Inf or a block's min or scale does not
+ * fit fp16, MOE_EWORKSPACE if dst is too small. */
+int moe_qb_pack(int32_t bits, const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes);
 
 /* Device unpack of one packed matrix to fp32 [rows][cols] (device), bit-exact
  * with the format definition (w = fp32(c * s + m) above). packed: device,
- * 16-byte aligned. */
+ * 16-byte aligned; dst: device, 16-byte aligned. Enqueued on `stream`. */
+int moe_qb_unpack(int32_t bits, const void *packed, int64_t rows, int64_t cols, float *dst, void *stream);
+
+/* The 2-bit instances: moe_qb_*(2, ...). */
+size_t moe_q2_packed_bytes(int64_t rows, int64_t cols);
+int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes);
 int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream);
 
 #ifdef __cplusplus

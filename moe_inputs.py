@@ -37,6 +37,10 @@ STREAM_NORM = 6
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
 
+# Expert formats stored as 32-weight blocks of 2-, 3- or 4-bit codes.
+BLOCK_FORMATS = ("q2", "q3", "q4")
+
+
 @dataclass(frozen=True)
 class LayerConfig:
     """Shape, weight formats and draw parameters of one MoE layer workload."""
@@ -50,7 +54,7 @@ class LayerConfig:
     T: int                # rows of x in the workload
     rows_per_call: int    # rows handed to one forward call (1 = decode)
     router_t: str         # "f32" | "bf16"
-    expert_t: str         # "f32" | "bf16" | "q2"
+    expert_t: str         # "f32" | "bf16" | "q2" | "q3" | "q4"
     shared_t: str         # "f32" | "bf16"
     router_std: float
     expert_std: float = 0.02
@@ -119,13 +123,14 @@ def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
 def expert_matrix_f32(cfg: LayerConfig, e: int, mat: int) -> np.ndarray:
     """Routed expert ``e`` matrix as fp32 values.
 
-    gate/up are [I][H], down is [H][I]. For bf16 and q2 experts the draw is
-    rounded to bf16 first, so the q2 workloads quantize exactly the values the
-    bf16 workload stores (same seed namespace rule as the bf16 case).
+    gate/up are [I][H], down is [H][I]. For bf16 and block-format (q2, q3,
+    q4) experts the draw is rounded to bf16 first, so the block workloads
+    quantize exactly the values the bf16 workload stores (same seed namespace
+    rule as the bf16 case).
     """
     shape = (cfg.I, cfg.H) if mat in (MAT_GATE, MAT_UP) else (cfg.H, cfg.I)
     a = _normal(_rng(cfg, STREAM_EXPERTS, e, mat), shape, cfg.expert_std)
-    if cfg.expert_t in ("bf16", "q2"):
+    if cfg.expert_t == "bf16" or cfg.expert_t in BLOCK_FORMATS:
         a = bf16_bits_to_f32(f32_to_bf16_bits(a)).reshape(shape)
     return a
 
@@ -133,14 +138,14 @@ def expert_matrix_f32(cfg: LayerConfig, e: int, mat: int) -> np.ndarray:
 def expert_matrix_stored(cfg: LayerConfig, e: int, mat: int) -> np.ndarray:
     """Routed expert matrix in its storage format (f32 values or bf16 bits).
 
-    q2 experts are returned as their fp32 source; packing belongs to the
-    consumer (the library packer or the oracle's own quantizer).
+    Block-format experts are returned as their fp32 source; packing belongs to
+    the consumer (the library packer or the oracle's own quantizer).
     """
     shape = (cfg.I, cfg.H) if mat in (MAT_GATE, MAT_UP) else (cfg.H, cfg.I)
     a = _normal(_rng(cfg, STREAM_EXPERTS, e, mat), shape, cfg.expert_std)
     if cfg.expert_t == "bf16":
         return f32_to_bf16_bits(a)
-    if cfg.expert_t == "q2":
+    if cfg.expert_t in BLOCK_FORMATS:
         return bf16_bits_to_f32(f32_to_bf16_bits(a)).reshape(shape)
     return a
 
@@ -156,8 +161,8 @@ def _threads() -> int:
 def expert_stacks(cfg: LayerConfig, experts=None):
     """Stacked routed-expert weights (gate [E][I][H], up [E][I][H], down [E][H][I]).
 
-    f32/bf16 workloads only (q2 stacks are packed matrix by matrix by the
-    consumer). ``experts`` restricts generation to a subset (others are zero).
+    f32/bf16 workloads only (block-format stacks are packed matrix by matrix
+    by the consumer). ``experts`` restricts generation to a subset (others are zero).
     """
     assert cfg.expert_t in ("f32", "bf16")
     dt = np.float32 if cfg.expert_t == "f32" else np.uint16

@@ -17,13 +17,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EALIGN, MOE_EHIP, MOE_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
-MOE_F32, MOE_BF16, MOE_Q2B32 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_Q2B32, MOE_Q3B32, MOE_Q4B32 = 0, 1, 2, 3, 4
 MOE_BIAS_SELECT_AND_WEIGH, MOE_BIAS_SELECT_ONLY = 0, 1
-WTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "q2": MOE_Q2B32}
+WTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "q2": MOE_Q2B32, "q3": MOE_Q3B32, "q4": MOE_Q4B32}
+BITS = {"q2": 2, "q3": 3, "q4": 4}   # code width of the block formats
 
 EXPORTS = ("moe_abi_version", "moe_strerror", "moe_workspace_bytes", "moe_route", "moe_forward",
-           "moe_forward_noalloc", "moe_sort_workspace_bytes", "moe_sort_by_expert", "moe_q2_packed_bytes", "moe_q2_pack",
-           "moe_q2_unpack")
+           "moe_forward_noalloc", "moe_sort_workspace_bytes", "moe_sort_by_expert", "moe_qb_packed_bytes", "moe_qb_pack",
+           "moe_qb_unpack", "moe_q2_packed_bytes", "moe_q2_pack", "moe_q2_unpack")
 
 
 class MoEError(RuntimeError):
@@ -72,6 +73,12 @@ def lib():
             L.moe_sort_workspace_bytes.restype = sz
             L.moe_sort_by_expert.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
             L.moe_sort_by_expert.restype = C.c_int
+            L.moe_qb_packed_bytes.argtypes = [i32, i64, i64]
+            L.moe_qb_packed_bytes.restype = sz
+            L.moe_qb_pack.argtypes = [i32, vp, i64, i64, vp, sz]
+            L.moe_qb_pack.restype = C.c_int
+            L.moe_qb_unpack.argtypes = [i32, vp, i64, i64, vp, vp]
+            L.moe_qb_unpack.restype = C.c_int
             L.moe_q2_packed_bytes.argtypes = [i64, i64]
             L.moe_q2_packed_bytes.restype = sz
             L.moe_q2_pack.argtypes = [vp, i64, i64, vp, sz]
@@ -97,22 +104,34 @@ def strerror(status: int) -> str:
 
 # ------------------------------------------------------------ packer (host)
 
+def qb_packed_bytes(bits: int, rows: int, cols: int) -> int:
+    return int(lib().moe_qb_packed_bytes(bits, rows, cols))
+
+
+def qb_pack(bits: int, w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Pack an fp32 [rows][cols] matrix (host) into the b-bit block format."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w: expected a 2-D matrix")
+    rows, cols = w.shape
+    n = qb_packed_bytes(bits, rows, cols)
+    if n == 0:
+        raise MoEError(MOE_EINVAL, "moe_qb_pack")
+    if out is None:
+        out = np.empty(n, np.uint8)
+    if not (out.dtype == np.uint8 and out.flags.c_contiguous and out.nbytes >= n):
+        raise ValueError("out: expected a contiguous uint8 buffer of moe_qb_packed_bytes bytes")
+    _check(lib().moe_qb_pack(bits, w.ctypes.data, rows, cols, out.ctypes.data, out.nbytes), "moe_qb_pack")
+    return out
+
+
 def q2_packed_bytes(rows: int, cols: int) -> int:
     return int(lib().moe_q2_packed_bytes(rows, cols))
 
 
 def q2_pack(w: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """Pack an fp32 [rows][cols] matrix (host) into the 2-bit block format."""
-    w = np.ascontiguousarray(w, dtype=np.float32)
-    rows, cols = w.shape
-    n = q2_packed_bytes(rows, cols)
-    if n == 0:
-        raise MoEError(MOE_EINVAL, "moe_q2_pack")
-    if out is None:
-        out = np.empty(n, np.uint8)
-    assert out.flags.c_contiguous and out.nbytes >= n
-    _check(lib().moe_q2_pack(w.ctypes.data, rows, cols, out.ctypes.data, out.nbytes), "moe_q2_pack")
-    return out
+    return qb_pack(2, w, out)
 
 
 # --------------------------------------------------------------- device calls
@@ -235,14 +254,18 @@ def sort_by_expert(ids, E: int, counts, offsets, perm, ws, stream=None) -> None:
                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_sort_by_expert")
 
 
-def q2_unpack(packed, rows: int, cols: int, dst, stream=None) -> None:
+def qb_unpack(bits: int, packed, rows: int, cols: int, dst, stream=None) -> None:
     import torch
     _want(dst, "dst", torch.float32, (rows, cols))
     _on_gpu(dst=dst)
-    if packed.numel() * packed.element_size() < q2_packed_bytes(rows, cols) or not packed.is_contiguous() \
+    if packed.numel() * packed.element_size() < qb_packed_bytes(bits, rows, cols) or not packed.is_contiguous() \
             or not packed.is_cuda:
-        raise ValueError("packed: expected a contiguous GPU buffer of moe_q2_packed_bytes(rows, cols) bytes")
-    _check(lib().moe_q2_unpack(_ptr(packed), rows, cols, _ptr(dst), _stream(stream)), "moe_q2_unpack")
+        raise ValueError("packed: expected a contiguous GPU buffer of moe_qb_packed_bytes(bits, rows, cols) bytes")
+    _check(lib().moe_qb_unpack(bits, _ptr(packed), rows, cols, _ptr(dst), _stream(stream)), "moe_qb_unpack")
+
+
+def q2_unpack(packed, rows: int, cols: int, dst, stream=None) -> None:
+    qb_unpack(2, packed, rows, cols, dst, stream)
 
 
 # ------------------------------------------------------------- layer holder
@@ -251,7 +274,8 @@ class Layer:
     """Device-resident weights of one layer and its descriptor.
 
     Built from host arrays (fp32 values, bf16 bit patterns as uint16, or fp32
-    sources of 2-bit experts which are packed here by the library packer).
+    sources of 2-, 3- or 4-bit experts which are packed here by the library
+    packer).
     """
 
     def __init__(self, *, H, E, K, I, Is, router_t, expert_t, shared_t, router_w, gate_vec, router_bias,
@@ -277,7 +301,7 @@ class Layer:
         self.router_bias = up(None if router_bias is None else np.asarray(router_bias, np.float32))
         self.norm_w = up(None if norm_w is None else np.asarray(norm_w, np.float32))
         self.sh_gate, self.sh_up, self.sh_down = up(sh_gate), up(sh_up), up(sh_down)
-        if expert_t == "q2":
+        if expert_t in BITS:
             # expert_source(e, mat) -> fp32 [rows][cols]; mat 0 gate, 1 up, 2 down
             self.exp_gate = self._pack_stack(expert_source, 0, I, H)
             self.exp_up = self._pack_stack(expert_source, 1, I, H)
@@ -335,11 +359,12 @@ class Layer:
     def _pack_stack(self, source, mat, rows, cols):
         import torch
         from concurrent.futures import ThreadPoolExecutor
-        n = q2_packed_bytes(rows, cols)
+        bits = BITS[self.expert_t]
+        n = qb_packed_bytes(bits, rows, cols)
         host = np.empty((self.E, n), np.uint8)
 
         def one(e):
-            q2_pack(source(e, mat), out=host[e])
+            qb_pack(bits, source(e, mat), out=host[e])
 
         with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
             list(ex.map(one, range(self.E)))

@@ -20,8 +20,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.cpp", "decode.hip", "q2_unpack.hip", "sort.hip", "prefill.hip", "noalloc.hip"]
-HOST_SOURCES = ["pack_q2.cpp"]
+HIP_SOURCES = ["api.cpp", "decode.hip", "block_unpack.hip", "sort.hip", "prefill.hip", "noalloc.hip"]
+HOST_SOURCES = ["pack_blocks.cpp"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",

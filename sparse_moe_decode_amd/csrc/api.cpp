@@ -38,7 +38,7 @@ int validate_desc(const moe_layer_desc *d)
         return MOE_EINVAL;
     if ((d->router_t != MOE_F32 && d->router_t != MOE_BF16) ||
         (d->shared_t != MOE_F32 && d->shared_t != MOE_BF16) ||
-        (d->expert_t != MOE_F32 && d->expert_t != MOE_BF16 && d->expert_t != MOE_Q2B32))
+        (d->expert_t < MOE_F32 || d->expert_t > MOE_Q4B32))
         return MOE_EINVAL;
     if (d->n_experts > moe::kMaxE || d->hidden > 8192 || d->inter > 4096 || d->shared_inter > 4096)
         return MOE_EUNSUPPORTED;
@@ -302,14 +302,19 @@ int moe_sort_by_expert(const int32_t *ids, int32_t T, int32_t K, int32_t E, int3
                                       nullptr);
 }
 
-int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream)
+int moe_qb_unpack(int32_t bits, const void *packed, int64_t rows, int64_t cols, float *dst, void *stream)
 {
-    if (!packed || !dst || rows <= 0 || cols <= 0 || cols % 32 != 0)
+    if (bits < 2 || bits > 4 || !packed || !dst || rows <= 0 || cols <= 0 || cols % 32 != 0)
         return MOE_EINVAL;
     if (!aligned16(packed) || !aligned16(dst))
         return MOE_EALIGN;
     (void)hipGetLastError();
-    return moe::launch_q2_unpack(packed, rows, cols, dst, static_cast<hipStream_t>(stream));
+    return moe::launch_qb_unpack(bits, packed, rows, cols, dst, static_cast<hipStream_t>(stream));
+}
+
+int moe_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, void *stream)
+{
+    return moe_qb_unpack(2, packed, rows, cols, dst, stream);
 }
 
 }  // extern "C"

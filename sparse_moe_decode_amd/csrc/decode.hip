@@ -401,8 +401,8 @@ template <typename W>
 struct GuChunks {
     static constexpr int value = 4;
 };
-template <>
-struct GuChunks<Q2> {
+template <int B>
+struct GuChunks<QB<B>> {
     static constexpr int value = 1;
 };
 
@@ -410,6 +410,11 @@ struct GuChunks<Q2> {
 template <typename W>
 struct RowChunks {
     uint4 g[GuChunks<W>::value], u[GuChunks<W>::value];
+};
+template <int B>
+struct RowChunks<QB<B>> {   // 3- and 4-bit blocks: the block's code dwords and its scale/min word
+    uint32_t gc[B], uc[B];
+    uint32_t gs, us;
 };
 template <>
 struct RowChunks<Q2> {
@@ -446,6 +451,37 @@ __device__ __forceinline__ void load_rows(Q2, const MatRef &G, const MatRef &U, 
             r.us[u] = ld_nt4(U.base + static_cast<size_t>(U.rows) * (U.cols >> 2) +
                                                           (static_cast<size_t>(ch) * nb + b) * 4);
         }
+    }
+}
+
+// The 4b code bytes of a 3- or 4-bit block (4-byte aligned) as dwords.
+template <int B>
+__device__ __forceinline__ void load_block_codes(const uint8_t *p, uint32_t (&cw)[B])
+{
+    if constexpr (B == 4) {
+        const uint4 v = ld_nt16(p);
+        cw[0] = v.x;
+        cw[1] = v.y;
+        cw[2] = v.z;
+        cw[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i)
+            cw[i] = ld_nt4(p + 4 * i);
+    }
+}
+template <int B>
+__device__ __forceinline__ void load_rows(QB<B>, const MatRef &G, const MatRef &U, int ch, int base, int lane, int nch,
+                                          RowChunks<QB<B>> &r)
+{
+    const int nb = G.cols >> 5;
+    const int b = base + lane;
+    if (b < nch) {
+        const size_t blk = static_cast<size_t>(ch) * nb + b;
+        load_block_codes<B>(G.base + blk * 4 * B, r.gc);
+        load_block_codes<B>(U.base + blk * 4 * B, r.uc);
+        r.gs = ld_nt4(G.base + static_cast<size_t>(G.rows) * nb * 4 * B + blk * 4);
+        r.us = ld_nt4(U.base + static_cast<size_t>(U.rows) * nb * 4 * B + blk * 4);
     }
 }
 
@@ -533,6 +569,49 @@ __device__ __forceinline__ void dot_block2(const uint2 &gc0, uint32_t gsm, const
     }
 }
 
+// 3- and 4-bit blocks: the codes stay in place (extracted at fixed bit
+// positions) and x chunk c of the block is read from its staged slot
+// x_chunk_slot(b, c).
+template <int B, int R>
+__device__ __forceinline__ void dot_block_b(const uint32_t (&gc)[B], uint32_t gsm, const uint32_t (&uc)[B],
+                                            uint32_t usm, int b, const float *xs, int H, const float *xsum,
+                                            float (&a)[R], float (&c)[R])
+{
+    float ga[R], ua[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        ga[q] = ua[q] = 0.0f;
+    // the slot offset of the block, opaque so that the eight slot addresses
+    // are formed here (one xor each) rather than hoisted out of the item
+    // loop, where they would be held in registers for the whole kernel
+    int m = b & 7;
+    asm volatile("" : "+v"(m));
+    // chunk by chunk: its 4 gate and 4 up codes once, then every row
+#pragma unroll
+    for (int cl = 0; cl < 8; ++cl) {
+        float g[4], u[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            g[k] = static_cast<float>(block_code<B>(gc, 4 * cl + k));
+            u[k] = static_cast<float>(block_code<B>(uc, 4 * cl + k));
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float4 xv = reinterpret_cast<const float4 *>(xs + q * H + b * 32)[cl ^ m];   // x_chunk_slot(b, cl)
+            ga[q] = fmaf(g[0], xv.x, fmaf(g[1], xv.y, fmaf(g[2], xv.z, fmaf(g[3], xv.w, ga[q]))));
+            ua[q] = fmaf(u[0], xv.x, fmaf(u[1], xv.y, fmaf(u[2], xv.z, fmaf(u[3], xv.w, ua[q]))));
+        }
+    }
+    const float gsc = f16_to_f32(gsm & 0xffffu), gmn = f16_to_f32(gsm >> 16);
+    const float usc = f16_to_f32(usm & 0xffffu), umn = f16_to_f32(usm >> 16);
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float sx = xsum[q * (H >> 5) + b];
+        a[q] = fmaf(gsc, ga[q], fmaf(gmn, sx, a[q]));
+        c[q] = fmaf(usc, ua[q], fmaf(umn, sx, c[q]));
+    }
+}
+
 template <int R, typename W>
 __device__ __forceinline__ void dot_rows(W, const RowChunks<W> &r, int base, int lane, int nch, const float *xs,
                                          int H, const float *, float (&a)[R], float (&c)[R])
@@ -557,13 +636,21 @@ __device__ __forceinline__ void dot_rows(Q2, const RowChunks<Q2> &r, int base, i
             dot_block2<R>(r.gc[u], r.gs[u], r.uc[u], r.us[u], b, xs, H, xsum, a, c);
     }
 }
+template <int R, int B>
+__device__ __forceinline__ void dot_rows(QB<B>, const RowChunks<QB<B>> &r, int base, int lane, int nch,
+                                         const float *xs, int H, const float *xsum, float (&a)[R], float (&c)[R])
+{
+    const int b = base + lane;
+    if (b < nch)
+        dot_block_b<B, R>(r.gc, r.gs, r.uc, r.us, b, xs, H, xsum, a, c);
+}
 
 // x of all rows into LDS (with the layer's RMS norm applied when gamma is
-// given), plus per-32 block sums when W is the 2-bit format.
+// given), plus per-32 block sums when W is a block format.
 template <int R, typename W>
 __device__ __forceinline__ void stage_x(const float *x, int H, float *xs, float *xsum, const float *gamma, float eps)
 {
-    // 2-bit weights: chunk c of block b of a row at slot x_chunk_slot(b, c)
+    // block formats: chunk c of block b of a row at slot x_chunk_slot(b, c)
     const int n4 = H >> 2;
     for (int i = threadIdx.x; i < R * n4; i += blockDim.x) {
         int d = i;
@@ -1037,13 +1124,68 @@ struct DnPiece<Q2> {
     }
 };
 
+// 3- and 4-bit pieces: 8 codes of B bits (B bytes at byte 8*B*c/8 of the
+// row's codes: one aligned dword for B = 4; for B = 3 the two aligned dwords
+// around the 3 bytes, joined by a funnel shift), plus the block's scale/min.
+template <int B>
+struct DnPiece<QB<B>> {
+    static constexpr int kElems = 8;
+    using Dec = DnPiece<Q2>::Dec;
+    uint32_t codes;   // code k at bits B*k
+    uint32_t sm;
+    static __device__ __forceinline__ size_t row_bytes(const MatRef &M) { return static_cast<size_t>(M.cols) * B / 8; }
+    __device__ __forceinline__ void load(const MatRef &M, int j, int c)
+    {
+        const int nb = M.cols >> 5;
+        const uint8_t *row = M.base + static_cast<size_t>(j) * row_bytes(M);
+        if constexpr (B == 4) {
+            codes = ld_nt4(row + c * 4);
+        } else {
+            const int o = c * B;
+            const uint32_t lo = ld_nt4(row + (o & ~3)), hi = ld_nt4(row + (o & ~3) + 4);
+            codes = __builtin_amdgcn_alignbit(hi, lo, 8 * (o & 3));
+        }
+        sm = ld_nt4(M.base + static_cast<size_t>(M.rows) * row_bytes(M) + (static_cast<size_t>(j) * nb + (c >> 2)) * 4);
+    }
+    __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t r, const MatRef &M, int j, int c, bool ok)
+    {
+        const int nb = M.cols >> 5;
+        const uint32_t rb = static_cast<uint32_t>(row_bytes(M));
+        const uint32_t os = ok ? static_cast<uint32_t>(M.rows * rb + (j * nb + (c >> 2)) * 4) : kPastEnd;
+        if constexpr (B == 4) {
+            codes = __builtin_amdgcn_raw_buffer_load_b32(r, ok ? j * rb + c * 4 : kPastEnd, 0, kAuxNT);
+        } else {
+            const int o = c * B;
+            const uint32_t oc = ok ? static_cast<uint32_t>(j * rb + (o & ~3)) : kPastEnd;
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(r, oc, 0, kAuxNT);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r, ok ? oc + 4 : kPastEnd, 0, kAuxNT);
+            codes = __builtin_amdgcn_alignbit(hi, lo, 8 * (o & 3));
+        }
+        sm = __builtin_amdgcn_raw_buffer_load_b32(r, os, 0, kAuxNT);
+    }
+    __device__ __forceinline__ Dec dec() const
+    {
+        Dec d;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            d.c[k] = static_cast<float>((codes >> (B * k)) & ((1u << B) - 1u));
+        d.s = f16_to_f32(sm & 0xffffu);
+        d.m = f16_to_f32(sm >> 16);
+        return d;
+    }
+    __device__ __forceinline__ void fma1(const float *h, int c, float &acc) const
+    {
+        DnPiece<Q2>::fma_d(dec(), h, c, DnPiece<Q2>::hsum(h, c), acc);
+    }
+};
+
 template <typename W>
 struct DnBatch {
     static constexpr int value = 12;   // 16-byte pieces in flight per lane
 };
-template <>
-struct DnBatch<Q2> {
-    static constexpr int value = 32;   // 2 + 4 bytes per piece
+template <int B>
+struct DnBatch<QB<B>> {
+    static constexpr int value = B == 3 ? 24 : 32;   // 2-4 bytes of codes (3 bits: two dwords) + 4 per piece
 };
 
 // Down projection and combine, one output row j per wave:
@@ -1124,10 +1266,10 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     }
     gate[tq] = t_gate;
     const float *hl = p.hbuf;
-    // One-row calls with 2-bit pieces also use the sum of each 8-value piece
+    // One-row calls with block-format pieces also use the sum of each 8-value piece
     // of h': formed here once per workgroup from the two float4 halves held
     // by lanes 2i, 2i+1 (measured slower with several rows)
-    constexpr bool HS = STAGED && R == 1 && std::is_same<ET, Q2>::value;
+    constexpr bool HS = STAGED && R == 1 && is_block_format<ET>::value;
     float *hsl = reinterpret_cast<float *>(lds_raw) + (HS ? p.max_pairs * p.Imax : 0);
     if (STAGED) {
         float4 *dst = reinterpret_cast<float4 *>(lds_raw);
@@ -1397,9 +1539,9 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     dn.hbuf = w.hbuf;
     dn.max_pairs = max_pairs(R, K);
     const dim3 dgrid((H + kDnWaves - 1) / kDnWaves), dblock(kDnWaves * kWave);
-    // staged h' (and, for one row with 2-bit experts, one sum per 8-value piece)
+    // staged h' (and, for one row with block-format experts, one sum per 8-value piece)
     const size_t stage =
-        static_cast<size_t>(dn.max_pairs) * Imax * sizeof(float) * (R == 1 && std::is_same<ET, Q2>::value ? 9 : 8) / 8;
+        static_cast<size_t>(dn.max_pairs) * Imax * sizeof(float) * (R == 1 && is_block_format<ET>::value ? 9 : 8) / 8;
     if (stage <= kDnStageLds) {
         switch (R) {
         case 1: hipLaunchKernelGGL((k_down<1, ET, ST, true>), dgrid, dblock, stage, s, dn); break;
@@ -1431,13 +1573,21 @@ int launch_decode_forward(const moe_layer_desc *d, const float *x, int R, float 
     const RoutingIO io{ids_in, wts_in, gate_in, ids_out, wts_out, gate_out};
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32) {
-        if (et == MOE_F32) return launch_experts_t<F32, F32>(d, x, R, y, io, w, s);
-        if (et == MOE_BF16) return launch_experts_t<BF16, F32>(d, x, R, y, io, w, s);
-        return launch_experts_t<Q2, F32>(d, x, R, y, io, w, s);
+        switch (et) {
+        case MOE_F32: return launch_experts_t<F32, F32>(d, x, R, y, io, w, s);
+        case MOE_BF16: return launch_experts_t<BF16, F32>(d, x, R, y, io, w, s);
+        case MOE_Q2B32: return launch_experts_t<Q2, F32>(d, x, R, y, io, w, s);
+        case MOE_Q3B32: return launch_experts_t<Q3, F32>(d, x, R, y, io, w, s);
+        default: return launch_experts_t<Q4, F32>(d, x, R, y, io, w, s);
+        }
     }
-    if (et == MOE_F32) return launch_experts_t<F32, BF16>(d, x, R, y, io, w, s);
-    if (et == MOE_BF16) return launch_experts_t<BF16, BF16>(d, x, R, y, io, w, s);
-    return launch_experts_t<Q2, BF16>(d, x, R, y, io, w, s);
+    switch (et) {
+    case MOE_F32: return launch_experts_t<F32, BF16>(d, x, R, y, io, w, s);
+    case MOE_BF16: return launch_experts_t<BF16, BF16>(d, x, R, y, io, w, s);
+    case MOE_Q2B32: return launch_experts_t<Q2, BF16>(d, x, R, y, io, w, s);
+    case MOE_Q3B32: return launch_experts_t<Q3, BF16>(d, x, R, y, io, w, s);
+    default: return launch_experts_t<Q4, BF16>(d, x, R, y, io, w, s);
+    }
 }
 
 // Routing only: the logits, then the routing workgroup (no slot table).

@@ -17,8 +17,8 @@ constexpr int kMaxRows = 4;   // rows per few-row call
 // ------------------------------------------------------------ formats
 //
 // Every matrix is read in 16-byte "chunks" (f32: 4 values, bf16: 8 values)
-// or, for the 2-bit format, in 32-weight blocks (8 bytes of codes plus one
-// dword holding the fp16 scale and min).
+// or, for the b-bit block formats, in 32-weight blocks (4b bytes of codes
+// plus one dword holding the fp16 scale and min).
 
 struct F32 {
     static constexpr int kChunk = 4;   // elements per chunk
@@ -26,8 +26,22 @@ struct F32 {
 struct BF16 {
     static constexpr int kChunk = 8;
 };
-struct Q2 {
+template <int B>
+struct QB {
     static constexpr int kChunk = 32;
+    static constexpr int kBits = B;
+};
+using Q2 = QB<2>;
+using Q3 = QB<3>;
+using Q4 = QB<4>;
+
+template <typename W>
+struct is_block_format {
+    static constexpr bool value = false;
+};
+template <int B>
+struct is_block_format<QB<B>> {
+    static constexpr bool value = true;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -43,102 +57,47 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16)
 }
 
 // A dense matrix of type F32/BF16: row-major, `cols` elements per row.
-// A Q2 matrix: codes plane then scale/min plane (see moe_q2_pack).
+// A b-bit matrix: codes plane then scale/min plane (see moe_qb_pack).
 struct MatRef {
     const uint8_t *base;   // matrix start
     int rows, cols;
 };
 
-// Byte size of one stacked matrix of each format.
-__host__ __device__ inline size_t q2_packed_bytes(int64_t rows, int64_t cols)
+// Byte size of one stacked b-bit matrix: (b + 1) / 8 bytes per weight,
+// rounded up to 256.
+__host__ __device__ inline size_t qb_packed_bytes(int bits, int64_t rows, int64_t cols)
 {
-    const uint64_t raw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols) / 8u * 3u;
+    const uint64_t raw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols) / 8u * static_cast<uint64_t>(bits + 1);
     return static_cast<size_t>((raw + 255u) / 256u * 256u);
 }
 
 template <typename W>
-__host__ __device__ inline size_t mat_bytes(int64_t rows, int64_t cols);
+struct MatBytes;
 template <>
-__host__ __device__ inline size_t mat_bytes<F32>(int64_t rows, int64_t cols) { return rows * cols * 4; }
+struct MatBytes<F32> {
+    __host__ __device__ static size_t of(int64_t rows, int64_t cols) { return rows * cols * 4; }
+};
 template <>
-__host__ __device__ inline size_t mat_bytes<BF16>(int64_t rows, int64_t cols) { return rows * cols * 2; }
-template <>
-__host__ __device__ inline size_t mat_bytes<Q2>(int64_t rows, int64_t cols) { return q2_packed_bytes(rows, cols); }
+struct MatBytes<BF16> {
+    __host__ __device__ static size_t of(int64_t rows, int64_t cols) { return rows * cols * 2; }
+};
+template <int B>
+struct MatBytes<QB<B>> {
+    __host__ __device__ static size_t of(int64_t rows, int64_t cols) { return qb_packed_bytes(B, rows, cols); }
+};
+template <typename W>
+__host__ __device__ inline size_t mat_bytes(int64_t rows, int64_t cols) { return MatBytes<W>::of(rows, cols); }
 
-// ----------------------------------------------------------- chunk dots
-//
-// dot of chunk `c` of row `r` with a vector v (fp32, in LDS), accumulated
-// into acc[R] for R vectors laid out with stride `vs`. For Q2 `vsum` holds
-// the per-block sums of each vector (stride vss), used for the min term:
-//   sum_j (code_j*s + m) v_j = s * sum_j code_j v_j + m * sum_j v_j.
-
-template <int R>
-__device__ __forceinline__ void chunk_dot(F32, const MatRef &M, int r, int c, const float *v, int vs,
-                                          const float *, int, float (&acc)[R])
+// Code j (0..31) of a b-bit block held as dwords cw[] (the block's 4b bytes
+// read little-endian): bits b*j .. b*j+b-1; a code that straddles two
+// dwords is joined with one funnel shift. j is a compile-time constant after
+// unrolling, so each code costs one or two instructions.
+template <int B, int N>
+__device__ __forceinline__ uint32_t block_code(const uint32_t (&cw)[N], int j)
 {
-    const float4 w = *reinterpret_cast<const float4 *>(M.base + (static_cast<size_t>(r) * M.cols + c * 4) * 4);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float4 xv = *reinterpret_cast<const float4 *>(v + q * vs + c * 4);
-        acc[q] = fmaf(w.x, xv.x, acc[q]);
-        acc[q] = fmaf(w.y, xv.y, acc[q]);
-        acc[q] = fmaf(w.z, xv.z, acc[q]);
-        acc[q] = fmaf(w.w, xv.w, acc[q]);
-    }
-}
-
-template <int R>
-__device__ __forceinline__ void chunk_dot(BF16, const MatRef &M, int r, int c, const float *v, int vs,
-                                          const float *, int, float (&acc)[R])
-{
-    const uint4 w = *reinterpret_cast<const uint4 *>(M.base + (static_cast<size_t>(r) * M.cols + c * 8) * 2);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(v + q * vs + c * 8);
-        const float4 x1 = *reinterpret_cast<const float4 *>(v + q * vs + c * 8 + 4);
-        float a = acc[q];
-        a = fmaf(bf16_lo(w.x), x0.x, a);
-        a = fmaf(bf16_hi(w.x), x0.y, a);
-        a = fmaf(bf16_lo(w.y), x0.z, a);
-        a = fmaf(bf16_hi(w.y), x0.w, a);
-        a = fmaf(bf16_lo(w.z), x1.x, a);
-        a = fmaf(bf16_hi(w.z), x1.y, a);
-        a = fmaf(bf16_lo(w.w), x1.z, a);
-        a = fmaf(bf16_hi(w.w), x1.w, a);
-        acc[q] = a;
-    }
-}
-
-// codes of one 32-weight block: two dwords, weight j at bits 2*(j%16) of dword j/16
-template <int R>
-__device__ __forceinline__ void chunk_dot(Q2, const MatRef &M, int r, int b, const float *v, int vs,
-                                          const float *vsum, int vss, float (&acc)[R])
-{
-    const int nb = M.cols >> 5;
-    const uint2 cw = *reinterpret_cast<const uint2 *>(M.base + static_cast<size_t>(r) * (M.cols >> 2) + b * 8);
-    const uint32_t sm = *reinterpret_cast<const uint32_t *>(
-        M.base + static_cast<size_t>(M.rows) * (M.cols >> 2) + (static_cast<size_t>(r) * nb + b) * 4);
-    const float s = f16_to_f32(sm & 0xffffu);
-    const float m = f16_to_f32(sm >> 16);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const float *x = v + q * vs + b * 32;
-        float cx = 0.0f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint32_t d = half ? cw.y : cw.x;
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                const float4 xv = *reinterpret_cast<const float4 *>(x + half * 16 + j4 * 4);
-                const uint32_t byte = d >> (8 * j4);
-                cx = fmaf(static_cast<float>(byte & 3u), xv.x, cx);
-                cx = fmaf(static_cast<float>((byte >> 2) & 3u), xv.y, cx);
-                cx = fmaf(static_cast<float>((byte >> 4) & 3u), xv.z, cx);
-                cx = fmaf(static_cast<float>((byte >> 6) & 3u), xv.w, cx);
-            }
-        }
-        acc[q] = fmaf(s, cx, fmaf(m, vsum[q * vss + b], acc[q]));
-    }
+    const int bit = B * j, w = bit >> 5, sh = bit & 31;
+    const uint32_t v = sh + B <= 32 ? cw[w] >> sh : __builtin_amdgcn_alignbit(cw[w + 1], cw[w], sh);
+    return v & ((1u << B) - 1u);
 }
 
 // ----------------------------------------------------------- reductions

@@ -20,8 +20,8 @@ int launch_decode_forward(const moe_layer_desc *d, const float *x, int R, float 
                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,
                           float *gate_out, void *ws, hipStream_t s);
 
-// 2-bit unpack
-int launch_q2_unpack(const void *packed, int64_t rows, int64_t cols, float *dst, hipStream_t s);
+// b-bit block unpack (bits 2, 3, 4)
+int launch_qb_unpack(int bits, const void *packed, int64_t rows, int64_t cols, float *dst, hipStream_t s);
 
 // stable counting sort of (row, slot) pairs by expert
 size_t sort_ws_bytes_tke(int64_t n, int E);

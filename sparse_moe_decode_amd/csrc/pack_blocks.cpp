@@ -1,11 +1,14 @@
-// Host-side packer for the 2-bit block weight format (MOE_Q2B32).
+// Host-side packer for the b-bit block weight formats (MOE_Q2B32,
+// MOE_Q3B32, MOE_Q4B32; b = 2, 3, 4).
 //
-// Format: 32 weights per block along a row, 2-bit unsigned codes, fp16 scale
+// Format: 32 weights per block along a row, b-bit unsigned codes, fp16 scale
 // and fp16 minimum, w = code * scale + min. The pages' kernels work on
 // 32-weight chunks of the expert rows (Red Lite "Research notes, October
 // 2026", section 4, narrow-row mul_mv entry); the block, code width and
-// formula are the layer's stated 2-bit format. Quantizer rule and physical
-// layout are documented in include/moe.h.
+// formula are the layer's stated 2-bit format, and the 3- and 4-bit widths
+// are the higher-precision expert files of the same model ("DwarfStar Red
+// Lite" guide, the IQ3_XXS file). Quantizer rule and physical layout are
+// documented in include/moe.h.
 //
 // Built with -ffp-contract=off: every float operation below is one IEEE
 // binary32 operation with round-to-nearest-even.
@@ -74,28 +77,33 @@ float f16_bits_to_f32(uint16_t h)
     return f;
 }
 
+bool bits_ok(int32_t bits) { return bits >= 2 && bits <= 4; }
+
 }  // namespace
 
-extern "C" size_t moe_q2_packed_bytes(int64_t rows, int64_t cols)
+extern "C" size_t moe_qb_packed_bytes(int32_t bits, int64_t rows, int64_t cols)
 {
-    if (rows <= 0 || cols <= 0 || cols % 32 != 0)
+    if (!bits_ok(bits) || rows <= 0 || cols <= 0 || cols % 32 != 0)
         return 0;
-    const uint64_t raw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols) / 8u * 3u;
+    // b bits of code plus 32 bits of scale/min per 32 weights: (b + 1) / 8 bytes per weight
+    const uint64_t raw = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols) / 8u * static_cast<uint64_t>(bits + 1);
     return static_cast<size_t>((raw + 255u) / 256u * 256u);
 }
 
-extern "C" int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes)
+extern "C" int moe_qb_pack(int32_t bits, const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes)
 {
-    if (!src || !dst || rows <= 0 || cols <= 0 || cols % 32 != 0)
+    if (!bits_ok(bits) || !src || !dst || rows <= 0 || cols <= 0 || cols % 32 != 0)
         return MOE_EINVAL;
-    const size_t need = moe_q2_packed_bytes(rows, cols);
+    const size_t need = moe_qb_packed_bytes(bits, rows, cols);
     if (dst_bytes < need)
         return MOE_EWORKSPACE;
+    const int top = (1 << bits) - 1;
+    const float levels = static_cast<float>(top);
+    const int64_t nb = cols / 32, cbytes = 4 * bits;   // code bytes per block
     uint8_t *out = static_cast<uint8_t *>(dst);
-    const int64_t nb = cols / 32;
     uint8_t *codes = out;
-    uint8_t *sm = out + rows * cols / 4;
-    const size_t used = static_cast<size_t>(rows * cols / 8 * 3);
+    uint8_t *sm = out + rows * nb * cbytes;
+    const size_t used = static_cast<size_t>(rows * nb * (cbytes + 4));
     std::memset(out + used, 0, need - used);
 
     for (int64_t r = 0; r < rows; ++r) {
@@ -112,21 +120,29 @@ extern "C" int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *d
             const uint16_t min_h = f32_to_f16_bits(lo);
             const float minf = f16_bits_to_f32(min_h);
             const float span = hi - minf;
-            const float step = span / 3.0f;
+            const float step = span / levels;
             const uint16_t scale_h = f32_to_f16_bits(step);
             const float scalef = f16_bits_to_f32(scale_h);
             if (!std::isfinite(minf) || !std::isfinite(scalef))
                 return MOE_ENONFINITE;
-            uint8_t cb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            // the block's codes as one little-endian integer of 32*b bits,
+            // weight j at bits b*j .. b*j+b-1
+            uint64_t acc[2] = {0, 0};
             if (scalef != 0.0f) {
                 for (int j = 0; j < 32; ++j) {
                     const float t = (w[j] - minf) / scalef;
                     const float n = std::nearbyint(t);
-                    const int c = n <= 0.0f ? 0 : (n >= 3.0f ? 3 : static_cast<int>(n));
-                    cb[j >> 2] = static_cast<uint8_t>(cb[j >> 2] | (c << ((j & 3) * 2)));
+                    const uint64_t c = n <= 0.0f ? 0u : (n >= levels ? static_cast<uint64_t>(top)
+                                                                      : static_cast<uint64_t>(n));
+                    const int bit = bits * j;
+                    acc[bit >> 6] |= c << (bit & 63);
+                    if ((bit & 63) + bits > 64)
+                        acc[(bit >> 6) + 1] |= c >> (64 - (bit & 63));
                 }
             }
-            std::memcpy(codes + r * (cols / 4) + b * 8, cb, 8);
+            uint8_t *cb = codes + (r * nb + b) * cbytes;
+            for (int i = 0; i < cbytes; ++i)
+                cb[i] = static_cast<uint8_t>(acc[i >> 3] >> (8 * (i & 7)));
             uint8_t *p = sm + (r * nb + b) * 4;
             p[0] = static_cast<uint8_t>(scale_h & 0xff);
             p[1] = static_cast<uint8_t>(scale_h >> 8);
@@ -135,4 +151,11 @@ extern "C" int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *d
         }
     }
     return MOE_OK;
+}
+
+extern "C" size_t moe_q2_packed_bytes(int64_t rows, int64_t cols) { return moe_qb_packed_bytes(2, rows, cols); }
+
+extern "C" int moe_q2_pack(const float *src, int64_t rows, int64_t cols, void *dst, size_t dst_bytes)
+{
+    return moe_qb_pack(2, src, rows, cols, dst, dst_bytes);
 }

@@ -847,12 +847,13 @@ __global__ void __launch_bounds__(256) k_single_sum(const float *part, int ks, i
     out[i] = s;
 }
 
-// 2-bit main loop. B arrives in mega-steps of 8 blocks: 8 consecutive lanes
-// read one B row's 8 blocks (64 bytes of codes and 32 of scale/min words), so
-// each wave-wide load touches 8 rows of one matrix; the raw words are held in
-// registers one mega-step ahead, then the codes go to LDS as they are and the
-// scales as fp32. Each wave expands the codes of its own B operands to bf16
-// in registers (8 codes per lane per operand). A: each thread holds BM/32
+// Block-format main loop (b-bit codes, b = 2, 3, 4; the weight operand is
+// called B below). B arrives in mega-steps of 8 blocks: 8 consecutive lanes
+// read one B row's 8 blocks (8 * 4b bytes of codes and 32 of scale/min
+// words), so each wave-wide load touches 8 rows of one matrix; the raw words
+// are held in registers one mega-step ahead, then the codes go to LDS as they
+// are and the scales as fp32. Each wave expands the codes of its own B
+// operands to bf16 in registers (8 codes per lane per operand). A: each thread holds BM/32
 // 16-byte pieces (row, part, hi or lo) of 4 consecutive blocks; a group of 4
 // blocks goes to LDS at once (one barrier per group) and each block's pieces
 // are reloaded with the block 4 steps ahead as soon as they are stored.
@@ -864,8 +865,12 @@ constexpr int kAG = 4;           // A blocks per LDS group (and register ring sl
 // Word 3 of a raw buffer descriptor on gfx9 targets (32-bit data format;
 // offsets past num_records read as zero).
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kRawC = 2 * kMS + 1;   // LDS row stride (dwords) of raw codes
 constexpr int kRawS = kMS + 1;       // LDS row stride (floats) of scales
+// LDS row stride (dwords) of the raw codes of b-bit blocks
+template <int BITS>
+struct RawCodes {
+    static constexpr int kStride = BITS * kMS + 1;
+};
 
 // 8 codes (16 bits, code i at bits 2i..2i+1) -> the bf16 values 1 + c/4
 // (exact): each code becomes the top two mantissa bits of 1.0 (0x3F80), so
@@ -875,7 +880,10 @@ constexpr int kRawS = kMS + 1;       // LDS row stride (floats) of scales
 // one2 = 0x3F803F80 (a pair of bf16 1.0) in a register the compiler cannot
 // see through, so that each (shifted y & mask) | one2 is one bit-field insert
 // (one2 has no bits under the mask).
-__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c16, uint32_t one2)
+template <int BITS>
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c, uint32_t one2);
+template <>
+__device__ __forceinline__ bf16x8 codes_bf16<2>(uint32_t c16, uint32_t one2)
 {
     constexpr uint32_t m = 0x00600060u;
     const uint32_t y = c16 | (c16 << 14);
@@ -885,10 +893,65 @@ __device__ __forceinline__ bf16x8 codes_bf16(uint32_t c16, uint32_t one2)
     const uint32_t w3 = ((y >> 7) & m) | (one2 & ~m);
     return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
 }
-
-template <bool DUAL, int BM>
-__global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
+// 3- and 4-bit codes (code i at bits b*i of c): the bf16 values 1 + c/2^b,
+// exact for b <= 7, with the code in the top b mantissa bits; the weight
+// s*c + m equals (2^b s)*v + (m - 2^b s).
+template <int BITS>
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t c, uint32_t one2)
 {
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (c >> (2 * j * BITS)) & mask, hi = (c >> ((2 * j + 1) * BITS)) & mask;
+        w[j] = (lo << (7 - BITS)) | (hi << (23 - BITS)) | one2;
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// The raw words of one (B row, block): BITS dwords of codes.
+template <int BITS>
+__device__ __forceinline__ void load_raw_codes(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&cw)[BITS])
+{
+    if constexpr (BITS == 2) {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        cw[0] = v.x;
+        cw[1] = v.y;
+    } else if constexpr (BITS == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+        cw[0] = v[0];
+        cw[1] = v[1];
+        cw[2] = v[2];
+    } else {
+        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        cw[0] = v.x;
+        cw[1] = v.y;
+        cw[2] = v.z;
+        cw[3] = v.w;
+    }
+}
+
+// The 8 codes (8*BITS bits) of quarter kq of one block's raw words in LDS.
+template <int BITS>
+__device__ __forceinline__ uint32_t quarter_codes(const uint32_t *raw, int kq)
+{
+    if constexpr (BITS == 2)
+        return (raw[kq >> 1] >> (16 * (kq & 1))) & 0xffffu;
+    else if constexpr (BITS == 4)
+        return raw[kq];
+    else {
+        const int bit = 24 * kq, w = bit >> 5;   // the 24 bits may straddle two dwords
+        return __builtin_amdgcn_alignbit(raw[w + 1], raw[w], bit & 31) & 0xffffffu;
+    }
+}
+
+// Workgroups per CU: three 32-row tiles of 2-bit blocks; the wider raw
+// codes of 3- and 4-bit blocks (55-64 KiB of LDS per workgroup) fit two.
+template <int BITS, bool DUAL, int BM>
+__global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_ggemm_qb(GemmArgs p)
+{
+    constexpr int kRawC = RawCodes<BITS>::kStride;
+    constexpr float kLevels = static_cast<float>(1 << BITS);   // 2^b
     using S = GemmShape<BM>;
     constexpr int AP = BM / 32;            // A pieces per thread per block
     constexpr int BL = kGN * kMS / 256;    // (row, block) words per thread per mega-step
@@ -906,13 +969,13 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
     const int e = Ltile[0], r0 = Ltile[1], nrows = Ltile[2];
     const int n0 = blockIdx.x * (DUAL ? kGN / 2 : kGN);
     const int NB = p.Kd / 32;
-    const size_t plane = static_cast<size_t>(p.N) * (p.Kd >> 2);   // bytes of the codes plane
+    const size_t plane = static_cast<size_t>(p.N) * (p.Kd / 32) * 4 * BITS;   // bytes of the codes plane
 
     // B raw words: wave w loads 64 consecutive B rows of one matrix (DUAL:
     // waves 0-1 gate, 2-3 up), 8 rows per instruction
     const int bl = tid & 7;
     const size_t eoff = p.routed ? static_cast<size_t>(e) * p.bstride : 0;
-    const int rowb = p.Kd >> 2;   // bytes of codes per B row
+    const int rowb = (p.Kd / 32) * 4 * BITS;   // bytes of codes per B row
     const int msel = DUAL ? __builtin_amdgcn_readfirstlane(tid >> 7) : 0;   // wave-uniform
     const uint8_t *mbase = (msel ? p.b1 : p.b0) + eoff;
     const __amdgpu_buffer_rsrc_t rcode =
@@ -921,7 +984,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase + plane), 0, p.N * NB * 4, kBufWord3);
     const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + ((tid & 63) >> 3);   // local channel of row j: + 8 j
     const int ch0 = n0 + chl0;
-    uint2 rc[BL];
+    uint32_t rc[BL][BITS];
     uint32_t rs[BL];
     auto load_b = [&](int M) {
         const int blk = M * kMS + bl;
@@ -929,7 +992,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < BL; ++j) {
             const int n = ch0 + 8 * j;
-            rc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rcode, n * rowb + bb * 8, 0, 0));
+            load_raw_codes<BITS>(rcode, n * rowb + bb * 4 * BITS, rc[j]);
             rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rsmw, (n * NB + bb) * 4, 0, 0);
         }
     };
@@ -985,9 +1048,10 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < BL; ++j) {
                 const int row = lds_row(chl0 + 8 * j);
-                Lrc[row * kRawC + 2 * bl] = in ? rc[j].x : 0u;
-                Lrc[row * kRawC + 2 * bl + 1] = in ? rc[j].y : 0u;
-                Lsc[row * kRawS + bl] = in ? 4.0f * f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+#pragma unroll
+                for (int i = 0; i < BITS; ++i)
+                    Lrc[row * kRawC + BITS * bl + i] = in ? rc[j][i] : 0u;
+                Lsc[row * kRawS + bl] = in ? kLevels * f16_to_f32(rs[j] & 0xffffu) : 0.0f;
             }
         }
         if (M + 1 < nms)
@@ -1022,8 +1086,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
 #pragma unroll
                 for (int ct = 0; ct < S::CT; ++ct) {
                     const int c = wc * S::TC + ct * 16 + li;
-                    const uint32_t cw = Lrc[c * kRawC + 2 * b + (kq >> 1)];
-                    const bf16x8 fb = codes_bf16((cw >> (16 * (kq & 1))) & 0xffffu, one2);
+                    const bf16x8 fb = codes_bf16<BITS>(quarter_codes<BITS>(&Lrc[c * kRawC + BITS * b], kq), one2);
                     const float sc = Lsc[c * kRawS + b];
 #pragma unroll
                     for (int rt = 0; rt < S::RT; ++rt) {
@@ -1040,9 +1103,10 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
         }
     }
 
-    // minimum terms: acc += sum_b asum[row][b] * (m[col][b] - 4 s[col][b])
-    // (the offset of the 1 + c/4 code values), 32 blocks per MFMA; m and -4s
-    // are fp16 values, exact as bf16 hi + lo, and enter separately
+    // minimum terms: acc += sum_b asum[row][b] * (m[col][b] - 2^b s[col][b])
+    // (the offset of the 1 + c/2^b code values), 32 blocks per MFMA; m and
+    // -2^b s are fp16 values times a power of two, exact as bf16 hi + lo, and
+    // enter separately
     for (int b0 = 0; b0 < NB; b0 += 32) {
         bf16x8 xah[S::RT], xal[S::RT];
 #pragma unroll
@@ -1068,7 +1132,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? 3 : 1) k_ggemm_q2(GemmArgs p)
                 const uint32_t w =
                     (cn < p.N && b < NB) ? ld_nt4(cm + plane + (static_cast<size_t>(cn) * NB + b) * 4) : 0u;
                 vm[j] = f16_to_f32(w >> 16);
-                vs[j] = -4.0f * f16_to_f32(w & 0xffffu);
+                vs[j] = -kLevels * f16_to_f32(w & 0xffffu);
             }
             bf16x8 mh, ml, sh, sl;
             split_frag(vm, mh, ml);
@@ -1252,11 +1316,11 @@ template <typename W, bool DUAL>
 static void launch_ggemm(const GemmArgs &g, int bm, int tiles, hipStream_t s, int ks = 1)
 {
     const dim3 grid((g.N + (DUAL ? kGN / 2 : kGN) - 1) / (DUAL ? kGN / 2 : kGN), tiles, ks), block(256);
-    if constexpr (W::kChunk == 32) {
+    if constexpr (is_block_format<W>::value) {
         if (bm == 32)
-            hipLaunchKernelGGL((k_ggemm_q2<DUAL, 32>), grid, block, 0, s, g);
+            hipLaunchKernelGGL((k_ggemm_qb<W::kBits, DUAL, 32>), grid, block, 0, s, g);
         else
-            hipLaunchKernelGGL((k_ggemm_q2<DUAL, 64>), grid, block, 0, s, g);
+            hipLaunchKernelGGL((k_ggemm_qb<W::kBits, DUAL, 64>), grid, block, 0, s, g);
     } else {
         if (bm == 32)
             hipLaunchKernelGGL((k_ggemm<W, DUAL, 32>), grid, block, 0, s, g);
@@ -1466,13 +1530,22 @@ static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const 
     const int bm = routed_bm(P, E);
     hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off, w.tile_e);
     const int et = d->expert_t, st = d->shared_t;
-    if (st == MOE_F32)
-        return et == MOE_F32 ? run_gemms<F32, F32>(d, T, w, bm, s)
-                             : (et == MOE_BF16 ? run_gemms<BF16, F32>(d, T, w, bm, s)
-                                               : run_gemms<Q2, F32>(d, T, w, bm, s));
-    return et == MOE_F32 ? run_gemms<F32, BF16>(d, T, w, bm, s)
-                         : (et == MOE_BF16 ? run_gemms<BF16, BF16>(d, T, w, bm, s)
-                                           : run_gemms<Q2, BF16>(d, T, w, bm, s));
+    if (st == MOE_F32) {
+        switch (et) {
+        case MOE_F32: return run_gemms<F32, F32>(d, T, w, bm, s);
+        case MOE_BF16: return run_gemms<BF16, F32>(d, T, w, bm, s);
+        case MOE_Q2B32: return run_gemms<Q2, F32>(d, T, w, bm, s);
+        case MOE_Q3B32: return run_gemms<Q3, F32>(d, T, w, bm, s);
+        default: return run_gemms<Q4, F32>(d, T, w, bm, s);
+        }
+    }
+    switch (et) {
+    case MOE_F32: return run_gemms<F32, BF16>(d, T, w, bm, s);
+    case MOE_BF16: return run_gemms<BF16, BF16>(d, T, w, bm, s);
+    case MOE_Q2B32: return run_gemms<Q2, BF16>(d, T, w, bm, s);
+    case MOE_Q3B32: return run_gemms<Q3, BF16>(d, T, w, bm, s);
+    default: return run_gemms<Q4, BF16>(d, T, w, bm, s);
+    }
 }
 
 int launch_prefill_forward(const moe_layer_desc *d, const float *x, int T, float *y, const int32_t *ids_in,

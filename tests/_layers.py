@@ -110,8 +110,9 @@ def oracle_layer_from_config(cfg: mi.LayerConfig, dense=None, experts=None, stac
     """Oracle layer for a seeded workload.
 
     ``experts``: restrict routed experts to this set (others absent; the oracle
-    fails loudly if it selects one). 2-bit experts are quantized here with the
-    oracle's own quantizer from the generator's fp32 source.
+    fails loudly if it selects one). Block-format experts (2, 3 or 4 bits) are
+    quantized here with the oracle's own quantizer from the generator's fp32
+    source.
     """
     import oracle
     dense = dense if dense is not None else mi.dense_weights(cfg)
@@ -119,11 +120,17 @@ def oracle_layer_from_config(cfg: mi.LayerConfig, dense=None, experts=None, stac
     G = [None] * cfg.E
     U = [None] * cfg.E
     D = [None] * cfg.E
-    if cfg.expert_t == "q2":
-        for e in todo:
-            G[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_GATE))
-            U[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_UP))
-            D[e] = oracle.q2_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_DOWN))
+    if cfg.expert_t in oracle.BITS:
+        bits = oracle.BITS[cfg.expert_t]
+
+        def quantize(e):   # experts are independent: quantized on a thread pool
+            G[e] = oracle.qb_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_GATE), bits)
+            U[e] = oracle.qb_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_UP), bits)
+            D[e] = oracle.qb_quantize(mi.expert_matrix_f32(cfg, e, mi.MAT_DOWN), bits)
+
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(mi._threads()) as ex:
+            list(ex.map(quantize, todo))
     else:
         if stacks is None:
             stacks = mi.expert_stacks(cfg, experts)
@@ -147,14 +154,14 @@ def tolerance_ok(got, ref, atol=1e-4, rtol=2e-3):
 # ------------------------------------------------------------- GPU side
 
 def gpu_layer_from_config(cfg: mi.LayerConfig, dense=None, stacks=None, renormalize=1):
-    """The same seeded layer on the GPU (library packer for 2-bit experts)."""
+    """The same seeded layer on the GPU (library packer for block-format experts)."""
     import sparse_moe_decode_amd as moe
     dense = dense if dense is not None else mi.dense_weights(cfg)
     kw = dict(H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, router_t=cfg.router_t, expert_t=cfg.expert_t,
               shared_t=cfg.shared_t, router_w=dense["router_w"], gate_vec=dense["gate_vec"],
               router_bias=dense["router_bias"], sh_gate=dense["sh_gate"], sh_up=dense["sh_up"],
               sh_down=dense["sh_down"], renormalize=renormalize)
-    if cfg.expert_t == "q2":
+    if cfg.expert_t in moe.BITS:
         return moe.Layer(**kw, expert_source=lambda e, m: mi.expert_matrix_f32(cfg, e, m))
     g, u, d = stacks if stacks is not None else mi.expert_stacks(cfg)
     return moe.Layer(**kw, exp_gate=g, exp_up=u, exp_down=d)
@@ -167,7 +174,7 @@ def gpu_layer_from_arrays(a: dict, *, router_t="f32", expert_t="f32", shared_t="
               sh_gate=a["sh_gate"], sh_up=a["sh_up"], sh_down=a["sh_down"], renormalize=renormalize,
               bias_mode=a.get("bias_mode", 0), norm_w=a.get("norm_w"), norm_eps=float(np.float32(a.get("norm_eps", 1e-6))),
               residual=a.get("residual", 0))
-    if expert_t == "q2":
+    if expert_t in moe.BITS:
         src = {0: a["exp_gate"], 1: a["exp_up"], 2: a["exp_down"]}
         return moe.Layer(**kw, expert_source=lambda e, m: np.asarray(src[m][e], np.float32))
     return moe.Layer(**kw, exp_gate=a["exp_gate"], exp_up=a["exp_up"], exp_down=a["exp_down"])

@@ -30,7 +30,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_strerror():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert moe.strerror(code) and moe.strerror(code) != "unknown status"
     assert moe.strerror(-99) == "unknown status"
@@ -60,6 +60,10 @@ def _fwd(desc, x=0x20000, T=1, y=0x30000, ws=0x40000, ws_bytes=1 << 30, ids_in=N
     (dict(top_k=17), moe.MOE_EINVAL),               # K > 16
     (dict(renormalize=2), moe.MOE_EINVAL),
     (dict(router_t=moe.MOE_Q2B32), moe.MOE_EINVAL),
+    (dict(router_t=moe.MOE_Q4B32), moe.MOE_EINVAL),
+    (dict(shared_t=moe.MOE_Q3B32), moe.MOE_EINVAL),
+    (dict(expert_t=5), moe.MOE_EINVAL),
+    (dict(expert_t=-1), moe.MOE_EINVAL),
     (dict(shared_t=7), moe.MOE_EINVAL),
     (dict(reserved=1), moe.MOE_EINVAL),
     (dict(bias_mode=2), moe.MOE_EINVAL),
@@ -78,6 +82,13 @@ def test_descriptor_validation(kw, code):
     assert _fwd(d) == code
     assert moe.lib().moe_route(C.byref(d), 0x20000, 1, 0x50000, 0x60000, 0x70000, 0x40000, 1 << 30, None) == code
     assert moe.lib().moe_workspace_bytes(C.byref(d), 1) == 0
+
+
+@pytest.mark.parametrize("et", [moe.MOE_Q2B32, moe.MOE_Q3B32, moe.MOE_Q4B32])
+def test_block_formats_accepted(et):
+    d = _fake_desc(expert_t=et)
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 1) > 0
+    assert moe.lib().moe_workspace_bytes(C.byref(d), 2048) > 0
 
 
 def test_call_validation():
@@ -154,14 +165,18 @@ def test_sort_and_unpack_validation():
     assert L.moe_q2_unpack(0x1000, 4, 48, 0x2000, None) == moe.MOE_EINVAL
     assert L.moe_q2_unpack(0x1008, 4, 64, 0x2000, None) == moe.MOE_EALIGN
     assert L.moe_q2_unpack(None, 4, 64, 0x2000, None) == moe.MOE_EINVAL
+    for bits in (1, 5, 0, -2):
+        assert L.moe_qb_unpack(bits, 0x1000, 4, 64, 0x2000, None) == moe.MOE_EINVAL
+    assert L.moe_qb_unpack(3, 0x1000, 4, 48, 0x2000, None) == moe.MOE_EINVAL
+    assert L.moe_qb_unpack(4, 0x1000, 4, 64, 0x2008, None) == moe.MOE_EALIGN
 
 
 # ---------------------------------------------------------------- packer
 
-def _decode_physical(packed, rows, cols):
+def _decode_physical(packed, rows, cols, bits=2):
     """Split a packed matrix by the layout documented in include/moe.h."""
-    nc = rows * cols // 4
-    codes = packed[:nc].reshape(rows, cols // 4)
+    nc = rows * cols * bits // 8
+    codes = packed[:nc].reshape(rows, cols * bits // 8)
     sm = packed[nc:nc + rows * cols // 8].view(np.uint16).reshape(rows, cols // 32, 2)
     return codes, sm[..., 0], sm[..., 1]
 
@@ -173,6 +188,15 @@ def test_packed_bytes_formula():
     assert moe.q2_packed_bytes(3, 64) == 256
     assert moe.q2_packed_bytes(1, 48) == 0
     assert moe.q2_packed_bytes(0, 64) == 0
+    # (b + 1) / 8 bytes per weight, rounded up to 256
+    assert moe.qb_packed_bytes(3, 512, 2048) == 524288
+    assert moe.qb_packed_bytes(4, 2048, 512) == 655360
+    assert moe.qb_packed_bytes(3, 1, 32) == 256
+    assert moe.qb_packed_bytes(4, 7, 64) == 512
+    assert moe.qb_packed_bytes(2, 3, 64) == moe.q2_packed_bytes(3, 64)
+    for bits in (0, 1, 5, 8):
+        assert moe.qb_packed_bytes(bits, 4, 64) == 0
+    assert moe.qb_packed_bytes(4, 1, 48) == 0
 
 
 def _adversarial_blocks(rng):
@@ -194,8 +218,9 @@ def _adversarial_blocks(rng):
     return np.stack(blocks)
 
 
-def test_packer_equals_oracle_quantizer():
-    rng = np.random.default_rng(21)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_packer_equals_oracle_quantizer(bits):
+    rng = np.random.default_rng(21 + bits)
     mats = [
         (rng.standard_normal((64, 512)) * 0.02).astype(np.float32),
         (rng.standard_normal((16, 2048)) * 0.02).astype(np.float32),
@@ -205,15 +230,18 @@ def test_packer_equals_oracle_quantizer():
     ]
     for w in mats:
         rows, cols = w.shape
-        packed = moe.q2_pack(w)
-        assert packed.nbytes == moe.q2_packed_bytes(rows, cols)
-        codes, scale, minv = _decode_physical(packed, rows, cols)
-        q = oracle.q2_quantize(w)
+        packed = moe.qb_pack(bits, w)
+        assert packed.nbytes == moe.qb_packed_bytes(bits, rows, cols)
+        codes, scale, minv = _decode_physical(packed, rows, cols, bits)
+        q = oracle.qb_quantize(w, bits)
         np.testing.assert_array_equal(codes, q.codes)
         np.testing.assert_array_equal(scale, q.scale)
         np.testing.assert_array_equal(minv, q.minv)
-        used = rows * cols * 3 // 8
+        used = rows * cols * (bits + 1) // 8
         assert np.all(packed[used:] == 0)
+    if bits == 2:
+        w = mats[0]
+        np.testing.assert_array_equal(moe.q2_pack(w), moe.qb_pack(2, w))
 
 
 def test_packer_rejects_bad_input():
@@ -231,6 +259,13 @@ def test_packer_rejects_bad_input():
     dst = np.zeros(16, np.uint8)
     assert L.moe_q2_pack(src.ctypes.data, 2, 64, dst.ctypes.data, 16) == moe.MOE_EWORKSPACE
     assert L.moe_q2_pack(src.ctypes.data, 2, 48, dst.ctypes.data, 1 << 20) == moe.MOE_EINVAL
+    big = np.zeros(1 << 12, np.uint8)
+    for bits in (1, 5):
+        assert L.moe_qb_pack(bits, src.ctypes.data, 2, 64, big.ctypes.data, big.nbytes) == moe.MOE_EINVAL
+    assert L.moe_qb_pack(4, src.ctypes.data, 2, 64, dst.ctypes.data, 16) == moe.MOE_EWORKSPACE
+    assert L.moe_qb_pack(3, None, 2, 64, big.ctypes.data, big.nbytes) == moe.MOE_EINVAL
+    with pytest.raises(ValueError):
+        moe.qb_pack(3, np.zeros(64, np.float32))
 
 
 def _bf16_rne(v: np.ndarray) -> np.ndarray:

@@ -184,6 +184,33 @@ def test_bf16_and_q2_small_shapes():
     assert_parity(run_calls(Gq, x, 11, force_path="prefill"), ref, "q2 prefill")
 
 
+@pytest.mark.parametrize("fmt", ["q3", "q4"])
+def test_block_formats_small_shapes(fmt):
+    """3- and 4-bit experts on a small layer (H 320: ten blocks per row, a
+    ragged last set of lanes): decode, few-row calls of 2, 3, 5 and 11 rows
+    and the prefill path, with fp32 and bf16 shared experts."""
+    import oracle
+    bits = oracle.BITS[fmt]
+    rng = np.random.default_rng(300 + bits)
+    a = _random_arrays(rng, 320, 24, 5, 96, 64, rstd=0.05, estd=0.05)
+    x = rng.standard_normal((11, 320)).astype(np.float32)
+    for dense_t in ("f32", "bf16"):
+        _say(f"case: small {fmt} experts, {dense_t} router and shared expert")
+        b = dict(a)
+        if dense_t == "bf16":
+            for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down"):
+                b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
+        q = dict(b)
+        for k in ("exp_gate", "exp_up", "exp_down"):
+            q[k] = [oracle.qb_quantize(m, bits) for m in a[k]]
+        L = oracle_layer_from_arrays(q, router_t=dense_t, expert_t=fmt, shared_t=dense_t)
+        G = gpu_layer_from_arrays(b, router_t=dense_t, expert_t=fmt, shared_t=dense_t)
+        ref = _oracle_ref(L, x)
+        for rows in (1, 2, 3, 5, 11):
+            assert_parity(run_calls(G, x, rows), ref, f"{fmt} {dense_t} rows={rows}")
+        assert_parity(run_calls(G, x, 11, force_path="prefill"), ref, f"{fmt} {dense_t} prefill")
+
+
 def test_path_boundaries():
     """Calls at the edges of the library's path choice on a 2-bit layer:
     5, 8 and 12 rows run as few-row launches of three (remainders of two,
@@ -210,7 +237,7 @@ def test_path_boundaries():
     assert_parity(run_calls(G, x, 13, force_path="fewrow"), ref, "boundary rows=13 few-row")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "q2"])
+@pytest.mark.parametrize("fmt", ["bf16", "q2", "q3", "q4"])
 def test_wide_rows_and_large_pair_sets(fmt):
     """Rows wider than one chunk set per wave (H = 2112: the streamed gate/up
     path) and, at four rows with K = 16, more (slot, row) pairs than the down
@@ -231,10 +258,10 @@ def test_wide_rows_and_large_pair_sets(fmt):
         ef = {k: [mi.bf16_bits_to_f32(m) for m in b[k]] for k in ("exp_gate", "exp_up", "exp_down")}
         q = dict(b)
         for k in ef:
-            q[k] = [oracle.q2_quantize(m) for m in ef[k]]
-        L = oracle_layer_from_arrays(q, router_t="bf16", expert_t="q2", shared_t="bf16")
+            q[k] = [oracle.qb_quantize(m, oracle.BITS[fmt]) for m in ef[k]]
+        L = oracle_layer_from_arrays(q, router_t="bf16", expert_t=fmt, shared_t="bf16")
         G = gpu_layer_from_arrays(dict(b, **{k: np.stack(v) for k, v in ef.items()}),
-                                  router_t="bf16", expert_t="q2", shared_t="bf16")
+                                  router_t="bf16", expert_t=fmt, shared_t="bf16")
     ref = _oracle_ref(L, x)
     for rows in (1, 4, 8):
         assert_parity(run_calls(G, x, rows), ref, f"wide {fmt} rows={rows}")
@@ -308,7 +335,7 @@ def test_hand_fixtures_bias_norm_residual(name):
         assert tolerance_ok(y[0], exp["y"]).all(), (path, y[0][:8], exp["y"][:8])
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2", "q4"])
 def test_norm_and_residual_layers(fmt):
     """Layers with the pre-MoE RMS norm (random gamma) and the residual, with
     a selection-only bias, on decode, few-row (3 and 12 rows) and prefill
@@ -326,13 +353,13 @@ def test_norm_and_residual_layers(fmt):
     if fmt != "f32":
         for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
             b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
-    if fmt == "q2":
+    if fmt in oracle.BITS:
         src = {k: mi.bf16_bits_to_f32(b[k]).reshape(a[k].shape) for k in ("exp_gate", "exp_up", "exp_down")}
         qo = dict(b)
         for k in src:
-            qo[k] = [oracle.q2_quantize(m) for m in src[k]]
-        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t="q2", shared_t=st)
-        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t="q2", shared_t=st)
+            qo[k] = [oracle.qb_quantize(m, oracle.BITS[fmt]) for m in src[k]]
+        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t=fmt, shared_t=st)
+        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t=fmt, shared_t=st)
     else:
         L = oracle_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
         G = gpu_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
@@ -485,7 +512,7 @@ def test_prefill_in_chunks():
 
 # ------------------------------------------------------------- prefill
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "q2", "q3", "q4"])
 @pytest.mark.parametrize("T", [5, 37, 300])
 def test_prefill_small(fmt, T):
     """Grouped-GEMM path at small sizes: ragged expert groups (not multiples
@@ -502,13 +529,13 @@ def test_prefill_small(fmt, T):
     if fmt != "f32":
         for k in ("router_w", "gate_vec", "sh_gate", "sh_up", "sh_down", "exp_gate", "exp_up", "exp_down"):
             b[k] = mi.f32_to_bf16_bits(a[k]).reshape(a[k].shape)
-    if fmt == "q2":
+    if fmt in oracle.BITS:
         src = {k: mi.bf16_bits_to_f32(b[k]).reshape(a[k].shape) for k in ("exp_gate", "exp_up", "exp_down")}
         qo = dict(b)
         for k in src:
-            qo[k] = [oracle.q2_quantize(m) for m in src[k]]
-        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t="q2", shared_t=st)
-        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t="q2", shared_t=st)
+            qo[k] = [oracle.qb_quantize(m, oracle.BITS[fmt]) for m in src[k]]
+        L = oracle_layer_from_arrays(qo, router_t=rt, expert_t=fmt, shared_t=st)
+        G = gpu_layer_from_arrays(dict(b, **src), router_t=rt, expert_t=fmt, shared_t=st)
     else:
         L = oracle_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
         G = gpu_layer_from_arrays(b, router_t=rt, expert_t=fmt, shared_t=st)
@@ -568,42 +595,46 @@ def test_prefill_given_routing():
 
 # ------------------------------------------------------------ 2-bit format
 
-def test_q2_unpack_bit_exact_random_bytes():
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+def test_qb_unpack_bit_exact_random_bytes(nbits):
     """Random codes and random finite fp16 scale/min patterns (subnormals
     included): the device unpack equals the oracle's dequantizer bit for bit."""
-    _say("case: q2 unpack random bytes")
+    _say(f"case: {nbits}-bit unpack random bytes")
     import oracle
     import sparse_moe_decode_amd as moe
-    rng = np.random.default_rng(61)
+    rng = np.random.default_rng(61 + nbits)
     rows, cols = 96, 1024
     nb = cols // 32
-    codes = rng.integers(0, 256, (rows, cols // 4), dtype=np.uint8)
+    ncode = rows * cols * nbits // 8
+    codes = rng.integers(0, 256, (rows, cols * nbits // 8), dtype=np.uint8)
     bits = rng.integers(0, 0x7c00, (rows, nb, 2), dtype=np.uint16)     # finite magnitudes
     bits |= (rng.integers(0, 2, (rows, nb, 2), dtype=np.uint16) << 15)
-    packed = np.zeros(moe.q2_packed_bytes(rows, cols), np.uint8)
-    packed[: rows * cols // 4] = codes.reshape(-1)
-    packed[rows * cols // 4: rows * cols * 3 // 8] = bits.reshape(-1).view(np.uint8)
-    ref = oracle.q2_dequantize(oracle.Q2(codes, bits[..., 0].copy(), bits[..., 1].copy(), rows, cols))
+    packed = np.zeros(moe.qb_packed_bytes(nbits, rows, cols), np.uint8)
+    packed[:ncode] = codes.reshape(-1)
+    packed[ncode: ncode + rows * cols // 8] = bits.reshape(-1).view(np.uint8)
+    ref = oracle.qb_dequantize(oracle.Q2(codes, bits[..., 0].copy(), bits[..., 1].copy(), rows, cols, nbits))
     dev = torch.from_numpy(packed).cuda()
     out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
-    moe.q2_unpack(dev, rows, cols, out)
+    moe.qb_unpack(nbits, dev, rows, cols, out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-def test_q2_unpack_of_packed_expert_weights():
-    _say("case: q2 unpack of packed expert matrices")
+@pytest.mark.parametrize("fmt", ["q2", "q3", "q4"])
+def test_qb_unpack_of_packed_expert_weights(fmt):
+    _say(f"case: {fmt} unpack of packed expert matrices")
     import oracle
     import sparse_moe_decode_amd as moe
-    cfg = mi.CONFIGS[2]
+    nbits = oracle.BITS[fmt]
+    cfg = mi.CONFIGS[2].with_(expert_t=fmt)
     for e, m in [(0, mi.MAT_GATE), (7, mi.MAT_DOWN)]:
         w = mi.expert_matrix_f32(cfg, e, m)
         rows, cols = w.shape
-        dev = torch.from_numpy(moe.q2_pack(w)).cuda()
+        dev = torch.from_numpy(moe.qb_pack(nbits, w)).cuda()
         out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
-        moe.q2_unpack(dev, rows, cols, out)
+        moe.qb_unpack(nbits, dev, rows, cols, out)
         torch.cuda.synchronize()
-        ref = oracle.q2_dequantize(oracle.q2_quantize(w))
+        ref = oracle.qb_dequantize(oracle.qb_quantize(w, nbits))
         np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
@@ -727,6 +758,35 @@ def test_prefill_q2_full():
     ref = _oracle_rows(cfg, dense, x, got[0], rows)
     err = assert_parity(got, ref, cfg.name, rows)
     _say(f"{cfg.name}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
+
+
+@pytest.mark.parametrize("fmt", ["q3", "q4"])
+def test_block_formats_full(fmt):
+    """The full-shape decode layer with 3- and 4-bit experts quantized from
+    the same fp32 source as the 2-bit workload: 200 tokens one per call,
+    120 tokens as 3-row calls and a 256-row prefill call; every routing
+    decision and every fourth row's output against the oracle."""
+    cfg = mi.CONFIGS[2].with_(expert_t=fmt, name=f"decode_{fmt}")
+    _say(f"case: {cfg.name} full shape")
+    dense = mi.dense_weights(cfg)
+    G = gpu_layer_from_config(cfg, dense)
+    Lr = oracle_layer_from_config(cfg, dense=dense, experts=[])
+    runs = []
+    for what, T, rows, inst in (("decode", 200, 1, 0), ("few-row", 120, 3, 3), ("prefill", 256, 256, 7)):
+        x = mi.activations(cfg, T=T, instance=inst)
+        got = run_calls(G, x, rows)
+        ri, _, _, _ = Lr.route(x)
+        np.testing.assert_array_equal(got[0], ri)
+        runs.append((what, x, got, np.arange(0, T, 4)))
+    # one oracle layer holding every expert the sampled rows use
+    need = set()
+    for _, _, got, sample in runs:
+        need |= set(np.unique(got[0][sample]).tolist())
+    L = oracle_layer_from_config(cfg, dense=dense, experts=need)
+    for what, x, got, sample in runs:
+        ref = _oracle_ref(L, x[sample])
+        err = assert_parity(got, ref, f"{cfg.name} {what}", sample)
+        _say(f"{cfg.name} {what}: max abs err {err[0]:.3g}, max err/tolerance {err[1]:.3g}")
 
 
 def test_determinism(decode_q2):
