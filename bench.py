@@ -45,7 +45,8 @@ def wbytes(fmt: str, rows: int, cols: int) -> int:
         return rows * cols * 4
     if fmt == "bf16":
         return rows * cols * 2
-    return rows * cols * 3 // 8        # 2-bit blocks: 12 bytes per 32 weights
+    bits = {"q2": 2, "q3": 3, "q4": 4}[fmt]   # b-bit blocks: 4b bytes of codes + 4 of scale/min per 32 weights
+    return rows * cols * (bits + 1) // 8
 
 
 def expert_bytes(cfg) -> int:
@@ -77,12 +78,12 @@ class Workload:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         from _layers import gpu_layer_from_config
         self.dense0 = mi.dense_weights(cfg)
-        self.stacks = mi.expert_stacks(cfg) if cfg.expert_t != "q2" else None
+        self.stacks = mi.expert_stacks(cfg) if cfg.expert_t not in mi.BLOCK_FORMATS else None
         base = gpu_layer_from_config(cfg, self.dense0, self.stacks)
         self.layers = [base]
-        # 2-bit stacks (604 MB) would partly stay in the 256 MB last-level
-        # cache across calls: each instance gets its own copy
-        self.distinct_experts = cfg.expert_t == "q2" and rotate > 1
+        # block-format stacks (604 MB at 2 bits) would partly stay in the
+        # 256 MB last-level cache across calls: each instance gets its own copy
+        self.distinct_experts = cfg.expert_t in mi.BLOCK_FORMATS and rotate > 1
         for i in range(1, rotate):
             d = mi.dense_weights(mi.layer_instance(cfg, i))
             L = base.with_dense(**d)
@@ -254,9 +255,11 @@ def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0, per_step=Non
     return wl, ms, wall
 
 
-EXTRA_WORKLOADS = [("decode_q2", 2, 1, 1000), ("fewrow_q2_R2", 3, 2, 500), ("fewrow_q2_R3", 3, 3, 333),
-                   ("fewrow_q2_R8", 3, 8, 125),
-                   ("prefill_q2", 4, 2048, 1)]
+# (key, workload index, rows per call, calls, expert format if not the workload's)
+EXTRA_WORKLOADS = [("decode_q2", 2, 1, 1000, None), ("fewrow_q2_R2", 3, 2, 500, None),
+                   ("fewrow_q2_R3", 3, 3, 333, None), ("fewrow_q2_R8", 3, 8, 125, None),
+                   ("prefill_q2", 4, 2048, 1, None),
+                   ("decode_q3", 2, 1, 1000, "q3"), ("decode_q4", 2, 1, 1000, "q4")]
 
 
 def run_extra(args, keys):
@@ -264,10 +267,12 @@ def run_extra(args, keys):
     import torch
     cfg = mi.CONFIGS[1]
     extra = {}
-    for key, idx, rows, ncalls in EXTRA_WORKLOADS:
+    for key, idx, rows, ncalls, fmt in EXTRA_WORKLOADS:
         if keys is not None and key not in keys:
             continue
         c = mi.CONFIGS[idx].with_(rows_per_call=rows)
+        if fmt is not None:
+            c = c.with_(expert_t=fmt, name=key)
         print(f"[bench] {key}", file=sys.stderr, flush=True)
         # one prefill call is about a millisecond: time more of them, after a
         # longer warm-up, so that clock ramp-up does not show in the figure
@@ -409,8 +414,7 @@ def main():
     ap.add_argument("--cpu-single-seconds", type=float, default=8.0, help="oracle on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit, few-row and prefill lines")
-    ap.add_argument("--only", choices=["decode_q2", "fewrow_q2_R2", "fewrow_q2_R3", "fewrow_q2_R8", "prefill_q2",
-                                       "stack_q2_48"],
+    ap.add_argument("--only", choices=[k for k, *_ in EXTRA_WORKLOADS] + ["stack_q2_48"],
                     help="run just this one of the other workloads (for profiling); prints its record")
     ap.add_argument("--rows-sweep", action="store_true",
                     help="rows per call from 1 to 2048 on the 2-bit layer (decode, few-row, prefill paths); "

@@ -20,7 +20,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.cpp", "decode.hip", "block_unpack.hip", "sort.hip", "prefill.hip", "noalloc.hip"]
+HIP_SOURCES = ["api.cpp", "sizing.cpp", "decode.hip", "block_unpack.hip", "sort.hip", "prefill.hip", "noalloc.hip"]
 HOST_SOURCES = ["pack_blocks.cpp"]
 
 HIP_FLAGS = [

@@ -1356,11 +1356,6 @@ static_assert(sizeof(RouteLds) <= kDecodeStaticLds, "routing state exceeds its L
 static_assert(offsetof(SlotTable, expert) % 16 == 0 && sizeof(SlotTable) % 16 == 0,
               "the down pass reads expert ids 16 bytes at a time");
 
-size_t gateup_lds_bytes(int R, int H, int E)
-{
-    const size_t a = sizeof(float) * (R * H + R * (H >> 5)), b = sizeof(double) * R * ((E + 1) & ~1);
-    return a > b ? a : b;
-}
 
 struct RoutingIO {
     const int32_t *ids_in;
@@ -1560,10 +1555,6 @@ static int launch_experts_t(const moe_layer_desc *d, const float *x, int R, floa
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-int decode_ws_size(const moe_layer_desc *d, int R)
-{
-    return static_cast<int>(decode_ws_bytes(R, d->n_experts, d->top_k, imax_of(d)));
-}
 
 int launch_decode_forward(const moe_layer_desc *d, const float *x, int R, float *y, const int32_t *ids_in,
                           const float *wts_in, const float *gate_in, int32_t *ids_out, float *wts_out,

@@ -14,17 +14,11 @@
 
 #include "device_common.hpp"
 #include "internal.h"
+#include "workspace.hpp"
 
 namespace moe {
 
-constexpr int kSortChunk = 1024;                  // pairs per workgroup
-constexpr int kSortWaves = kSortChunk / kWave;    // one pair per thread
-
-size_t sort_ws_bytes_tke(int64_t n, int E)
-{
-    const int64_t chunks = (n + kSortChunk - 1) / kSortChunk;
-    return align256(sizeof(Control)) + align256(sizeof(int) * static_cast<size_t>(chunks) * E);
-}
+constexpr int kSortWaves = kSortChunk / kWave;    // one pair per thread (kSortChunk: workspace.hpp)
 
 __global__ void __launch_bounds__(kSortChunk) k_sort_hist(const int32_t *ids, int n, int E, int *table)
 {
