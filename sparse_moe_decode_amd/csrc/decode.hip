@@ -4,7 +4,7 @@
 // only synchronization between workgroups (no fences, counters or spin waits):
 //   k_logits   router logits in fp64 (products of bf16/fp32 weights with fp32
 //              activations are exact in double) plus the shared-gate logit,
-//              one row per wave.
+//              one row per workgroup (a quarter of it per wave).
 //   k_gateup   the shared expert's gate/up channels, and - in every other
 //              workgroup - the exact top-K per row, softmax weights, sigmoid
 //              gate and slot table (the union of the rows' experts; slot 0 is
@@ -904,61 +904,155 @@ struct LogitArgs {
     double *zlogit;          // [R]
 };
 
-constexpr int kLgPrefetch = 4;   // 16-byte chunks per lane loaded before x is staged
+constexpr int kLgThreads = 256;   // one router row per workgroup, four waves (the four quarters)
+constexpr int kLgPrefetch = 4;    // 16-byte chunks per thread requested first
 
-// Router logits of a call, one row per wave; row E is the shared-gate vector.
-template <int R, typename RT>
-__global__ void __launch_bounds__(256) k_logits(LogitArgs a)
+// x values (R rows) of the elements of one 16-byte router chunk c, read from
+// global memory (cached: every workgroup reads the same x); with a norm, the
+// normalized u = fp32((x r) gamma) of rms_norm_rows.
+template <int R, int EPC>
+__device__ __forceinline__ void chunk_x(const float *x, int H, int c, const float *gamma, const double (&r)[R],
+                                        float (&xv)[R][EPC])
 {
-    extern __shared__ float xs[];   // [R][H]
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int e = blockIdx.x * (blockDim.x / kWave) + tid / kWave;
-    const bool live = e <= a.E;
-    const size_t rb = static_cast<size_t>(a.H) * (RT::kChunk == 4 ? 4 : 2);
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int i = 0; i < EPC; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + static_cast<size_t>(q) * H + c * EPC + i);
+            xv[q][i] = v.x;
+            xv[q][i + 1] = v.y;
+            xv[q][i + 2] = v.z;
+            xv[q][i + 3] = v.w;
+        }
+    if (gamma) {
+#pragma unroll
+        for (int i = 0; i < EPC; i += 4) {
+            const float4 g = *reinterpret_cast<const float4 *>(gamma + c * EPC + i);
+            const float gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    xv[q][i + k] = static_cast<float>(static_cast<double>(xv[q][i + k]) * r[q] * static_cast<double>(gv[k]));
+        }
+    }
+}
+
+// One chunk's products (weights in element order) added to acc[q].
+template <int R>
+__device__ __forceinline__ void chunk_fma(F32, const uint4 &u, const float (&xv)[R][4], double (&acc)[R])
+{
+    const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[q] = fma(static_cast<double>(w[i]), static_cast<double>(xv[q][i]), acc[q]);
+}
+template <int R>
+__device__ __forceinline__ void chunk_fma(BF16, const uint4 &u, const float (&xv)[R][8], double (&acc)[R])
+{
+    const float w[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                        bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[q] = fma(static_cast<double>(w[i]), static_cast<double>(xv[q][i]), acc[q]);
+}
+
+// Router logits of a call: one router row per workgroup (row E is the
+// shared-gate vector), in the quartered order of router_chunk (wave w takes
+// quarter w: chunks c with (c >> 6) & 3 == w). Each thread reads its own
+// weight chunks and the x values they multiply straight from memory, so the
+// row's one HBM round trip is not preceded by staging x in LDS; with a norm,
+// the rows' sums of squares are formed first exactly as in rms_norm_rows
+// (float4 i = tid, tid + 256, ..., then wave_sum, then the waves in order),
+// so r matches the other kernels' bit for bit.
+template <int R, typename RT>
+__global__ void __launch_bounds__(kLgThreads) k_logits(LogitArgs a)
+{
+    constexpr int EPC = RT::kChunk;   // elements per 16-byte chunk
+    __shared__ double part[R][kLgThreads / kWave];
+    __shared__ double rr[R];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int e = blockIdx.x;
+    const size_t rb = static_cast<size_t>(a.H) * (EPC == 4 ? 4 : 2);
     const uint8_t *row = e < a.E ? a.router_w + e * rb : a.gate_w;
     const int nch = static_cast<int>(rb / 16);
-    // the weight row does not depend on x: start its loads first
+    // thread tid takes chunks c = tid + 256 k: quarter (c >> 6) & 3 = wave
     uint4 w[kLgPrefetch];
 #pragma unroll
     for (int u = 0; u < kLgPrefetch; ++u) {
-        const int c = lane + u * kWave;
-        if (live && c < nch)
+        const int c = tid + u * kLgThreads;
+        if (c < nch)
             w[u] = ld_nt16(row + c * 16);
     }
-    for (int i = tid; i < R * a.H / 4; i += blockDim.x)
-        reinterpret_cast<float4 *>(xs)[i] = reinterpret_cast<const float4 *>(a.x)[i];
-    if (a.norm_w)
-        rms_norm_rows<R>(xs, a.H, a.norm_w, a.norm_eps, SlotsInOrder{});
-    else
+    double r[R];
+    if (a.norm_w) {
+        const int n4 = a.H >> 2;
+        const float4 *x4 = reinterpret_cast<const float4 *>(a.x);
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            double ss = 0.0;
+            for (int i = tid; i < n4; i += kLgThreads) {
+                const float4 v = x4[q * n4 + i];
+                ss += static_cast<double>(v.x) * v.x + static_cast<double>(v.y) * v.y +
+                      static_cast<double>(v.z) * v.z + static_cast<double>(v.w) * v.w;
+            }
+            ss = wave_sum(ss);
+            if (lane == 0)
+                part[q][wave] = ss;
+        }
         __syncthreads();
-    if (!live)
-        return;
+        if (tid < R) {
+            double t = 0.0;
+            for (int v = 0; v < kLgThreads / kWave; ++v)
+                t += part[tid][v];
+            rr[tid] = 1.0 / sqrt(t / a.H + static_cast<double>(a.norm_eps));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            r[q] = rr[q];
+    } else {
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            r[q] = 1.0;
+    }
     double acc[R];
 #pragma unroll
     for (int q = 0; q < R; ++q)
         acc[q] = 0.0;
 #pragma unroll
     for (int u = 0; u < kLgPrefetch; ++u) {
-        const int c = lane + u * kWave;
-        if (c < nch)
-            router_chunk<R>(RT{}, w[u], c, xs, a.H, acc);
-    }
-    for (int c = lane + kLgPrefetch * kWave; c < nch; c += kWave) {
-        const uint4 u = ld_nt16(row + c * 16);
-        router_chunk<R>(RT{}, u, c, xs, a.H, acc);
-    }
-#pragma unroll
-    for (int q = 0; q < R; ++q)
-        acc[q] = wave_sum(acc[q]);
-    if (lane == 0) {
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            if (e < a.E)
-                a.logits[q * a.E + e] = acc[q] + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
-            else
-                a.zlogit[q] = acc[q];
+        const int c = tid + u * kLgThreads;
+        if (c < nch) {
+            float xv[R][EPC];
+            chunk_x<R, EPC>(a.x, a.H, c, a.norm_w, r, xv);
+            chunk_fma<R>(RT{}, w[u], xv, acc);
         }
+    }
+    for (int c = tid + kLgPrefetch * kLgThreads; c < nch; c += kLgThreads) {
+        const uint4 u = ld_nt16(row + c * 16);
+        float xv[R][EPC];
+        chunk_x<R, EPC>(a.x, a.H, c, a.norm_w, r, xv);
+        chunk_fma<R>(RT{}, u, xv, acc);
+    }
+    __syncthreads();   // part[] is reused
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const double p = wave_sum(acc[q]);
+        if (lane == 0)
+            part[q][wave] = p;
+    }
+    __syncthreads();
+    if (tid < R) {
+        const double v = combine_quarters(part[tid][0], part[tid][1], part[tid][2], part[tid][3]);
+        if (e < a.E)
+            a.logits[tid * a.E + e] = v + (a.bias ? static_cast<double>(a.bias[e]) : 0.0);
+        else
+            a.zlogit[tid] = v;
     }
 }
 
@@ -1435,13 +1529,12 @@ static int launch_logits_t(const moe_layer_desc *d, const float *x, int R, const
     a.gate_w = static_cast<const uint8_t *>(d->shared_gate_w);
     a.logits = w.logits;
     a.zlogit = w.zlogit;
-    const dim3 grid((a.E + 1 + 3) / 4), block(256);
-    const size_t lds = sizeof(float) * R * a.H;
+    const dim3 grid(a.E + 1), block(kLgThreads);
     switch (R) {
-    case 1: hipLaunchKernelGGL((k_logits<1, RT>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_logits<2, RT>), grid, block, lds, s, a); break;
-    case 3: hipLaunchKernelGGL((k_logits<3, RT>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((k_logits<4, RT>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_logits<1, RT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_logits<2, RT>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_logits<3, RT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_logits<4, RT>), grid, block, 0, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

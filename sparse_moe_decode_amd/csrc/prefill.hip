@@ -144,11 +144,12 @@ __device__ void router_norm(const uint8_t *router_w, int E, int H, float *wn, in
 }
 
 // Exact fp64 dot product of a router row (or the gate vector) with the x row
-// in LDS, by the whole wave (the decode path's order).
+// in LDS, by the whole wave, in the quartered order of the decode path
+// (router_chunk per quarter, wave_sum, combine_quarters).
 template <typename RT>
 __device__ __forceinline__ double exact_dot(const uint8_t *row, int nch, const float *xs, int H, int lane)
 {
-    double acc[1] = {0.0};
+    double acc[4][1] = {{0.0}, {0.0}, {0.0}, {0.0}};
     for (int c0 = lane; c0 < nch; c0 += 4 * kWave) {
         uint4 u4[4];
 #pragma unroll
@@ -158,12 +159,12 @@ __device__ __forceinline__ double exact_dot(const uint8_t *row, int nch, const f
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int c = c0 + u * kWave;
+            const int c = c0 + u * kWave;   // quarter u
             if (c < nch)
-                router_chunk<1>(RT{}, u4[u], c, xs, H, acc);
+                router_chunk<1>(RT{}, u4[u], c, xs, H, acc[u]);
         }
     }
-    return wave_sum(acc[0]);
+    return combine_quarters(wave_sum(acc[0][0]), wave_sum(acc[1][0]), wave_sum(acc[2][0]), wave_sum(acc[3][0]));
 }
 
 // Exact logits of experts cand[j] (cand null: expert j), j = j0, j0 + step,
@@ -177,8 +178,8 @@ __device__ __forceinline__ void exact_logits(const int *cand, int j0, int step, 
     for (int j = j0; j < n; j += 2 * step) {
         const int ja = j, jb = j + step < n ? j + step : j;
         const int ea = cand ? cand[ja] : ja, eb = cand ? cand[jb] : jb;
-        double a0[1] = {0.0}, a1[1] = {0.0};
-        // four chunks per lane of both rows requested at once
+        double a0[4][1] = {{0.0}, {0.0}, {0.0}, {0.0}}, a1[4][1] = {{0.0}, {0.0}, {0.0}, {0.0}};
+        // four chunks per lane of both rows (one per quarter) requested at once
         for (int c0 = lane; c0 < nch; c0 += 4 * kWave) {
             uint4 ua[4], ub[4];
 #pragma unroll
@@ -192,13 +193,15 @@ __device__ __forceinline__ void exact_logits(const int *cand, int j0, int step, 
             for (int u = 0; u < 4; ++u) {
                 const int c = c0 + u * kWave;
                 if (c < nch) {
-                    router_chunk<1>(RT{}, ua[u], c, xs, H, a0);
-                    router_chunk<1>(RT{}, ub[u], c, xs, H, a1);
+                    router_chunk<1>(RT{}, ua[u], c, xs, H, a0[u]);
+                    router_chunk<1>(RT{}, ub[u], c, xs, H, a1[u]);
                 }
             }
         }
-        const double va = wave_sum(a0[0]) + (bias ? static_cast<double>(bias[ea]) : 0.0);
-        const double vb = wave_sum(a1[0]) + (bias ? static_cast<double>(bias[eb]) : 0.0);
+        const double va = combine_quarters(wave_sum(a0[0][0]), wave_sum(a0[1][0]), wave_sum(a0[2][0]),
+                                           wave_sum(a0[3][0])) + (bias ? static_cast<double>(bias[ea]) : 0.0);
+        const double vb = combine_quarters(wave_sum(a1[0][0]), wave_sum(a1[1][0]), wave_sum(a1[2][0]),
+                                           wave_sum(a1[3][0])) + (bias ? static_cast<double>(bias[eb]) : 0.0);
         if (lane == 0) {
             out[ja] = va;
             out[jb] = vb;

@@ -31,9 +31,14 @@ struct RouteLds {
 // Router dot products in fp64 (exact products of an fp32 activation and a
 // bf16/fp32 weight): one 16-byte chunk c of a router row (4 fp32 or 8 bf16
 // weights) against x (fp32, R rows of H in `xs`), accumulated in element order.
-// Every path that needs an exact logit sums chunks c = lane, lane + 64, ...
-// in this order per lane, then wave_sum, then adds the bias, so all paths
-// produce the same bits.
+//
+// The order of an exact logit, the same on every path so that all paths
+// produce the same bits: chunk c of a row belongs to quarter (c >> 6) & 3
+// and lane c & 63; each lane sums its chunks of a quarter in increasing c
+// (router_chunk), each quarter is summed over the wave (wave_sum), and the
+// logit is (P0 + P1) + (P2 + P3), then + bias. Four waves compute the four
+// quarters side by side (the decode logits kernel); one wave computes them
+// with four accumulators (the prefill selection).
 template <int R>
 __device__ __forceinline__ void router_chunk(F32, const uint4 &u, int c, const float *xs, int H, double (&acc)[R])
 {
@@ -62,6 +67,11 @@ __device__ __forceinline__ void router_chunk(BF16, const uint4 &u, int c, const 
         for (int i = 0; i < 8; ++i)
             acc[q] = fma(static_cast<double>(wf[i]), static_cast<double>(xv[i]), acc[q]);
     }
+}
+
+__device__ __forceinline__ double combine_quarters(double p0, double p1, double p2, double p3)
+{
+    return (p0 + p1) + (p2 + p3);
 }
 
 // v[l] + v[l ^ 32] on every lane, with one VALU swap of the wave's halves
