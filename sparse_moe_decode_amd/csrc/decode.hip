@@ -601,10 +601,28 @@ __device__ __forceinline__ void dot_block_b(const uint32_t (&gc)[B], uint32_t gs
 #pragma unroll
     for (int cl = 0; cl < 8; ++cl) {
         float g[4], u[4];
+        if constexpr (B == 4) {
+            // dword cl / 2 holds chunks cl & ~1 and cl | 1; masking nibble k of
+            // every byte gives codes (k, k + 2) of both chunks, one per byte,
+            // converted with one byte conversion each (done for the even chunk)
+            const int t = cl >> 1, hb = 2 * (cl & 1);
+            uint32_t g0 = gc[t] & 0x0f0f0f0fu, g1 = (gc[t] >> 4) & 0x0f0f0f0fu;
+            uint32_t u0 = uc[t] & 0x0f0f0f0fu, u1 = (uc[t] >> 4) & 0x0f0f0f0fu;
+            asm("" : "+v"(g0), "+v"(g1), "+v"(u0), "+v"(u1));
+            g[0] = static_cast<float>((g0 >> (8 * hb)) & 0xffu);
+            g[1] = static_cast<float>((g1 >> (8 * hb)) & 0xffu);
+            g[2] = static_cast<float>((g0 >> (8 * hb + 8)) & 0xffu);
+            g[3] = static_cast<float>((g1 >> (8 * hb + 8)) & 0xffu);
+            u[0] = static_cast<float>((u0 >> (8 * hb)) & 0xffu);
+            u[1] = static_cast<float>((u1 >> (8 * hb)) & 0xffu);
+            u[2] = static_cast<float>((u0 >> (8 * hb + 8)) & 0xffu);
+            u[3] = static_cast<float>((u1 >> (8 * hb + 8)) & 0xffu);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            g[k] = static_cast<float>(block_code<B>(gc, 4 * cl + k));
-            u[k] = static_cast<float>(block_code<B>(uc, 4 * cl + k));
+            for (int k = 0; k < 4; ++k) {
+                g[k] = static_cast<float>(block_code<B>(gc, 4 * cl + k));
+                u[k] = static_cast<float>(block_code<B>(uc, 4 * cl + k));
+            }
         }
 #pragma unroll
         for (int q = 0; q < R; ++q) {

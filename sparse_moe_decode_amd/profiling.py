@@ -9,9 +9,12 @@ summaries of kernel traces and of HBM traffic counters.
         --stats --output-format csv` run;
     python -m sparse_moe_decode_amd.profiling traffic --fetch DIR --write DIR
         --copy-fetch DIR --copy-write DIR --key KEY --kernels k1,k2,... --out FILE
+        [--call-kernel NAME --launches-per-call N]
         turns two counter runs of a workload and two of the copy kernel into
-        HBM bytes per call (each listed kernel once per call) and records them,
-        keyed by KEY and the kernel-source hash, in profiles/traffic.json;
+        HBM bytes per call (each listed kernel once per call, or as many times
+        as it was dispatched per call, the calls counted by NAME's dispatches)
+        and records them, keyed by KEY and the kernel-source hash, in
+        profiles/traffic.json;
     python -m sparse_moe_decode_amd.profiling counters DIR --out FILE --cmd "..."
         summarizes every counter of a `rocprofv3 --pmc` run: mean per
         dispatch, by kernel.
@@ -140,6 +143,12 @@ def cmd_traffic(args) -> int:
              "|---|---|---|---|---|---|"]
     total_f = total_w = 0.0
     per = {}
+    calls = None
+    if args.call_kernel:
+        cm = [n for n in fetch if args.call_kernel in n]
+        if not cm:
+            raise SystemExit(f"kernel {args.call_kernel} not found in the counter runs")
+        calls = sum(fetch[n][1] for n in cm) / args.launches_per_call
     for k in kernels:
         match = [n for n in fetch if k in n]
         matchw = [n for n in write if k in n]
@@ -148,13 +157,19 @@ def cmd_traffic(args) -> int:
         fk_mean = sum(fetch[n][0] * fetch[n][1] for n in match) / sum(fetch[n][1] for n in match)
         wk_mean = sum(write[n][0] * write[n][1] for n in matchw) / sum(write[n][1] for n in matchw)
         nd = sum(fetch[n][1] for n in match)
-        fb = fk_mean * 1024.0 * ff
-        wb = wk_mean * 1024.0 * wf
+        ndw = sum(write[n][1] for n in matchw)
+        # dispatches of this kernel per call: 1, or counted against the calls
+        pf = 1.0 if calls is None else nd / calls
+        pw = 1.0 if calls is None else ndw / calls
+        fb = fk_mean * 1024.0 * ff * pf
+        wb = wk_mean * 1024.0 * wf * pw
         total_f += fb
         total_w += wb
-        per[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": nd}
+        per[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": nd, "per_call": round(pf, 3)}
         lines.append(f"| `{k}` | {nd} | {fk_mean:.1f} | {wk_mean:.1f} | {fb:,.0f} | {wb:,.0f} |")
-    lines += ["", f"per call (each kernel once): fetched {total_f:,.0f} B, written {total_w:,.0f} B, "
+    how = ("each kernel once" if calls is None else
+           f"dispatches per call counted against {calls:g} calls ({args.call_kernel} x {args.launches_per_call} per call)")
+    lines += ["", f"per call ({how}): fetched {total_f:,.0f} B, written {total_w:,.0f} B, "
                   f"total {total_f + total_w:,.0f} B", f"kernel-source hash: {source_sha()}"]
     text = "\n".join(lines) + "\n"
     with open(args.out, "w") as f:
@@ -223,6 +238,9 @@ def main(argv=None) -> int:
     r.add_argument("--fetch-cmd", default="")
     r.add_argument("--write-cmd", default="")
     r.add_argument("--copy-cmd", default="")
+    r.add_argument("--call-kernel", default="",
+                   help="calls = dispatches of this kernel / --launches-per-call (default: every kernel once per call)")
+    r.add_argument("--launches-per-call", type=int, default=1)
     k = sub.add_parser("counters")
     k.add_argument("dir")
     k.add_argument("--out", default="")
