@@ -171,7 +171,7 @@ int moe_route(const moe_layer_desc *d, const float *x, int32_t T,
  *   If ids_in != NULL, the routing ids_in [T][K], wts_in [T][K] and
  *   gate_in [T] (device) is used as given (wts_in/gate_in must then be
  *   non-NULL) and no routing is computed; ids outside [0, E) contribute
- *   nothing. Otherwise routing is computed and,
+ *   nothing (no expert is read for them). Otherwise routing is computed and,
  *   for each of ids_out / wts_out / gate_out that is non-NULL, written out.
  * Path by T: T == 1 decode; 2 <= T <= 4 few-row (the selected experts'
  * union is read once for all rows); 5 <= T <= 12 few-row launches of three

@@ -45,17 +45,22 @@ template <int R>
 __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
 {
     if (R == 1) {
-        if (lane < K) {
-            rl.slots.expert[lane + 1] = rl.sel_e[0][lane];
-            rl.slots.w[lane + 1][0] = rl.sel_w[0][lane];
+        // selections with an id below 0 (given ids outside [0, E)) get no slot
+        const int e = lane < K ? rl.sel_e[0][lane] : -1;
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        const unsigned long long valid = __ballot(e >= 0);
+        const int slot = 1 + __popcll(valid & lt), ns = 1 + __popcll(valid);
+        if (e >= 0) {
+            rl.slots.expert[slot] = e;
+            rl.slots.w[slot][0] = rl.sel_w[0][lane];
         }
-        if (lane <= K) {
+        if (lane < ns) {
             rl.slots.rmask[lane] = 1u;
             rl.slots.pstart[lane] = lane;
         }
         if (lane == 0) {
-            rl.slots.nslots = K + 1;
-            rl.slots.pstart[K + 1] = K + 1;
+            rl.slots.nslots = ns;
+            rl.slots.pstart[ns] = ns;
             rl.slots.expert[0] = -1;
             rl.slots.w[0][0] = rl.g[0];
         }
@@ -68,7 +73,7 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
     const int lq = in ? lane / K : 0, lk = in ? lane - lq * K : 0;
     const int e = in ? rl.sel_e[lq][lk] : -1;
     const float wl = in ? rl.sel_w[lq][lk] : 0.0f;
-    bool first = in;
+    bool first = in && e >= 0;   // an id below 0 (given ids outside [0, E)) gets no slot
     float wq[R];
     uint32_t rm = 0;
 #pragma unroll
@@ -265,8 +270,8 @@ __device__ __forceinline__ void route_block1(const RouteArgs &a, double *lg, Rou
 // row by the whole workgroup (route_block1), or wave q selects row q from the
 // logits (staged in `lg`, R rows of (E+1)&~1 doubles) and wave 0 then builds
 // the slot table; or the caller's selection is taken as given (ids outside
-// [0, E) become expert 0 with weight 0). Ends with a workgroup barrier, after
-// which `lg` may be reused.
+// [0, E) get no slot: nothing of them is read or added). Ends with a
+// workgroup barrier, after which `lg` may be reused.
 template <int R>
 __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, RouteLds &rl)
 {
@@ -277,7 +282,7 @@ __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, Rout
             const int q = tid / a.K, k = tid - q * a.K;
             const int e = a.ids_in[tid];
             const bool ok = e >= 0 && e < a.E;
-            rl.sel_e[q][k] = ok ? e : 0;
+            rl.sel_e[q][k] = ok ? e : -1;
             rl.sel_w[q][k] = ok ? a.wts_in[tid] : 0.0f;
         }
         if (tid < R)

@@ -372,7 +372,8 @@ __global__ void __launch_bounds__(kSelWaves * kWave) k_select_approx(
     }
 }
 
-// Caller-supplied routing: ids outside [0, E) become expert 0 with weight 0.
+// Caller-supplied routing: ids outside [0, E) become -1, which the sort
+// skips (no GEMM row) and the combine adds nothing for.
 __global__ void __launch_bounds__(256) k_take_routing(const int32_t *ids_in, const float *wts_in, const float *gate_in,
                                                       int n, int T, int E, int32_t *ids, float *wts, float *gate)
 {
@@ -380,7 +381,7 @@ __global__ void __launch_bounds__(256) k_take_routing(const int32_t *ids_in, con
     if (i < n) {
         const int e = ids_in[i];
         const bool ok = e >= 0 && e < E;
-        ids[i] = ok ? e : 0;
+        ids[i] = ok ? e : -1;
         wts[i] = ok ? wts_in[i] : 0.0f;
     }
     if (i < T)
@@ -1153,7 +1154,8 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
     gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
 }
 
-// y[t] = sum_k out[inv[t*K + k]] + g_t * shared[t]   (float4 per thread)
+// y[t] = sum_k out[inv[t*K + k]] + g_t * shared[t]   (float4 per thread);
+// a pair the sort skipped (inv < 0) adds nothing
 __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const float *shared_out,
                                                  const int32_t *inv, const float *gate, int T, int K, int H,
                                                  const float *xres, float *y)
@@ -1168,6 +1170,8 @@ __global__ void __launch_bounds__(256) k_combine(const float *routed_out, const 
     float4 acc = make_float4(g * s.x, g * s.y, g * s.z, g * s.w);
     for (int k = 0; k < K; ++k) {
         const int r = inv[t * K + k];
+        if (r < 0)
+            continue;
         const float4 v = reinterpret_cast<const float4 *>(routed_out + static_cast<size_t>(r) * H)[c];
         acc.x += v.x;
         acc.y += v.y;

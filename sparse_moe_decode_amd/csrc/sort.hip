@@ -113,6 +113,8 @@ __global__ void __launch_bounds__(kSortChunk) k_sort_scatter(const int32_t *ids,
         perm[pos] = i;
         if (inv)
             inv[i] = pos;
+    } else if (inv && i < n) {
+        inv[i] = -1;
     }
 }
 

@@ -396,6 +396,49 @@ def test_given_routing_entry():
         assert tolerance_ok(out.cpu().numpy(), y64).all()
 
 
+def test_given_routing_with_ids_outside_range():
+    """Given ids outside [0, E) contribute nothing: each row's second choice
+    is replaced by -1 or E; the reference is the oracle on the layer whose
+    dropped expert has a zero down matrix (same routing, that expert adding
+    zero), row by row. Decode, few-row and prefill calls."""
+    _say("case: caller-supplied routing with ids outside [0, E)")
+    rng = np.random.default_rng(53)
+    a = _random_arrays(rng, 128, 16, 3, 64, 64)
+    T = 6
+    x = rng.standard_normal((T, 128)).astype(np.float32)
+    ri, rw, rg, _, _ = oracle_layer_from_arrays(a).forward(x)
+    ref = np.zeros((T, 128))
+    for t in range(T):
+        b = dict(a, exp_down=a["exp_down"].copy())
+        b["exp_down"][ri[t, 1]] = 0.0
+        ref[t] = oracle_layer_from_arrays(b).forward(x[t:t + 1])[4][0]
+    ids = ri.copy()
+    ids[:, 1] = np.where(np.arange(T) % 2 == 0, -1, 16)
+    G = gpu_layer_from_arrays(a)
+    import sparse_moe_decode_amd as moe
+    xt = torch.from_numpy(x).cuda()
+    for rows, path in ((1, None), (2, None), (3, None), (6, "prefill")):
+        out = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+        old = os.environ.get("MOE_FORCE_PATH")
+        if path:
+            os.environ["MOE_FORCE_PATH"] = path
+        try:
+            ws = G.workspace(rows)   # sized for the forced path
+            for t in range(0, T, rows):
+                moe.forward(G.desc, xt[t:t + rows], out[t:t + rows], ws,
+                            ids_in=torch.from_numpy(ids[t:t + rows].copy()).cuda(),
+                            wts_in=torch.from_numpy(rw[t:t + rows].astype(np.float32)).cuda(),
+                            gate_in=torch.from_numpy(rg[t:t + rows].astype(np.float32)).cuda())
+            torch.cuda.synchronize()
+        finally:
+            if path:
+                if old is None:
+                    os.environ.pop("MOE_FORCE_PATH", None)
+                else:
+                    os.environ["MOE_FORCE_PATH"] = old
+        assert tolerance_ok(out.cpu().numpy(), ref).all(), rows
+
+
 # --------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("rows", [1, 3, 300])   # decode, few-row, prefill
