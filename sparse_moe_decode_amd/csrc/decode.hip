@@ -1346,14 +1346,18 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     constexpr int kT = kDnWaves * kWave;
     const int n4 = STAGED ? p.max_pairs * p.Imax / 4 : 1;
     const float4 *hsrc = reinterpret_cast<const float4 *>(p.hbuf);
-    const int i0 = min(tid, n4 - 1), i1 = min(tid + kT, n4 - 1), i2 = min(tid + 2 * kT, n4 - 1),
-              i3 = min(tid + 3 * kT, n4 - 1);
-    float4 h0, h1, h2, h3;   // separate values, never an indexed array
+    // float4 of h' per thread requested at once: all of it for top-10
+    // routing and 512 channels (R (K + 1) pairs of 128 float4), so that the
+    // staging is one round trip; larger shapes stage the rest in a loop
+    constexpr int NH = R == 1 ? 4 : (R * 11 + 3) / 4;
+    int hix[NH];
+    float4 hv[NH];   // indexed only by unrolled constants: registers
     if (STAGED) {
-        h0 = hsrc[i0];
-        h1 = hsrc[i1];
-        h2 = hsrc[i2];
-        h3 = hsrc[i3];
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+            hix[k] = min(tid + k * kT, n4 - 1);
+            hv[k] = hsrc[hix[k]];
+        }
     }
     const int ti = min(tid, kMaxRows * kMaxK), tq = min(tid, R - 1);
     const int t_expert = p.slots->expert[ti];
@@ -1401,7 +1405,7 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
     float *hsl = reinterpret_cast<float *>(lds_raw) + (HS ? p.max_pairs * p.Imax : 0);
     if (STAGED) {
         float4 *dst = reinterpret_cast<float4 *>(lds_raw);
-        auto put = [&](int i, int ic, const float4 &v) {
+        auto put = [&](int i, int ic, float4 v) {
             dst[ic] = v;
             if constexpr (HS) {
                 const float part = (v.x + v.y) + (v.z + v.w);
@@ -1410,11 +1414,10 @@ __global__ void __launch_bounds__(kDnWaves * kWave) k_down(DownArgs p)
                     hsl[i >> 1] = part + other;
             }
         };
-        put(tid, i0, h0);
-        put(tid + kT, i1, h1);
-        put(tid + 2 * kT, i2, h2);
-        put(tid + 3 * kT, i3, h3);
-        for (int i = tid + 4 * kT; i < n4; i += kT)
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+            put(tid + k * kT, hix[k], hv[k]);
+        for (int i = tid + NH * kT; i < n4; i += kT)
             put(i, i, hsrc[i]);
         hl = reinterpret_cast<const float *>(lds_raw);
     }
