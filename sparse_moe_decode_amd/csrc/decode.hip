@@ -41,8 +41,15 @@ namespace moe {
 // slots 1.. are the distinct routed experts in order of first appearance
 // (row-major over [R][K]); the weight of a slot for row q is that row's route
 // weight of the expert (0 if the row did not select it). Run by one wave.
+// With `tab` (E ints of LDS, contents arbitrary) the rows' selections must
+// hold distinct experts within each row, as computed routing does: each
+// expert's first selection is then an LDS minimum over the selections, its
+// slot the count of first selections before it, and each selection sets its
+// own row's weight and mask bit (a few steps per lane). Without `tab` (caller
+// routing, where a row may repeat an expert and its weights add up) every
+// selection is compared with every other in a loop over the selections.
 template <int R>
-__device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
+__device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane, int *tab = nullptr)
 {
     if (R == 1) {
         // selections with an id below 0 (given ids outside [0, E)) get no slot
@@ -66,39 +73,70 @@ __device__ __forceinline__ void build_slots(RouteLds &rl, int K, int lane)
         }
         return;
     }
-    // lane l < R*K holds selection l (row l / K); the other selections are
-    // broadcast with readlane in uniform loops (no LDS round trips)
+    // lane l < R*K holds selection l (row l / K)
     const int RK = R * K;
     const bool in = lane < RK;
     const int lq = in ? lane / K : 0, lk = in ? lane - lq * K : 0;
     const int e = in ? rl.sel_e[lq][lk] : -1;
     const float wl = in ? rl.sel_w[lq][lk] : 0.0f;
-    bool first = in && e >= 0;   // an id below 0 (given ids outside [0, E)) gets no slot
-    float wq[R];
-    uint32_t rm = 0;
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        wq[q] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int j = q * K + k;
-            const int ej = __builtin_amdgcn_readlane(e, j);
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
-            const bool m = ej == e;
-            first = first && !(m && j < lane);
-            wq[q] += m ? wj : 0.0f;
-            rm |= m ? 1u << q : 0u;
-        }
-    }
+    const bool live = e >= 0;   // an id below 0 (given ids outside [0, E)) gets no slot
     const unsigned long long lt = (1ull << lane) - 1ull;
-    const unsigned long long mask = __ballot(first);
-    const int slot = 1 + __popcll(mask & lt);
-    const int ns = 1 + __popcll(mask);
-    if (first) {
-        rl.slots.expert[slot] = e;
+    bool first;
+    int slot, ns;
+    uint32_t rm = 0;
+    if (tab) {
+        if (live)
+            tab[e] = kWave;
+        __builtin_amdgcn_wave_barrier();
+        if (live)
+            atomicMin(&tab[e], lane);
+        __builtin_amdgcn_wave_barrier();
+        const int f = live ? tab[e] : kWave;
+        first = live && f == lane;
+        const unsigned long long mask = __ballot(first);
+        ns = 1 + __popcll(mask);
+        slot = live ? 1 + __popcll(mask & ((1ull << f) - 1ull)) : 0;
+        for (int i = lane; i < (ns - 1) * R; i += kWave)
+            rl.slots.w[1 + i / R][i % R] = 0.0f;
+        for (int i = lane; i < ns - 1; i += kWave)
+            rl.slots.rmask[1 + i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        if (live) {
+            rl.slots.w[slot][lq] = wl;
+            atomicOr(&rl.slots.rmask[slot], 1u << lq);
+        }
+        if (first)
+            rl.slots.expert[slot] = e;
+        __builtin_amdgcn_wave_barrier();
+        if (first)
+            rm = rl.slots.rmask[slot];
+    } else {
+        // the other selections are broadcast with readlane in uniform loops
+        first = live;
+        float wq[R];
 #pragma unroll
-        for (int q = 0; q < R; ++q)
-            rl.slots.w[slot][q] = wq[q];
-        rl.slots.rmask[slot] = rm;
+        for (int q = 0; q < R; ++q) {
+            wq[q] = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const int j = q * K + k;
+                const int ej = __builtin_amdgcn_readlane(e, j);
+                const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+                const bool m = ej == e;
+                first = first && !(m && j < lane);
+                wq[q] += m ? wj : 0.0f;
+                rm |= m ? 1u << q : 0u;
+            }
+        }
+        const unsigned long long mask = __ballot(first);
+        slot = 1 + __popcll(mask & lt);
+        ns = 1 + __popcll(mask);
+        if (first) {
+            rl.slots.expert[slot] = e;
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+                rl.slots.w[slot][q] = wq[q];
+            rl.slots.rmask[slot] = rm;
+        }
     }
     // pair numbering: slot 0 (all rows) first, then the slots in order; the
     // prefix of the per-slot pair counts (< 8) from ballots of their bits
@@ -321,8 +359,10 @@ __device__ __forceinline__ void route_block(const RouteArgs &a, double *lg, Rout
         }
     }
     __syncthreads();
+    // the staged logits are no longer read: their space holds the per-expert
+    // table of build_slots (computed routing only)
     if (wave == 0)
-        build_slots<R>(rl, a.K, lane);
+        build_slots<R>(rl, a.K, lane, a.ids_in ? nullptr : reinterpret_cast<int *>(lg));
     __syncthreads();
 }
 

@@ -115,7 +115,7 @@ def test_duplicate_router_rows_tie_on_gpu(layout):
     ri, _, _, logits = L.route(x)
     G = gpu_layer_from_arrays(a)
     ref = _oracle_ref(L, x)
-    for rows in (1, 200):   # decode and one prefill call
+    for rows in (1, 2, 3, 4, 200):   # decode, few-row calls and one prefill call
         got = run_calls(G, x, rows)
         np.testing.assert_array_equal(got[0], ri)
         assert_parity(got, ref, f"tie fixture rows={rows}")
