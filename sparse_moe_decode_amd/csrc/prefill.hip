@@ -26,8 +26,9 @@
 //
 // MFMA precision: activations enter as bf16 hi+lo pairs; 2-bit weights as
 // the exact bf16 values 1 + c/4 of their codes with 4 x the block scale
-// applied to each 32-deep partial sum and (minimum - 4 scale) as a separate
-// small GEMM; bf16 weights exactly; fp32 weights as hi+lo pairs.
+// applied to each 32-deep partial sum, and (minimum - 4 scale) times the
+// block sums of the activations as one more MFMA for every 4 blocks; bf16
+// weights exactly; fp32 weights as hi+lo pairs.
 // v_mfma_f32_16x16x32_bf16 accumulates in fp32; the dropped lo*lo terms are
 // below 2^-16 of each product.
 #include <hip/hip_runtime.h>
@@ -437,12 +438,13 @@ __global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, in
 //      gathered by token (gate/up) or taken in sorted order (down).
 //   B: 2-bit blocks, bf16 (exact) or fp32 (as hi/lo pairs).
 // 2-bit weights enter as the bf16 values v = 1 + c/4 of their codes (exact):
-// each 32-deep step is one block, t = A_hi.v + A_lo.v, acc += 4s * t with the
-// block's scale s (per B row); the remaining terms
-// sum_b (m[n][b] - 4 s[n][b]) * asum[r][b] (asum: block sums of A, m: block
-// minima) are a second small GEMM with K = blocks (m and -4s as separate
-// operands, 3 passes over hi/lo pairs each). bf16 weights: two passes (A_hi.w + A_lo.w); fp32 weights:
-// three (A_hi.w_hi + A_hi.w_lo + A_lo.w_hi).
+// each 32-deep step is one block, t = A_hi.v + A_lo.v, then
+// acc += 4s * t with the block's scale s (per B row), and the remaining terms
+// (m - 4s) * asum (m: the block's minimum, asum: the block sum of the A row)
+// as one more MFMA per tile for every 4 blocks: m and -4s as exact bf16
+// hi + lo, asum as hi + lo, the six products of 4 blocks in one 32-deep step.
+// bf16 weights: two passes (A_hi.w + A_lo.w); fp32 weights: three
+// (A_hi.w_hi + A_hi.w_lo + A_lo.w_hi).
 // Workgroup: 4 waves, BM rows x kGN B rows. Gate/up (DUAL) puts the gate and
 // up rows of the same channels in the same wave (the LDS B rows alternate
 // gate / up chunks) and ends with SwiGLU times the route weight, written as
@@ -469,7 +471,8 @@ struct GemmArgs {
     const uint16_t *ah, *al;   // A rows, bf16 hi/lo [rows][Kd]
     int a_bytes;               // bytes of each of ah, al
     int a_lo_off;              // bytes from ah to al (al follows ah)
-    const float *asum;         // 2-bit B: block sums of the A rows [rows][Kd/32]
+    const float *asum;         // block-format B: block sums of the A rows [rows][Kd/32]
+    int asum_bytes;            // bytes of asum
     int a_gather;              // A row of a tile row: token of the pair (1) or the row itself (0)
     const uint8_t *b0, *b1;    // B: gate, up (dual) or one matrix; routed expert e at base + e * bstride
     size_t bstride;
@@ -851,24 +854,26 @@ __global__ void __launch_bounds__(256) k_single_sum(const float *part, int ks, i
 }
 
 // Block-format main loop (b-bit codes, b = 2, 3, 4; the weight operand is
-// called B below). B arrives in mega-steps of 8 blocks: 8 consecutive lanes
-// read one B row's 8 blocks (8 * 4b bytes of codes and 32 of scale/min
-// words), so each wave-wide load touches 8 rows of one matrix; the raw words
-// are held in registers one mega-step ahead, then the codes go to LDS as they
-// are and the scales as fp32. Each wave expands the codes of its own B
-// operands to bf16 in registers (8 codes per lane per operand). A: each thread holds BM/32
-// 16-byte pieces (row, part, hi or lo) of 4 consecutive blocks; a group of 4
-// blocks goes to LDS at once (one barrier per group) and each block's pieces
-// are reloaded with the block 4 steps ahead as soon as they are stored.
-// Loads go through buffer descriptors: rows past the end read as zero. The
-// minimum terms run after the loop (from the block sums of A and the minima
-// in global memory).
-constexpr int kMS = 8;           // blocks per mega-step
+// called B below). B arrives in mega-steps of 4 blocks: 4 consecutive lanes
+// read one B row's 4 blocks (4 * 4b bytes of codes and 16 of scale/min
+// words), so each wave-wide load touches 16 rows of one matrix; the raw
+// words are held in registers one mega-step ahead, then the codes go to LDS
+// as they are, the scales as fp32, and the minima and scales as the operands
+// of the minimum term, with the block sums of the tile's A rows. Each wave
+// expands the codes of its own B operands to bf16 in registers (8 codes per
+// lane per operand). A: each thread holds BM/32 16-byte pieces (row, part,
+// hi or lo) of 4 consecutive blocks; a group of 4 blocks goes to LDS at once
+// (one barrier per group) and each block's pieces are reloaded with the
+// block 4 steps ahead as soon as they are stored. Loads go through buffer
+// descriptors: rows past the end read as zero.
+constexpr int kMS = 4;           // blocks per mega-step (a divisor of 64)
 constexpr int kAG = 4;           // A blocks per LDS group (and register ring slots)
 // Word 3 of a raw buffer descriptor on gfx9 targets (32-bit data format;
 // offsets past num_records read as zero).
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kRawS = kMS + 1;       // LDS row stride (floats) of scales
+constexpr int kMinS = 12;            // LDS row stride (dwords) of the minimum-term fragments
+static_assert(kMS == 4, "the minimum term packs 4 blocks x 6 products into one 32-deep MFMA");
 // LDS row stride (dwords) of the raw codes of b-bit blocks
 template <int BITS>
 struct RawCodes {
@@ -958,9 +963,16 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
     using S = GemmShape<BM>;
     constexpr int AP = BM / 32;            // A pieces per thread per block
     constexpr int BL = kGN * kMS / 256;    // (row, block) words per thread per mega-step
+    constexpr int ASN = (BM * kMS + 255) / 256;   // (A row, block) sums per thread per mega-step (at most)
+    constexpr int RPI = 64 / kMS;          // B rows per wave-wide load
     __shared__ __align__(16) uint16_t La[kAG][2][BM * kLD];
     __shared__ __align__(16) uint32_t Lrc[kGN * kRawC];
     __shared__ float Lsc[kGN * kRawS];
+    // minimum-term operands of the mega-step, three MFMA fragments per B row
+    // and per A row (see the staging below), and a zero fragment
+    __shared__ __align__(16) uint32_t Lmb[kGN * kMinS];
+    __shared__ __align__(16) uint32_t Lma[BM * kMinS];
+    __shared__ __align__(16) uint32_t Lz[4];
     __shared__ int Ltok[BM];
     __shared__ float Lrw[BM];
     __shared__ int Ltile[3];
@@ -976,7 +988,7 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
 
     // B raw words: wave w loads 64 consecutive B rows of one matrix (DUAL:
     // waves 0-1 gate, 2-3 up), 8 rows per instruction
-    const int bl = tid & 7;
+    const int bl = tid % kMS;
     const size_t eoff = p.routed ? static_cast<size_t>(e) * p.bstride : 0;
     const int rowb = (p.Kd / 32) * 4 * BITS;   // bytes of codes per B row
     const int msel = DUAL ? __builtin_amdgcn_readfirstlane(tid >> 7) : 0;   // wave-uniform
@@ -985,18 +997,36 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase), 0, static_cast<int>(plane), kBufWord3);
     const __amdgpu_buffer_rsrc_t rsmw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase + plane), 0, p.N * NB * 4, kBufWord3);
-    const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + ((tid & 63) >> 3);   // local channel of row j: + 8 j
+    const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + (tid & 63) / kMS;   // local channel of row j: + RPI j
     const int ch0 = n0 + chl0;
     uint32_t rc[BL][BITS];
     uint32_t rs[BL];
+    // block sums of A: value j of this thread is (row q % BM, block q / BM)
+    // of the mega-step, q = tid + 256 j; rows past the tile read as zero
+    // through a buffer descriptor: padding rows read past its range (zeros)
+    const __amdgpu_buffer_rsrc_t rsum =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.asum), 0, p.asum_bytes, kBufWord3);
+    float ras[ASN];
+    int asoff[ASN];
+#pragma unroll
+    for (int j = 0; j < ASN; ++j) {
+        const int q = tid + 256 * j;
+        const int src = q < BM * kMS ? Ltok[q % BM] : -1;
+        asoff[j] = src >= 0 ? (src * NB + q / BM) * 4 : 0x7fff0000;
+    }
     auto load_b = [&](int M) {
         const int blk = M * kMS + bl;
         const int bb = blk < NB ? blk : 0;
 #pragma unroll
         for (int j = 0; j < BL; ++j) {
-            const int n = ch0 + 8 * j;
+            const int n = ch0 + RPI * j;
             load_raw_codes<BITS>(rcode, n * rowb + bb * 4 * BITS, rc[j]);
             rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rsmw, (n * NB + bb) * 4, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < ASN; ++j) {
+            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsum, asoff[j] + M * kMS * 4, 0, 0));
+            ras[j] = M * kMS + (tid + 256 * j) / BM < NB ? v : 0.0f;
         }
     };
     // LDS B row of local channel c of matrix msel (DUAL: chunks alternate gate / up)
@@ -1037,6 +1067,8 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
         for (int ct = 0; ct < S::CT; ++ct)
             acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if (tid < 4)
+        Lz[tid] = 0u;   // ordered before its first read by the first group's barrier
     uint32_t one2 = 0x3F803F80u;   // see codes_bf16
     asm volatile("" : "+v"(one2));
     load_b(0);
@@ -1050,11 +1082,35 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
             const bool in = M * kMS + bl < NB;
 #pragma unroll
             for (int j = 0; j < BL; ++j) {
-                const int row = lds_row(chl0 + 8 * j);
+                const int row = lds_row(chl0 + RPI * j);
 #pragma unroll
                 for (int i = 0; i < BITS; ++i)
                     Lrc[row * kRawC + BITS * bl + i] = in ? rc[j][i] : 0u;
-                Lsc[row * kRawS + bl] = in ? kLevels * f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+                const float s = in ? f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+                Lsc[row * kRawS + bl] = kLevels * s;
+                // m and -2^b s as exact bf16 hi + lo (11-bit fp16 values):
+                // the pairs (m_hi, m_lo), (m_hi, s_hi), (s_lo, s_hi) of block bl
+                const float mf = in ? f16_to_f32(rs[j] >> 16) : 0.0f, sf = -kLevels * s;
+                const uint32_t mh = bf16_rne_bits(mf), ml = bf16_rne_bits(mf - __uint_as_float(mh << 16));
+                const uint32_t sh = bf16_rne_bits(sf), sl = bf16_rne_bits(sf - __uint_as_float(sh << 16));
+                Lmb[row * kMinS + bl] = mh | (ml << 16);
+                Lmb[row * kMinS + 4 + bl] = mh | (sh << 16);
+                Lmb[row * kMinS + 8 + bl] = sl | (sh << 16);
+            }
+            // the A rows' block sums as bf16 hi + lo (residual below 2^-17):
+            // the matching pairs (a_hi, a_hi), (a_lo, a_hi), (a_hi, a_lo), so
+            // that fragment f of both sides multiplies to
+            // a_hi m_hi + a_hi m_lo | a_lo m_hi + a_hi s_hi | a_hi s_lo + a_lo s_hi
+#pragma unroll
+            for (int j = 0; j < ASN; ++j) {
+                const int q = tid + 256 * j;
+                if (q < BM * kMS) {
+                    const uint32_t ah = bf16_rne_bits(ras[j]), al = bf16_rne_bits(ras[j] - __uint_as_float(ah << 16));
+                    uint32_t *ma = &Lma[(q % BM) * kMinS + q / BM];
+                    ma[0] = ah | (ah << 16);
+                    ma[4] = al | (ah << 16);
+                    ma[8] = ah | (al << 16);
+                }
             }
         }
         if (M + 1 < nms)
@@ -1102,55 +1158,30 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
                     }
                 }
             }
+            // the minimum terms of the mega-step's blocks: one MFMA per tile
+            // (lanes kq = 0..2 hold fragments 0..2, lanes kq = 3 zeros)
+            {
+                bf16x8 fma_[S::RT];
+#pragma unroll
+                for (int rt = 0; rt < S::RT; ++rt) {
+                    const int r = wr * S::TR + rt * 16 + li;
+                    fma_[rt] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4 *>(kq < 3 ? &Lma[r * kMinS + 4 * kq] : Lz));
+                }
+#pragma unroll
+                for (int ct = 0; ct < S::CT; ++ct) {
+                    const int c = wc * S::TC + ct * 16 + li;
+                    const bf16x8 fmb = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4 *>(kq < 3 ? &Lmb[c * kMinS + 4 * kq] : Lz));
+#pragma unroll
+                    for (int rt = 0; rt < S::RT; ++rt)
+                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fma_[rt], fmb, acc[rt][ct], 0, 0, 0);
+                }
+            }
             __syncthreads();
         }
     }
 
-    // minimum terms: acc += sum_b asum[row][b] * (m[col][b] - 2^b s[col][b])
-    // (the offset of the 1 + c/2^b code values), 32 blocks per MFMA; m and
-    // -2^b s are fp16 values times a power of two, exact as bf16 hi + lo, and
-    // enter separately
-    for (int b0 = 0; b0 < NB; b0 += 32) {
-        bf16x8 xah[S::RT], xal[S::RT];
-#pragma unroll
-        for (int rt = 0; rt < S::RT; ++rt) {
-            const int src = Ltok[wr * S::TR + rt * 16 + li];
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int b = b0 + kq * 8 + j;
-                v[j] = (src >= 0 && b < NB) ? p.asum[static_cast<size_t>(src) * NB + b] : 0.0f;
-            }
-            split_frag(v, xah[rt], xal[rt]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < S::CT; ++ct) {
-            const int c = wc * S::TC + ct * 16 + li;
-            const uint8_t *cm;
-            const int cn = gemm_brow<DUAL, BM>(p, e, n0, c, cm);
-            float vm[8], vs[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int b = b0 + kq * 8 + j;
-                const uint32_t w =
-                    (cn < p.N && b < NB) ? ld_nt4(cm + plane + (static_cast<size_t>(cn) * NB + b) * 4) : 0u;
-                vm[j] = f16_to_f32(w >> 16);
-                vs[j] = -kLevels * f16_to_f32(w & 0xffffu);
-            }
-            bf16x8 mh, ml, sh, sl;
-            split_frag(vm, mh, ml);
-            split_frag(vs, sh, sl);
-#pragma unroll
-            for (int rt = 0; rt < S::RT; ++rt) {
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], mh, acc[rt][ct], 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], ml, acc[rt][ct], 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal[rt], mh, acc[rt][ct], 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], sh, acc[rt][ct], 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah[rt], sl, acc[rt][ct], 0, 0, 0);
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal[rt], sh, acc[rt][ct], 0, 0, 0);
-            }
-        }
-    }
     gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
 }
 
@@ -1257,6 +1288,7 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     g.hh = w.hh;
     g.hl = w.hl;
     g.asum = w.xsum;
+    g.asum_bytes = static_cast<int>(sizeof(float) * T * (H / 32));
     g.hsum = ET::kChunk == 32 ? w.hsum : nullptr;
     launch_ggemm<ET, true>(g, bm, max_tiles, s);
     // shared gate/up: A = all x rows
@@ -1286,6 +1318,7 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     dg.al = w.hl;
     dg.a_gather = 0;
     dg.asum = w.hsum;
+    dg.asum_bytes = static_cast<int>(sizeof(float) * P * (I / 32));
     dg.b0 = static_cast<const uint8_t *>(d->exp_down);
     dg.b1 = nullptr;
     dg.bstride = mat_bytes<ET>(H, I);
