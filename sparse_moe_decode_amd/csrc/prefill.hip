@@ -1088,14 +1088,18 @@ __global__ void __launch_bounds__(256, BM == 32 ? (BITS == 2 ? 3 : 2) : 1) k_gge
                     Lrc[row * kRawC + BITS * bl + i] = in ? rc[j][i] : 0u;
                 const float s = in ? f16_to_f32(rs[j] & 0xffffu) : 0.0f;
                 Lsc[row * kRawS + bl] = kLevels * s;
-                // m and -2^b s as exact bf16 hi + lo (11-bit fp16 values):
-                // the pairs (m_hi, m_lo), (m_hi, s_hi), (s_lo, s_hi) of block bl
+                // m and -2^b s as exact bf16 hi + lo: hi keeps the top 8 of
+                // the 11 significant bits of the fp16 value, lo = v - hi (at
+                // most 3 bits, exact); the pairs (m_hi, m_lo), (m_hi, s_hi),
+                // (s_lo, s_hi) of block bl, each packed by one byte permute of
+                // the fp32 bit patterns' upper halves
                 const float mf = in ? f16_to_f32(rs[j] >> 16) : 0.0f, sf = -kLevels * s;
-                const uint32_t mh = bf16_rne_bits(mf), ml = bf16_rne_bits(mf - __uint_as_float(mh << 16));
-                const uint32_t sh = bf16_rne_bits(sf), sl = bf16_rne_bits(sf - __uint_as_float(sh << 16));
-                Lmb[row * kMinS + bl] = mh | (ml << 16);
-                Lmb[row * kMinS + 4 + bl] = mh | (sh << 16);
-                Lmb[row * kMinS + 8 + bl] = sl | (sh << 16);
+                const uint32_t mh = __float_as_uint(mf) & 0xffff0000u, sh = __float_as_uint(sf) & 0xffff0000u;
+                const uint32_t ml = __float_as_uint(mf - __uint_as_float(mh));
+                const uint32_t sl = __float_as_uint(sf - __uint_as_float(sh));
+                Lmb[row * kMinS + bl] = __builtin_amdgcn_perm(ml, mh, 0x07060302u);
+                Lmb[row * kMinS + 4 + bl] = __builtin_amdgcn_perm(sh, mh, 0x07060302u);
+                Lmb[row * kMinS + 8 + bl] = __builtin_amdgcn_perm(sh, sl, 0x07060302u);
             }
             // the A rows' block sums as bf16 hi + lo (residual below 2^-17):
             // the matching pairs (a_hi, a_hi), (a_lo, a_hi), (a_hi, a_lo), so
