@@ -954,8 +954,9 @@ __device__ __forceinline__ uint32_t quarter_codes(const uint32_t *raw, int kq)
     }
 }
 
-// Workgroups per CU: three 32-row tiles of 2-bit blocks; the wider raw
-// codes of 3- and 4-bit blocks (55-64 KiB of LDS per workgroup) fit two.
+// Workgroups per CU: three for 32-row tiles of 2-bit blocks (48 KiB of LDS
+// each); two for the wider raw codes of 3- and 4-bit blocks and for 64-row
+// tiles (their A staging and accumulators).
 template <int BITS, bool DUAL, int BM>
 __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb(GemmArgs p)
 {
@@ -988,7 +989,7 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
     const size_t plane = static_cast<size_t>(p.N) * (p.Kd / 32) * 4 * BITS;   // bytes of the codes plane
 
     // B raw words: wave w loads 64 consecutive B rows of one matrix (DUAL:
-    // waves 0-1 gate, 2-3 up), 8 rows per instruction
+    // waves 0-1 gate, 2-3 up), RPI rows per instruction
     const int bl = tid % kMS;
     const size_t eoff = p.routed ? static_cast<size_t>(e) * p.bstride : 0;
     const int rowb = (p.Kd / 32) * 4 * BITS;   // bytes of codes per B row
@@ -1000,36 +1001,45 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase + plane), 0, p.N * NB * 4, kBufWord3);
     const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + (tid & 63) / kMS;   // local channel of row j: + RPI j
     const int ch0 = n0 + chl0;
-    uint32_t rc[BL][BITS];
-    uint32_t rs[BL];
-    // block sums of A: value j of this thread is (row q % BM, block q / BM)
-    // of the mega-step, q = tid + 256 j; rows past the tile read as zero
-    // through a buffer descriptor: padding rows read past its range (zeros)
+    // 2-bit codes: two register sets (even and odd mega-steps), both loaded
+    // at once, so that each B row's words of 8 consecutive blocks (64 bytes of
+    // codes) are requested together; 3- and 4-bit codes (48 or 64 bytes per
+    // row and mega-step): one set, reloaded after each mega-step
+    constexpr int NSET = BITS == 2 ? 2 : 1;
+    uint32_t rc[NSET][BL][BITS];
+    uint32_t rs[NSET][BL];
+    // block sums of A: value j of this thread is (row q / kMS, block q % kMS)
+    // of the mega-step, q = tid + 256 j, loaded through a buffer descriptor
+    // (padding rows read past its range: zeros)
     const __amdgpu_buffer_rsrc_t rsum =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.asum), 0, p.asum_bytes, kBufWord3);
-    float ras[ASN];
+    float ras[NSET][ASN];
     int asoff[ASN];
 #pragma unroll
     for (int j = 0; j < ASN; ++j) {
         const int q = tid + 256 * j;
-        const int src = q < BM * kMS ? Ltok[q % BM] : -1;
-        asoff[j] = src >= 0 ? (src * NB + q / BM) * 4 : 0x7fff0000;
+        const int src = q < BM * kMS ? Ltok[q / kMS] : -1;
+        asoff[j] = src >= 0 ? (src * NB + q % kMS) * 4 : 0x7fff0000;
     }
-    auto load_b = [&](int M) {
+    // the words of mega-step M into register set `set`
+    auto load_b = [&](int M, auto set) {
+        constexpr int R = decltype(set)::value;
         const int blk = M * kMS + bl;
         const int bb = blk < NB ? blk : 0;
 #pragma unroll
         for (int j = 0; j < BL; ++j) {
             const int n = ch0 + RPI * j;
-            load_raw_codes<BITS>(rcode, n * rowb + bb * 4 * BITS, rc[j]);
-            rs[j] = __builtin_amdgcn_raw_buffer_load_b32(rsmw, (n * NB + bb) * 4, 0, 0);
+            load_raw_codes<BITS>(rcode, n * rowb + bb * 4 * BITS, rc[R][j]);
+            rs[R][j] = __builtin_amdgcn_raw_buffer_load_b32(rsmw, (n * NB + bb) * 4, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < ASN; ++j) {
             const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsum, asoff[j] + M * kMS * 4, 0, 0));
-            ras[j] = M * kMS + (tid + 256 * j) / BM < NB ? v : 0.0f;
+            ras[R][j] = M * kMS + (tid + 256 * j) % kMS < NB ? v : 0.0f;
         }
     };
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, NSET - 1>;
     // LDS B row of local channel c of matrix msel (DUAL: chunks alternate gate / up)
     auto lds_row = [&](int c) {
         if (!DUAL)
@@ -1072,7 +1082,10 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
         Lz[tid] = 0u;   // ordered before its first read by the first group's barrier
     uint32_t one2 = 0x3F803F80u;   // see codes_bf16
     asm volatile("" : "+v"(one2));
-    load_b(0);
+    const int nms = (NB + kMS - 1) / kMS;
+    load_b(0, Set0{});
+    if (NSET == 2 && nms > 1)
+        load_b(1, Set1{});
 #pragma unroll
     for (int u = 0; u < kAG; ++u)
         load_a(u, u);
@@ -1082,25 +1095,27 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
     // result.
     auto main_loop = [&](auto na) {
         constexpr int NA = decltype(na)::value;
-        const int nms = (NB + kMS - 1) / kMS;
-        for (int M = 0; M < nms; ++M) {
-            // raw codes and scales of this mega-step to LDS, then the next ones
+        // mega-step M from register set R (R = M % NSET)
+        auto mstep = [&](int M, auto set) {
+            constexpr int R = decltype(set)::value;
+            // raw codes and scales of this mega-step to LDS, then the words
+            // of the next one (one set) or, after an odd one, of the next two
             {
                 const bool in = M * kMS + bl < NB;
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < BL; ++j) {
                     const int row = lds_row(chl0 + RPI * j);
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < BITS; ++i)
-                        Lrc[row * kRawC + BITS * bl + i] = in ? rc[j][i] : 0u;
-                    const float s = in ? f16_to_f32(rs[j] & 0xffffu) : 0.0f;
+                        Lrc[row * kRawC + BITS * bl + i] = in ? rc[R][j][i] : 0u;
+                    const float s = in ? f16_to_f32(rs[R][j] & 0xffffu) : 0.0f;
                     Lsc[row * kRawS + bl] = kLevels * s;
                     // m and -2^b s as exact bf16 hi + lo: hi keeps the top 8 of
                     // the 11 significant bits of the fp16 value, lo = v - hi (at
                     // most 3 bits, exact); the pairs (m_hi, m_lo), (m_hi, s_hi),
                     // (s_lo, s_hi) of block bl, each packed by one byte permute of
                     // the fp32 bit patterns' upper halves
-                    const float mf = in ? f16_to_f32(rs[j] >> 16) : 0.0f, sf = -kLevels * s;
+                    const float mf = in ? f16_to_f32(rs[R][j] >> 16) : 0.0f, sf = -kLevels * s;
                     const uint32_t mh = __float_as_uint(mf) & 0xffff0000u, sh = __float_as_uint(sf) & 0xffff0000u;
                     const uint32_t ml = __float_as_uint(mf - __uint_as_float(mh));
                     const uint32_t sl = __float_as_uint(sf - __uint_as_float(sh));
@@ -1112,58 +1127,66 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
                 // the matching pairs (a_hi, a_hi), (a_lo, a_hi), (a_hi, a_lo), so
                 // that fragment f of both sides multiplies to
                 // a_hi m_hi + a_hi m_lo | a_lo m_hi + a_hi s_hi | a_hi s_lo + a_lo s_hi
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < ASN; ++j) {
                     const int q = tid + 256 * j;
                     if (q < BM * kMS) {
-                        const uint32_t ah = bf16_rne_bits(ras[j]), al = bf16_rne_bits(ras[j] - __uint_as_float(ah << 16));
-                        uint32_t *ma = &Lma[(q % BM) * kMinS + q / BM];
+                        const float av = ras[R][j];
+                        const uint32_t ah = bf16_rne_bits(av), al = bf16_rne_bits(av - __uint_as_float(ah << 16));
+                        uint32_t *ma = &Lma[(q / kMS) * kMinS + q % kMS];
                         ma[0] = ah | (ah << 16);
                         ma[4] = al | (ah << 16);
                         ma[8] = ah | (al << 16);
                     }
                 }
             }
-            if (M + 1 < nms)
-                load_b(M + 1);
+            if constexpr (NSET == 1) {
+                if (M + 1 < nms)
+                    load_b(M + 1, Set0{});
+            } else if constexpr (R == 1) {
+                if (M + 1 < nms)
+                    load_b(M + 1, Set0{});
+                if (M + 2 < nms)
+                    load_b(M + 2, Set1{});
+            }
             // A in groups of kAG blocks (the register ring): the group goes to
             // LDS, its slots are refilled kAG blocks ahead, one barrier, then the
             // group's blocks are computed
-    #pragma unroll
+#pragma unroll
             for (int g = 0; g < kMS; g += kAG) {
                 if (M * kMS + g >= NB)
                     break;
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < kAG; ++u) {
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < AP; ++j)
                         *reinterpret_cast<uint4 *>(&La[u][ahl[j]][arow[j] * kLD + apart[j] * 8]) = ra[u][j];
                     load_a(u, M * kMS + g + u + kAG);
                 }
                 __syncthreads();
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < kAG; ++u) {
                     const int b = g + u;
                     if (M * kMS + b >= NB)
                         break;
                     bf16x8 fah[S::RT], fal[S::RT];
-    #pragma unroll
+#pragma unroll
                     for (int rt = 0; rt < NA; ++rt) {
                         const int r = wr * S::TR + rt * 16 + li;
                         fah[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[u][0][r * kLD + kq * 8]));
                         fal[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(&La[u][1][r * kLD + kq * 8]));
                     }
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < S::CT; ++ct) {
                         const int c = wc * S::TC + ct * 16 + li;
                         const bf16x8 fb = codes_bf16<BITS>(quarter_codes<BITS>(&Lrc[c * kRawC + BITS * b], kq), one2);
                         const float sc = Lsc[c * kRawS + b];
-    #pragma unroll
+#pragma unroll
                         for (int rt = 0; rt < NA; ++rt) {
                             f32x4 t =
                                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(fah[rt], fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                             t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fal[rt], fb, t, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 acc[rt][ct][i] = fmaf(sc, t[i], acc[rt][ct][i]);
                         }
@@ -1173,36 +1196,47 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
                 // (lanes kq = 0..2 hold fragments 0..2, lanes kq = 3 zeros)
                 {
                     bf16x8 fma_[S::RT];
-    #pragma unroll
+#pragma unroll
                     for (int rt = 0; rt < NA; ++rt) {
                         const int r = wr * S::TR + rt * 16 + li;
                         fma_[rt] = __builtin_bit_cast(
                             bf16x8, *reinterpret_cast<const uint4 *>(kq < 3 ? &Lma[r * kMinS + 4 * kq] : Lz));
                     }
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < S::CT; ++ct) {
                         const int c = wc * S::TC + ct * 16 + li;
                         const bf16x8 fmb = __builtin_bit_cast(
                             bf16x8, *reinterpret_cast<const uint4 *>(kq < 3 ? &Lmb[c * kMinS + 4 * kq] : Lz));
-    #pragma unroll
+#pragma unroll
                         for (int rt = 0; rt < NA; ++rt)
                             acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fma_[rt], fmb, acc[rt][ct], 0, 0, 0);
                     }
                 }
                 __syncthreads();
             }
+        };
+        if constexpr (NSET == 1) {
+            for (int M = 0; M < nms; ++M)
+                mstep(M, Set0{});
+        } else {
+            for (int M = 0; M < nms; M += 2) {
+                mstep(M, Set0{});
+                if (M + 1 < nms)
+                    mstep(M + 1, Set1{});
+            }
         }
     };
-    const int nact = (nrows + 15) >> 4;   // wave-uniform
+    static_assert(S::RT == 2 || S::RT == 4, "32- or 64-row tiles");
+    const int nact = (nrows + 15) >> 4;   // wave-uniform, 1..RT
     if (nact >= S::RT)
         main_loop(std::integral_constant<int, S::RT>{});
     else if (nact == 1)
         main_loop(std::integral_constant<int, 1>{});
-    else if constexpr (S::RT > 2) {
+    else if constexpr (S::RT == 4) {
         if (nact == 2)
             main_loop(std::integral_constant<int, 2>{});
         else
-            main_loop(std::integral_constant<int, (S::RT > 3 ? 3 : 1)>{});
+            main_loop(std::integral_constant<int, 3>{});
     }
 
     gemm_epilogue<DUAL, BM>(p, acc, n0, r0, nrows, Lrw, wr, wc, lane);
