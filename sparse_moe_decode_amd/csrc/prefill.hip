@@ -10,8 +10,8 @@
 //                     logits exactly in fp64, exact top-K, softmax weights,
 //                     sigmoid gate
 //   sort (sort.hip)   stable counting sort of the T*K (row, slot) pairs by
-//                     expert, with the inverse permutation
-//   k_tiles           per-expert row-tile offsets (32- or 64-row tiles)
+//                     expert, with the inverse permutation and the per-expert
+//                     row tiles (32 or 64 rows) with each tile's expert
 //   k_ggemm (dual)    per (expert row tile, 128-channel block): gathered x
 //                     rows times the gate and up rows of the expert, SwiGLU,
 //                     times the route weight -> h (bf16 hi/lo, sorted rows)
@@ -74,13 +74,15 @@ __device__ void router_norm(const uint8_t *router_w, int E, int H, float *wn, in
 // the router rows, one wave per row (router_norm).
 template <typename RT>
 __global__ void __launch_bounds__(256) k_split_x(const float *x, int64_t n8, uint4 *xh, uint4 *xl, float *xsum,
-                                                 int nbx, const uint8_t *router_w, int E, int H, float *wn)
+                                                 int nbn, const uint8_t *router_w, int E, int H, float *wn)
 {
-    if (static_cast<int>(blockIdx.x) >= nbx) {
-        router_norm<RT>(router_w, E, H, wn, (blockIdx.x - nbx) * 4 + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
+    // the norm blocks come first, so that their longer dependent loads
+    // overlap the element-wise blocks instead of trailing them
+    if (static_cast<int>(blockIdx.x) < nbn) {
+        router_norm<RT>(router_w, E, H, wn, blockIdx.x * 4 + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
         return;
     }
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t i = static_cast<int64_t>(blockIdx.x - nbn) * blockDim.x + threadIdx.x;
     if (i >= n8)   // n8 is a multiple of 4: a lane quad is all in or all out
         return;
     const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
@@ -388,46 +390,6 @@ __global__ void __launch_bounds__(256) k_take_routing(const int32_t *ids_in, con
     }
     if (i < T)
         gate[i] = gate_in[i];
-}
-
-// Per-expert tile offsets: tile_off[e] = sum_{e' < e} ceil(count[e'] / bm),
-// and the expert of every row tile (tile_e[tix], tix < tile_off[E]), so that
-// a GEMM workgroup finds its expert with one load.
-__global__ void __launch_bounds__(1024) k_tiles(const int32_t *counts, int E, int bm, int32_t *tile_off,
-                                                int32_t *tile_e)
-{
-    __shared__ int s[kMaxE];
-    const int t = threadIdx.x;
-    const int v = t < E ? (counts[t] + bm - 1) / bm : 0;
-    if (t < E)
-        s[t] = v;
-    __syncthreads();
-    for (int off = 1; off < E; off <<= 1) {
-        int a = 0;
-        if (t < E && t >= off)
-            a = s[t - off];
-        __syncthreads();
-        if (t < E)
-            s[t] += a;
-        __syncthreads();
-    }
-    if (t < E)
-        tile_off[t] = s[t] - v;
-    if (t == 0)
-        tile_off[E] = s[E - 1];
-    // expert of tile tix: the first e whose inclusive sum exceeds tix
-    const int total = s[E - 1];
-    for (int tix = t; tix < total; tix += blockDim.x) {
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s[mid] > tix)
-                hi = mid;
-            else
-                lo = mid + 1;
-        }
-        tile_e[tix] = lo;
-    }
 }
 
 // ================================================================= GEMMs
@@ -1462,18 +1424,18 @@ static int prefill_route(const moe_layer_desc *d, const float *x, int T, const P
 }
 
 // x hi/lo and block sums; with `norms`, also the router row norms (for the
-// routing) in trailing blocks of the same launch.
+// routing) in leading blocks of the same launch.
 static void split_x(const moe_layer_desc *d, const float *x, int T, const PrefillWs &w, bool norms, hipStream_t s)
 {
     const int H = d->hidden, E = d->n_experts;
     const int64_t n8 = static_cast<int64_t>(T) * H / 8;
-    const int nbx = static_cast<int>((n8 + 255) / 256);
-    const dim3 grid(nbx + (norms ? (E + 3) / 4 : 0));
+    const int nbx = static_cast<int>((n8 + 255) / 256), nbn = norms ? (E + 3) / 4 : 0;
+    const dim3 grid(nbn + nbx);
     const uint8_t *rw = static_cast<const uint8_t *>(d->router_w);
     if (d->router_t == MOE_F32)
-        hipLaunchKernelGGL((k_split_x<F32>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
+        hipLaunchKernelGGL((k_split_x<F32>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbn, rw, E, H, w.wn);
     else
-        hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbx, rw, E, H, w.wn);
+        hipLaunchKernelGGL((k_split_x<BF16>), grid, dim3(256), 0, s, x, n8, w.xh, w.xl, w.xsum, nbn, rw, E, H, w.wn);
 }
 
 // The layer's input: x, or its RMS norm (k_rmsnorm into the workspace).
@@ -1513,11 +1475,11 @@ static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const 
     }
     if (rc != MOE_OK)
         return rc;
-    rc = launch_sort_by_expert(w.ids, T, K, E, w.counts, w.offsets, w.perm, w.sort_ws, s, w.inv);
+    const int bm = routed_bm(P, E);
+    rc = launch_sort_by_expert(w.ids, T, K, E, w.counts, w.offsets, w.perm, w.sort_ws, s, w.inv, bm, w.tile_off,
+                               w.tile_e);
     if (rc != MOE_OK)
         return rc;
-    const int bm = routed_bm(P, E);
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, s, w.counts, E, bm, w.tile_off, w.tile_e);
     const int et = d->expert_t, st = d->shared_t;
     if (st == MOE_F32) {
         switch (et) {
