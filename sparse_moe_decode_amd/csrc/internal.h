@@ -27,7 +27,7 @@ int launch_qb_unpack(int bits, const void *packed, int64_t rows, int64_t cols, f
 size_t sort_ws_bytes_tke(int64_t n, int E);
 int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
                           int32_t *perm, void *ws, hipStream_t s, int32_t *inv = nullptr, int bm = 0,
-                          int32_t *tile_off = nullptr, int32_t *tile_e = nullptr);
+                          int max_tiles = 0, int4 *tiles = nullptr);
 
 // prefill path (any number of rows; rows grouped by expert, MFMA GEMMs)
 size_t prefill_ws_bytes(const moe_layer_desc *d, int T);

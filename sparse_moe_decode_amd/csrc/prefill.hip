@@ -426,8 +426,7 @@ struct GemmShape {
 
 struct GemmArgs {
     int routed, T, K, E;
-    const int32_t *tile_off;   // [E+1] (routed)
-    const int32_t *tile_e;     // [tiles] expert of each row tile (routed)
+    const int4 *tiles;         // [tiles] expert, first sorted row, rows of each row tile (routed)
     const int32_t *offsets;    // [E+1] (routed)
     const int32_t *perm;       // [T*K] sorted row -> pair index (routed)
     const float *wts;          // [T*K] route weights by pair index (routed)
@@ -465,11 +464,10 @@ __device__ __forceinline__ bool gemm_tile(const GemmArgs &p, int *tile, int *tok
         const int tix = blockIdx.y;
         int e = -1, r0 = 0, nr = 0;
         if (p.routed) {
-            if (tix < p.tile_off[p.E]) {
-                e = p.tile_e[tix];
-                r0 = p.offsets[e] + (tix - p.tile_off[e]) * BM;
-                nr = min(BM, p.offsets[e + 1] - r0);
-            }
+            const int4 t = p.tiles[tix];   // e = -1 past the last tile
+            e = t.x;
+            r0 = t.y;
+            nr = t.z;
         } else if (tix * BM < p.T) {
             e = 0;
             r0 = tix * BM;
@@ -1290,8 +1288,7 @@ static int run_gemms(const moe_layer_desc *d, int T, const PrefillWs &w, int bm,
     g.T = T;
     g.K = K;
     g.E = E;
-    g.tile_off = w.tile_off;
-    g.tile_e = w.tile_e;
+    g.tiles = w.tiles;
     g.offsets = w.offsets;
     g.perm = w.perm;
     g.wts = w.wts;
@@ -1476,8 +1473,8 @@ static int prefill_middle(const moe_layer_desc *d, const float *x, int T, const 
     if (rc != MOE_OK)
         return rc;
     const int bm = routed_bm(P, E);
-    rc = launch_sort_by_expert(w.ids, T, K, E, w.counts, w.offsets, w.perm, w.sort_ws, s, w.inv, bm, w.tile_off,
-                               w.tile_e);
+    rc = launch_sort_by_expert(w.ids, T, K, E, w.counts, w.offsets, w.perm, w.sort_ws, s, w.inv, bm,
+                               static_cast<int>((P + bm - 1) / bm + E), w.tiles);
     if (rc != MOE_OK)
         return rc;
     const int et = d->expert_t, st = d->shared_t;

@@ -4,8 +4,8 @@
 //   k_sort_scan     one workgroup: per expert, the pairs of earlier chunks
 //                   (running sums over the chunks, loads batched 8 chunks at
 //                   a time), then counts and offsets (a scan over experts);
-//                   for the prefill GEMMs also the row tiles of each expert
-//                   and the expert of each tile.
+//                   for the prefill GEMMs also the row tiles (expert, first
+//                   sorted row, rows of each tile).
 //   k_sort_scatter  per chunk: per-wave histograms give the pairs of earlier
 //                   waves, a broadcast loop the earlier lanes of the same
 //                   wave; perm[offset + earlier chunks + earlier waves +
@@ -43,10 +43,9 @@ __global__ void __launch_bounds__(kSortChunk) k_sort_hist(const int32_t *ids, in
 // table[c][e] becomes the pairs of expert e in chunks before c; counts and
 // offsets (exclusive scan over experts, Hillis-Steele in LDS).
 __global__ void __launch_bounds__(kSortChunk) k_sort_scan(int C, int E, int *table, int32_t *counts,
-                                                         int32_t *offsets, int bm, int32_t *tile_off,
-                                                         int32_t *tile_e)
+                                                         int32_t *offsets, int bm, int max_tiles, int4 *tiles)
 {
-    __shared__ int sc[kMaxE];
+    __shared__ int sc[kMaxE], soff[kMaxE], scnt[kMaxE];
     const int tid = threadIdx.x;
     int total = 0;
     if (tid < E) {
@@ -75,15 +74,17 @@ __global__ void __launch_bounds__(kSortChunk) k_sort_scan(int C, int E, int *tab
     if (tid < E) {
         counts[tid] = total;
         offsets[tid] = sc[tid] - total;
+        soff[tid] = sc[tid] - total;
+        scnt[tid] = total;
         if (tid == E - 1)
             offsets[E] = sc[tid];
     }
     if (bm <= 0)
         return;
-    // row tiles of bm rows per expert: tile_off[e] = sum_{e' < e}
-    // ceil(count[e'] / bm), and the expert of every tile (tile_e[tix],
-    // tix < tile_off[E]), so that a GEMM workgroup finds its expert with one
-    // load
+    // row tiles of bm rows per expert, in expert order: tiles[tix] =
+    // (expert, first sorted row, rows) for tix < the number of tiles, and
+    // (-1, 0, 0) up to max_tiles, so that a GEMM workgroup finds its tile
+    // with one load
     const int v = tid < E ? (total + bm - 1) / bm : 0;
     __syncthreads();
     if (tid < E)
@@ -96,22 +97,24 @@ __global__ void __launch_bounds__(kSortChunk) k_sort_scan(int C, int E, int *tab
             sc[tid] += a;
         __syncthreads();
     }
-    if (tid < E)
-        tile_off[tid] = sc[tid] - v;
-    if (tid == 0)
-        tile_off[E] = sc[E - 1];
-    // expert of tile tix: the first e whose inclusive sum exceeds tix
+    // expert of tile tix: the first e whose inclusive tile sum exceeds tix
     const int ntiles = sc[E - 1];
-    for (int tix = tid; tix < ntiles; tix += blockDim.x) {
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (sc[mid] > tix)
-                hi = mid;
-            else
-                lo = mid + 1;
+    for (int tix = tid; tix < max_tiles; tix += blockDim.x) {
+        int4 t = make_int4(-1, 0, 0, 0);
+        if (tix < ntiles) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (sc[mid] > tix)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            const int first = sc[lo] - (scnt[lo] + bm - 1) / bm;   // the expert's first tile
+            const int r0 = soff[lo] + (tix - first) * bm;
+            t = make_int4(lo, r0, min(bm, soff[lo] + scnt[lo] - r0), 0);
         }
-        tile_e[tix] = lo;
+        tiles[tix] = t;
     }
 }
 
@@ -157,16 +160,15 @@ __global__ void __launch_bounds__(kSortChunk) k_sort_scatter(const int32_t *ids,
 }
 
 int launch_sort_by_expert(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                          int32_t *perm, void *ws, hipStream_t s, int32_t *inv, int bm, int32_t *tile_off,
-                          int32_t *tile_e)
+                          int32_t *perm, void *ws, hipStream_t s, int32_t *inv, int bm, int max_tiles, int4 *tiles)
 {
     const int n = T * K;
     const int chunks = (n + kSortChunk - 1) / kSortChunk;
     uint8_t *p = static_cast<uint8_t *>(ws);
     int *table = reinterpret_cast<int *>(p + align256(sizeof(Control)));
     hipLaunchKernelGGL(k_sort_hist, dim3(chunks), dim3(kSortChunk), 0, s, ids, n, E, table);
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortChunk), 0, s, chunks, E, table, counts, offsets, bm, tile_off,
-                       tile_e);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortChunk), 0, s, chunks, E, table, counts, offsets, bm, max_tiles,
+                       tiles);
     hipLaunchKernelGGL(k_sort_scatter, dim3(chunks), dim3(kSortChunk), 0, s, ids, n, E, table, offsets, perm, inv);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

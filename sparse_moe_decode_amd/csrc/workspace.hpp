@@ -77,7 +77,8 @@ struct PrefillWs {
     float *kpart_sh;                 // split-K partial sums of the shared expert's GEMMs
     int32_t *ids;
     float *wts, *gate;
-    int32_t *counts, *offsets, *perm, *inv, *tile_off, *tile_e;
+    int32_t *counts, *offsets, *perm, *inv;
+    int4 *tiles;                     // row tiles (expert, first sorted row, rows)
     uint16_t *hh, *hl, *shh, *shl;   // h of the routed pairs [T*K][I] and of the shared expert [T][Is], bf16 hi/lo
     float *xsum, *hsum;              // 32-element block sums of x [T][H/32] and of h [T*K][I/32]
     float *rout, *sout;
@@ -109,8 +110,7 @@ inline PrefillWs prefill_carve(void *ws, const moe_layer_desc *d, int T, bool ca
     w.offsets = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (E + 1)));
     w.perm = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
     w.inv = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * P));
-    w.tile_off = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (E + 1)));
-    w.tile_e = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * ((P + 31) / 32 + E)));   // tiles at the smallest bm
+    w.tiles = reinterpret_cast<int4 *>(take(sizeof(int4) * ((P + 31) / 32 + E)));   // tiles at the smallest bm
     w.hh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
     w.hl = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * P * I));
     w.shh = reinterpret_cast<uint16_t *>(take(sizeof(uint16_t) * T * Is));

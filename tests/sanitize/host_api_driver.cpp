@@ -48,7 +48,7 @@ int launch_qb_unpack(int, const void *, int64_t, int64_t, float *, hipStream_t)
     return MOE_EUNSUPPORTED;
 }
 int launch_sort_by_expert(const int32_t *, int, int, int, int32_t *, int32_t *, int32_t *, void *, hipStream_t,
-                          int32_t *, int, int32_t *, int32_t *)
+                          int32_t *, int, int, int4 *)
 {
     ++launches;
     return MOE_EUNSUPPORTED;
