@@ -259,11 +259,12 @@ def measure(cfg, rows, ncalls, rotate, steps, warmup, x_instance=0, per_step=Non
 EXTRA_WORKLOADS = [("decode_q2", 2, 1, 1000, None), ("fewrow_q2_R2", 3, 2, 500, None),
                    ("fewrow_q2_R3", 3, 3, 333, None), ("fewrow_q2_R8", 3, 8, 125, None),
                    ("prefill_q2", 4, 2048, 1, None),
-                   ("decode_q3", 2, 1, 1000, "q3"), ("decode_q4", 2, 1, 1000, "q4")]
+                   ("decode_q3", 2, 1, 1000, "q3"), ("decode_q4", 2, 1, 1000, "q4"),
+                   ("prefill_q3", 4, 2048, 1, "q3"), ("prefill_q4", 4, 2048, 1, "q4")]
 
 
 def run_extra(args, keys):
-    """The 2-bit decode, few-row and prefill workloads (all, or those in keys)."""
+    """The block-format decode, few-row and prefill workloads (all, or those in keys)."""
     import torch
     cfg = mi.CONFIGS[1]
     extra = {}

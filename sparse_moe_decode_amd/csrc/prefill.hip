@@ -961,11 +961,13 @@ __global__ void __launch_bounds__(256, BM == 32 && BITS == 2 ? 3 : 2) k_ggemm_qb
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(mbase + plane), 0, p.N * NB * 4, kBufWord3);
     const int chl0 = (DUAL ? ((tid >> 6) & 1) : (tid >> 6)) * 64 + (tid & 63) / kMS;   // local channel of row j: + RPI j
     const int ch0 = n0 + chl0;
-    // 2-bit codes: two register sets (even and odd mega-steps), both loaded
-    // at once, so that each B row's words of 8 consecutive blocks (64 bytes of
-    // codes) are requested together; 3- and 4-bit codes (48 or 64 bytes per
-    // row and mega-step): one set, reloaded after each mega-step
-    constexpr int NSET = BITS == 2 ? 2 : 1;
+    // two register sets (even and odd mega-steps), both loaded at once, so
+    // that each B row's words of 8 consecutive blocks (64 or 128 bytes of
+    // codes) are requested together; 4-bit codes in 64-row tiles (no
+    // registers to spare) and 3-bit codes (measured: the second set fetches
+    // less but runs slower, 984 against 914 us per 2048-row chunk): one set,
+    // reloaded after each mega-step
+    constexpr int NSET = BITS == 2 || (BITS == 4 && BM == 32) ? 2 : 1;
     uint32_t rc[NSET][BL][BITS];
     uint32_t rs[NSET][BL];
     // block sums of A: value j of this thread is (row q / kMS, block q % kMS)
